@@ -1,0 +1,232 @@
+"""ctypes front end of the verification oracle (``sv_oracle.c``).
+
+TEST INFRASTRUCTURE.  Only the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this module.  The product path
+(``rejection_sampling_verify_17_amd``) never imports it, and it never imports
+the product path: the two share no code.
+
+The C file states the rule and cites the pages it follows; this module only
+marshals numpy arrays and builds the shared object with gcc.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "sv_oracle.c")
+LIB = os.path.join(HERE, "libsv_oracle.so")
+
+F32 = 0
+BF16 = 1
+ACCEPT = 0
+SAMPLE = 1
+
+
+def build(force: bool = True, src: str = SRC, out: str = LIB) -> str:
+    """Compile the oracle C source with gcc (IEEE fp64, OpenMP) into `out`."""
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
+        tmp = out + ".tmp"
+        subprocess.run(
+            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
+             "-Wall", "-Wextra", "-o", tmp, src, "-lm"],
+            check=True)
+        os.replace(tmp, out)
+    return out
+
+
+def load(path: str) -> ctypes.CDLL:
+    """Load a built oracle shared object and declare its signatures."""
+    L = ctypes.CDLL(path)
+    vp, i32, u64, u32, dbl, flt = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64,
+                                   ctypes.c_uint32, ctypes.c_double, ctypes.c_float)
+    L.svo_philox4x32_10.argtypes = [vp, vp, vp]
+    L.svo_philox4x32_10.restype = None
+    L.svo_word.argtypes = [u64, u64, u32, u32, u32]
+    L.svo_word.restype = u32
+    L.svo_uniform_accept.argtypes = [u32]
+    L.svo_uniform_accept.restype = dbl
+    L.svo_exponential.argtypes = [u32]
+    L.svo_exponential.restype = dbl
+    L.svo_row_probs.argtypes = [vp, i32, i32, flt, i32, vp, vp]
+    L.svo_row_probs.restype = None
+    L.svo_accept.argtypes = [dbl, dbl, dbl]
+    L.svo_accept.restype = i32
+    L.svo_accept_count.argtypes = [dbl, dbl]
+    L.svo_accept_count.restype = ctypes.c_int64
+    L.svo_residual.argtypes = [vp, vp, i32, vp]
+    L.svo_residual.restype = i32
+    L.svo_gumbel_sample.argtypes = [vp, i32, u64, u64, u32, vp]
+    L.svo_gumbel_sample.restype = i32
+    L.svo_gumbel_sample_many.argtypes = [vp, i32, u64, u64, i32, u32, vp]
+    L.svo_gumbel_sample_many.restype = None
+    L.svo_verify.argtypes = [vp, vp, vp, i32, i32, i32, i32, flt, i32, u64, u64, i32,
+                             vp, vp, vp, vp, vp, vp]
+    L.svo_verify.restype = i32
+    L.svo_token_probs.argtypes = [vp, vp, vp, i32, i32, i32, i32, flt, i32, i32, vp, vp]
+    L.svo_token_probs.restype = i32
+    L.svo_max_threads.argtypes = []
+    L.svo_max_threads.restype = i32
+    return L
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The oracle library (built on first use if missing or stale)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build(force=True)
+        _lib = load(LIB)
+    return _lib
+
+
+def use(L: ctypes.CDLL | None) -> ctypes.CDLL | None:
+    """Swap the library behind the module functions (tests load deliberately
+    broken variants to show the pins catch them); returns the previous one."""
+    global _lib
+    prev, _lib = _lib, L
+    return prev
+
+
+def _ptr(a: np.ndarray) -> ctypes.c_void_p:
+    assert a.flags["C_CONTIGUOUS"]
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:  # bf16 bit patterns
+        return BF16
+    raise TypeError(f"logits must be float32 or uint16 (bf16 bits), got {a.dtype}")
+
+
+# --------------------------------------------------------------------------
+# Philox and the two variates
+# --------------------------------------------------------------------------
+def philox(ctr, key) -> np.ndarray:
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, dtype=np.uint32)
+    lib().svo_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def word(seed: int, seq: int, pos: int, v: int, purpose: int) -> int:
+    return int(lib().svo_word(seed, seq, pos, v, purpose))
+
+
+def uniform_accept(w: int) -> float:
+    return float(lib().svo_uniform_accept(w))
+
+
+def exponential(w: int) -> float:
+    return float(lib().svo_exponential(w))
+
+
+# --------------------------------------------------------------------------
+# Rows and rule pieces
+# --------------------------------------------------------------------------
+def row_probs(row: np.ndarray, temperature: float, top_k: int = 0) -> np.ndarray:
+    row = np.ascontiguousarray(row)
+    out = np.zeros(row.shape[-1], dtype=np.float64)
+    lib().svo_row_probs(_ptr(row), _dtype_code(row), row.shape[-1], temperature, top_k,
+                        _ptr(out), None)
+    return out
+
+
+def accept(u: float, p_t: float, q_t: float) -> bool:
+    return bool(lib().svo_accept(u, p_t, q_t))
+
+
+def accept_count(p_t: float, q_t: float) -> int:
+    return int(lib().svo_accept_count(p_t, q_t))
+
+
+def residual(q: np.ndarray, p: np.ndarray):
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    p = np.ascontiguousarray(p, dtype=np.float64)
+    r = np.zeros_like(q)
+    empty = lib().svo_residual(_ptr(q), _ptr(p), q.shape[0], _ptr(r))
+    return r, bool(empty)
+
+
+def gumbel_sample_many(w: np.ndarray, seed: int, seq0: int, n: int, pos: int) -> np.ndarray:
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    out = np.zeros(n, dtype=np.int32)
+    lib().svo_gumbel_sample_many(_ptr(w), w.shape[0], seed, seq0, n, pos, _ptr(out))
+    return out
+
+
+def gumbel_sample(w: np.ndarray, seed: int, seq: int, pos: int):
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    gap = np.zeros(1, dtype=np.float64)
+    idx = lib().svo_gumbel_sample(_ptr(w), w.shape[0], seed, seq, pos, _ptr(gap))
+    return int(idx), float(gap[0])
+
+
+# --------------------------------------------------------------------------
+# The whole step
+# --------------------------------------------------------------------------
+@dataclass
+class OracleResult:
+    out_tokens: np.ndarray   # [B, gamma+1] int32
+    n_accepted: np.ndarray   # [B] int32
+    u: np.ndarray            # [B, gamma] acceptance uniforms (NaN after the first rejection)
+    ratio: np.ndarray        # [B, gamma] q(t)/p(t)            (NaN after the first rejection)
+    gap: np.ndarray          # [B] best - second-best key of the sampled row
+    flags: np.ndarray        # [B] bit 0: empty residual, q sampled instead
+
+
+def verify(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray, temperature: float,
+           top_k: int = 0, seed: int = 0, seq_offset: int = 0, nthreads: int = 0) -> OracleResult:
+    """Oracle verification step.  target [B, gamma+1, V], draft [B, gamma, V]
+    (float32, or uint16 holding bf16 bits), tokens [B, gamma] int32."""
+    target = np.ascontiguousarray(target)
+    draft = np.ascontiguousarray(draft)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    B, g1, V = target.shape
+    gamma = g1 - 1
+    assert draft.shape == (B, gamma, V) and tokens.shape == (B, gamma)
+    assert target.dtype == draft.dtype
+    out = np.zeros((B, gamma + 1), dtype=np.int32)
+    n = np.zeros(B, dtype=np.int32)
+    u = np.zeros((B, gamma), dtype=np.float64)
+    ratio = np.zeros((B, gamma), dtype=np.float64)
+    gap = np.zeros(B, dtype=np.float64)
+    flags = np.zeros(B, dtype=np.int32)
+    rc = lib().svo_verify(_ptr(target), _ptr(draft), _ptr(tokens), B, gamma, V,
+                          _dtype_code(target), temperature, top_k, seed, seq_offset, nthreads,
+                          _ptr(out), _ptr(n), _ptr(u), _ptr(ratio), _ptr(gap), _ptr(flags))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return OracleResult(out, n, u, ratio, gap, flags)
+
+
+def token_probs(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray, temperature: float,
+                top_k: int = 0, nthreads: int = 0):
+    """(p_j(t_j), q_j(t_j)) for every draft position, each [B, gamma] float64."""
+    target = np.ascontiguousarray(target)
+    draft = np.ascontiguousarray(draft)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    B, g1, V = target.shape
+    gamma = g1 - 1
+    pt = np.zeros((B, gamma), dtype=np.float64)
+    qt = np.zeros((B, gamma), dtype=np.float64)
+    rc = lib().svo_token_probs(_ptr(target), _ptr(draft), _ptr(tokens), B, gamma, V,
+                               _dtype_code(target), temperature, top_k, nthreads,
+                               _ptr(pt), _ptr(qt))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return pt, qt
+
+
+def max_threads() -> int:
+    return int(lib().svo_max_threads())
