@@ -1,0 +1,312 @@
+#!/usr/bin/env python3
+"""Benchmark: batched speculative-sampling verification on one MI355X.
+
+A step is one sv_verify call over one batch of a synthetic workload (every
+kernel of the hot path: softmax statistics, acceptance ratios, first-rejection
+ballot, residual / bonus Gumbel-max sampling).  Inputs are resident in HBM
+before timing starts; for workloads smaller than 1 GiB several copies are
+rotated so repeated steps do not hit the 256 MB last-level cache.
+
+Prints ONE JSON line: verified draft positions per second on the headline
+workload (c4b: B=1024, gamma=4, V=50257, fp32, draft noise sigma 1), the
+roofline of the dominant kernel measured with HIP events recorded by the
+library around each launch, the CPU oracle timed on a bounded sample on this
+host, and the same measurements for the other workloads under "sweep".
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+HEADLINE = "c4b"
+SWEEP = ["c2", "c3", "c4a", "c4c", "c1"]
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "rejection_sampling_verify_17_amd", "csrc")
+
+
+# ---------------------------------------------------------------------------
+# HIP events (the library records them on the caller's stream)
+# ---------------------------------------------------------------------------
+class Hip:
+    def __init__(self):
+        self.L = ctypes.CDLL("libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self) -> int:
+        e = ctypes.c_void_p()
+        assert self.L.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def record(self, e, stream):
+        assert self.L.hipEventRecord(e, stream) == 0
+
+    def sync(self, e):
+        assert self.L.hipEventSynchronize(e) == 0
+
+    def ms(self, a, b) -> float:
+        f = ctypes.c_float()
+        assert self.L.hipEventElapsedTime(ctypes.byref(f), a, b) == 0
+        return float(f.value)
+
+    def destroy(self, e):
+        self.L.hipEventDestroy(e)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic bytes
+# ---------------------------------------------------------------------------
+def algorithmic_bytes(w, n_accepted: np.ndarray) -> dict:
+    """Bytes the method must move ("Roofline"):
+    pass 1 reads every draft row and target row 0..gamma-1 once (2 V b per
+    verified position); the sampling pass re-reads the rejected row pair
+    (2 V b) or the bonus row (V b) of each sequence; with top-k the rejected
+    position is resampled from the kept lists (no re-read) and only bonus rows
+    are read again.  Plus tokens in and outputs out."""
+    B, gamma, V = w.B, w.gamma, w.V
+    b = 2 if w.is_bf16 else 4
+    pass1 = 2 * B * gamma * V * b + 4 * B * gamma
+    valid = n_accepted >= 0
+    rej = int(np.sum(valid & (n_accepted < gamma)))
+    bonus = int(np.sum(valid & (n_accepted == gamma)))
+    if 0 < w.top_k < V:
+        pass2 = bonus * V * b
+    else:
+        pass2 = rej * 2 * V * b + bonus * V * b
+    out = 4 * B * (gamma + 1) + 4 * B
+    return {"pass1": pass1, "pass2": pass2, "outputs": out, "total": pass1 + pass2 + out}
+
+
+# ---------------------------------------------------------------------------
+# One workload
+# ---------------------------------------------------------------------------
+def run_workload(name: str, steps: int, warmup: int, hip: Hip, seed: int = 3000) -> dict:
+    import torch
+    import rejection_sampling_verify_17_amd as S
+    from rejection_sampling_verify_17_amd import inputs as I
+
+    t0 = time.time()
+    w = I.make(name)
+    gen_s = time.time() - t0
+    dev = torch.device("cuda:0")
+    nbytes = w.target.nbytes + w.draft.nbytes
+    copies = max(1, min(8, int(np.ceil((1 << 30) / nbytes))))
+    if w.is_bf16:
+        tgt0 = torch.from_numpy(w.target.view(np.int16)).view(torch.bfloat16)
+        drf0 = torch.from_numpy(w.draft.view(np.int16)).view(torch.bfloat16)
+    else:
+        tgt0, drf0 = torch.from_numpy(w.target), torch.from_numpy(w.draft)
+    tgts = [tgt0.to(dev) for _ in range(copies)]
+    drfs = [drf0.to(dev) for _ in range(copies)]
+    tok = torch.from_numpy(w.tokens).to(dev)
+    dt = S.SV_BF16 if w.is_bf16 else S.SV_F32
+    ws = torch.zeros(S.workspace_bytes(w.B, w.gamma, w.V, w.top_k, dt), dtype=torch.uint8, device=dev)
+    out = torch.empty((w.B, w.gamma + 1), dtype=torch.int32, device=dev)
+    nacc = torch.empty((w.B,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = int(stream.cuda_stream)
+    names = S.launch_names(w.B, w.gamma, w.V, dt, w.top_k)
+    nl = len(names)
+
+    def step(i, events=None):
+        k = i % copies
+        if events is None:
+            S.verify(tgts[k], drfs[k], tok, w.temperature, w.top_k, seed=seed, out_tokens=out, n_accepted=nacc,
+                     workspace=ws)
+        else:
+            S.verify_timed(tgts[k], drfs[k], tok, w.temperature, events, w.top_k, seed=seed, out_tokens=out,
+                           n_accepted=nacc, workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: plain calls bracketed by events on the launch stream.
+    e0, e1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    hip.record(e0, sp)
+    for i in range(steps):
+        step(i)
+    hip.record(e1, sp)
+    hip.sync(e1)
+    torch.cuda.synchronize()
+    ms_total = hip.ms(e0, e1)
+    ms_step = ms_total / steps
+
+    # Same steps again with the library recording an event pair around each
+    # kernel: per-kernel average durations for the roofline.
+    evs = [[hip.event() for _ in range(2 * nl)] for _ in range(steps)]
+    f0, f1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    hip.record(f0, sp)
+    for i in range(steps):
+        step(i, evs[i])
+    hip.record(f1, sp)
+    hip.sync(f1)
+    torch.cuda.synchronize()
+    per_kernel = {}
+    for li, kname in enumerate(names):
+        d = [hip.ms(evs[i][2 * li], evs[i][2 * li + 1]) for i in range(steps)]
+        per_kernel[kname] = {"avg_us": 1e3 * float(np.mean(d)), "min_us": 1e3 * float(np.min(d))}
+    ms_step_evented = hip.ms(f0, f1) / steps
+    for row in evs:
+        for e in row:
+            hip.destroy(e)
+    for e in (e0, e1, f0, f1):
+        hip.destroy(e)
+
+    n_acc = nacc.cpu().numpy()
+    ab = algorithmic_bytes(w, n_acc)
+    positions = w.B * w.gamma
+    dominant = names[0]
+    dom_bytes = ab["pass1"]
+    dom_us = per_kernel[dominant]["avg_us"]
+    res = {
+        "workload": name, "B": w.B, "gamma": w.gamma, "V": w.V, "dtype": "bf16" if w.is_bf16 else "f32",
+        "temperature": w.temperature, "top_k": w.top_k, "input_copies": copies,
+        "ms_per_step": ms_step, "ms_per_step_with_kernel_events": ms_step_evented,
+        "positions_per_s": positions / (ms_step * 1e-3),
+        "algorithmic_bytes": ab, "GBps_step": ab["total"] / (ms_step * 1e-3) / 1e9,
+        "frac_peak_step": ab["total"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "kernels": per_kernel, "dominant": dominant,
+        "dominant_GBps": dom_bytes / (dom_us * 1e-6) / 1e9,
+        "mean_accepted": float(n_acc[n_acc >= 0].mean()), "all_kept": float(np.mean(n_acc == w.gamma)),
+        "gen_s": gen_s,
+    }
+    del tgts, drfs
+    torch.cuda.empty_cache()
+    return res, w
+
+
+# ---------------------------------------------------------------------------
+# Traffic from committed rocprofv3 PMC summaries
+# ---------------------------------------------------------------------------
+def read_traffic(kernel: str, workload: str) -> float | None:
+    """HBM bytes per launch from profiles/<kernel>_<workload>_pmc.txt, or None if
+    absent or taken on different kernel sources."""
+    path = os.path.join(PROFILE_DIR, f"{kernel}_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith((" ", "#", "|")):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_digest") != source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, as it stands, on a bounded sample
+# ---------------------------------------------------------------------------
+def cpu_baseline(w, seed: int, budget_s: float = 12.0) -> dict:
+    from oracle import oracle as O
+    cores = len(os.sched_getaffinity(0))
+    B = w.B
+    n = min(B, max(cores, 8))
+    t0 = time.perf_counter()
+    O.verify(w.target[:n], w.draft[:n], w.tokens[:n], w.temperature, w.top_k, seed=seed, nthreads=cores)
+    t1 = time.perf_counter() - t0
+    if t1 < budget_s / 4 and n < B:
+        n = int(min(B, max(n + 1, n * (budget_s / max(t1, 1e-3)) * 0.8)))
+        t0 = time.perf_counter()
+        O.verify(w.target[:n], w.draft[:n], w.tokens[:n], w.temperature, w.top_k, seed=seed, nthreads=cores)
+        t1 = time.perf_counter() - t0
+    return {"value": n * w.gamma / t1, "unit": "verified draft positions/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n} of {B} sequences of {w.spec.name} (seed {seed}), {t1:.2f} s on {cores} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+    if args.copy_calib_mb:
+        n = args.copy_calib_mb << 20
+        a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
+        return
+
+    import rejection_sampling_verify_17_amd as S
+    S.lib()
+    hip = Hip()
+    print(f"# bench {args.workload}: steps {args.steps} warmup {args.warmup}", file=sys.stderr, flush=True)
+    head, w = run_workload(args.workload, args.steps, args.warmup, hip)
+    print(f"# {args.workload}: {head['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    dom = head["dominant"]
+    dom_us = head["kernels"][dom]["avg_us"]
+    traffic = read_traffic(dom, args.workload)
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": head["dominant_GBps"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": head["dominant_GBps"] / HBM_PEAK_GBS, "traffic": traffic,
+                "algorithmic_bytes_per_launch": head["algorithmic_bytes"]["pass1"], "avg_launch_us": dom_us}
+    cpu = None if args.no_cpu else cpu_baseline(w, 3000)
+    sweep = []
+    if not args.no_sweep:
+        for name in SWEEP:
+            if name == args.workload:
+                continue
+            r, _ = run_workload(name, max(10, args.steps // 2), max(3, args.warmup // 2), hip)
+            print(f"# {name}: {r['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+            sweep.append({k: r[k] for k in ("workload", "ms_per_step", "positions_per_s", "GBps_step",
+                                            "frac_peak_step", "dominant", "dominant_GBps", "kernels",
+                                            "mean_accepted", "input_copies")})
+    line = {
+        "metric": "verified draft positions/sec (and HBM GB/s, fraction of MI355X peak) at 1 GPU",
+        "value": head["positions_per_s"], "unit": "verified draft positions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if not w.is_bf16 else "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: B={w.B} gamma={w.gamma} V={w.V} "
+                               f"{'bf16' if w.is_bf16 else 'fp32'} T={w.temperature} top_k={w.top_k}",
+                   "B": w.B, "gamma": w.gamma, "V": w.V, "parallelism": "single GPU"},
+        "GBps_step": head["GBps_step"], "frac_peak_step": head["frac_peak_step"],
+        "kernels": head["kernels"], "mean_accepted": head["mean_accepted"],
+        "roofline": roofline, "cpu_baseline": cpu, "sweep": sweep, "source_digest": source_digest(),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,147 @@
+/*
+ * specverify — batched speculative-sampling verification on one MI355X (gfx950).
+ *
+ * C ABI: plain pointers and sizes, no C++ or framework types.  All compute runs
+ * in HIP kernels of this library, enqueued on the caller's stream.
+ *
+ * The operation (one verification step over B independent sequences):
+ *   For each sequence b, the target scored gamma+1 positions (logits
+ *   target_logits[b][0..gamma][V]) and the draft scored gamma positions
+ *   (draft_logits[b][0..gamma-1][V]) and emitted draft_tokens[b][0..gamma-1].
+ *   Both sets of logits become distributions by temperature and top-k:
+ *   q_j = softmax(topk(target[b][j]) / T), p_j = softmax(topk(draft[b][j]) / T)
+ *   (page "추측 디코딩: 큰 모델을 빠르게 돌리는 법", ai-trend.me, section
+ *   "어떻게 작동하나": temperature and top-k sampling are ordinary sampling from
+ *   adjusted distributions).  Draft t_j is kept with probability
+ *   min(1, q_j(t_j) / p_j(t_j)), judged left to right; the first rejected
+ *   position n is replaced by a draw from max(0, q_n - p_n) normalised, and
+ *   if all gamma are kept one more token is drawn from q_gamma (page
+ *   "스펙큘러티브 디코딩 — 작은 모델이 먼저 쓰고 큰 모델이 검사한다",
+ *   blog.mna-game.duckdns.org post 46, §1 for the rule, §3 for "accepted + 1"
+ *   tokens per step; page ai-trend.me, "어떻게 작동하나", for the scan order,
+ *   the discarded tail and the bonus token).
+ *
+ * Conventions fixed by this library where the pages are silent:
+ *   - top-k keeps exactly K entries with the largest raw logit, the smaller
+ *     vocabulary index on equal logits; top_k <= 0 or >= V turns it off.
+ *     It applies to every row of both inputs, the bonus row included.
+ *   - acceptance: keep iff q(t) > 0 and (p(t) == 0 or u < q(t)/p(t)), where
+ *     u = (w >> 8) * 2^-24 and w is the Philox4x32-10 word (below) at
+ *     (seq, pos = j, v = 0, purpose 0).
+ *   - the replacement and the bonus token are Gumbel-max draws: the arg-max
+ *     over the support of ln(weight_v) - ln(E_v), E_v = -ln U_v,
+ *     U_v = (2 * (w >> 9) + 1) * 2^-24, w the word at (seq, pos, v,
+ *     purpose 1), pos = the sampled row; ties go to the smaller v.  An empty
+ *     residual (only reachable through rounding) falls back to q_n.
+ *   - Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) with key
+ *     (seed mod 2^32, seed >> 32), counter (v >> 2, pos, seq mod 2^32,
+ *     purpose); the word is output (v mod 4).  seq = seq_offset + b.
+ *   Results are a pure function of (inputs, temperature, top_k, seed,
+ *   seq_offset): independent of launch geometry and repeatable bit for bit.
+ *
+ * Layouts: row-major, contiguous.
+ *   target_logits [B][gamma+1][V], draft_logits [B][gamma][V], both of dtype
+ *   `dtype` (SV_F32: IEEE binary32; SV_BF16: bfloat16 as 16-bit patterns);
+ *   logits must be finite or -inf and every row must keep a finite logit.
+ *   draft_tokens [B][gamma] int32.
+ *   out_tokens [B][gamma+1] int32: drafts 0..n-1, the sampled token at n,
+ *   -1 after it.  n_accepted [B] int32: n in [0, gamma]; a sequence with a
+ *   drafted token outside [0, V) gets n_accepted = -1 and a row of -1.
+ *
+ * Ownership: the caller allocates every buffer (device memory of the current
+ * HIP device, or memory the device can address).  The library allocates
+ * nothing and keeps no state between calls beyond the workspace contents.
+ *
+ * Workspace: sv_workspace_bytes() bytes of device memory.  It must be
+ * zero-filled before its first use (sv_workspace_init does that on the
+ * stream); every call that returns SV_OK leaves it zero-filled again for the
+ * next call.  One workspace serves one call at a time: calls that overlap
+ * (different streams, same workspace) race.
+ *
+ * Errors: argument errors return SV_EINVAL before anything is enqueued
+ * (null pointer, B < 1, gamma not in [1, 64], V < 2 or V > 2^28, temperature
+ * not finite or <= 0, unknown dtype, a logits pointer not aligned to its
+ * element size, workspace too small).  A failed launch returns SV_EHIP (the
+ * workspace must then be re-initialised).  Calls never synchronise.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define SV_API __attribute__((visibility("default")))
+#else
+#define SV_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+typedef enum { SV_OK = 0, SV_EINVAL = 1, SV_EHIP = 2 } sv_status;
+
+/* Bytes of device workspace sv_verify needs for this shape (0 on bad shape). */
+SV_API size_t sv_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype);
+
+/* Zero-fill `workspace_bytes` bytes of `workspace` on `stream` (a hipStream_t;
+ * NULL = the default stream), with a kernel of this library.  Async. */
+SV_API sv_status sv_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
+
+/* One verification step; see the top of this file.  All pointers are device
+ * pointers; `stream` is a hipStream_t (NULL = default stream). */
+SV_API sv_status sv_verify(const void *target_logits, const void *draft_logits,
+                    const int32_t *draft_tokens,
+                    int32_t B, int32_t gamma, int32_t V, int32_t dtype,
+                    float temperature, int32_t top_k,
+                    uint64_t seed, uint64_t seq_offset,
+                    int32_t *out_tokens, int32_t *n_accepted,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* sv_verify plus per-position diagnostics for tests (device outputs, either
+ * may be NULL):
+ *   token_probs [B][gamma][2] float: p_j(t_j), q_j(t_j) for every j < gamma
+ *     (computed for all positions, judged or not);
+ *   accept_ur [B][gamma][2] float: the acceptance uniform u_j and the ratio
+ *     q_j(t_j)/p_j(t_j) (+inf when p_j(t_j) = 0) for every j < gamma. */
+SV_API sv_status sv_verify_debug(const void *target_logits, const void *draft_logits,
+                          const int32_t *draft_tokens,
+                          int32_t B, int32_t gamma, int32_t V, int32_t dtype,
+                          float temperature, int32_t top_k,
+                          uint64_t seed, uint64_t seq_offset,
+                          int32_t *out_tokens, int32_t *n_accepted,
+                          void *workspace, size_t workspace_bytes, void *stream,
+                          float *token_probs, float *accept_ur);
+
+/* sv_verify that also records caller-created hipEvent_t handles on `stream`
+ * around each kernel it enqueues, for per-kernel timing: events[2i] before
+ * and events[2i+1] after launch i.  `n_events` is the array length; launches
+ * beyond n_events/2 are not bracketed.  *n_launches receives the number of
+ * kernels enqueued (may be NULL).  Same results as sv_verify. */
+SV_API sv_status sv_verify_timed(const void *target_logits, const void *draft_logits,
+                          const int32_t *draft_tokens,
+                          int32_t B, int32_t gamma, int32_t V, int32_t dtype,
+                          float temperature, int32_t top_k,
+                          uint64_t seed, uint64_t seq_offset,
+                          int32_t *out_tokens, int32_t *n_accepted,
+                          void *workspace, size_t workspace_bytes, void *stream,
+                          void *const *events, int32_t n_events, int32_t *n_launches);
+
+/* Name of kernel launch i of a call with these arguments (for matching event
+ * timings to profiler rows); NULL past the last launch. */
+SV_API const char *sv_launch_name(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
+                           int32_t top_k, int32_t i);
+
+/* Human-readable status. */
+SV_API const char *sv_status_string(sv_status s);
+
+/* Library version string. */
+SV_API const char *sv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

@@ -1,0 +1,12 @@
+"""specverify: batched speculative-sampling verification on one MI355X.
+
+The C ABI (include/specverify.h) is implemented by libspecverify.so, built
+from csrc/ with hipcc for gfx950; this package is its thin torch binding
+(`verify`, `verify_debug`, `verify_timed`) plus seeded synthetic inputs
+(`inputs`).
+"""
+from ._binding import (SV_BF16, SV_EHIP, SV_EINVAL, SV_F32, SV_OK, SpecVerifyError, launch_names, lib,
+                       status_string, verify, verify_debug, verify_timed, version, workspace_bytes)
+
+__all__ = ["verify", "verify_debug", "verify_timed", "workspace_bytes", "launch_names", "lib", "version",
+           "status_string", "SpecVerifyError", "SV_F32", "SV_BF16", "SV_OK", "SV_EINVAL", "SV_EHIP"]

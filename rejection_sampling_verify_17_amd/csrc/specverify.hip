@@ -1,0 +1,236 @@
+// C ABI of the verification library: argument checks, workspace layout,
+// launch geometry.  The operation and every convention are documented in
+// include/specverify.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "specverify.h"
+#include "sv_kernels.h"
+#include "sv_topk.h"
+
+namespace {
+
+using namespace sv;
+
+constexpr int kMaxGamma = 64;           // one wave ballots all positions
+constexpr int kMaxV = 1 << 28;          // byte offsets of a row fit 32 bits
+constexpr int kListMax = 1024;          // top-k lists kept up to this K
+constexpr int kTargetTiles = 2048;      // pass-1 / pass-2 blocks to aim for (8 per CU)
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+  bool topk;
+  int nch, cv, nch2, cv2, klist;
+  size_t off_part, off_seqstat, off_nseq, off_cnt1, off_cnt2, off_cnt3, off_best, off_rowinfo, off_lists;
+  size_t total;
+};
+
+bool shape_ok(int32_t B, int32_t gamma, int32_t V, int32_t dtype) {
+  return B >= 1 && gamma >= 1 && gamma <= kMaxGamma && V >= 2 && V <= kMaxV &&
+         (dtype == SV_F32 || dtype == SV_BF16);
+}
+
+// Split a row of nvec 16-byte vectors into chunks so that `rows` rows give
+// about kTargetTiles blocks, each thread keeping at least two vectors.
+void split(int rows, int nvec, int *nch, int *cv) {
+  const int max_ch = std::max(1, nvec / (2 * kThreads));
+  int n = (kTargetTiles + rows - 1) / rows;
+  n = std::max(1, std::min(n, max_ch));
+  int per = (nvec + n - 1) / n;
+  *cv = per;
+  *nch = (nvec + per - 1) / per;
+}
+
+Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype) {
+  Plan p{};
+  const int ne = dtype == SV_BF16 ? 8 : 4;
+  const int nvec = (V + ne - 1) / ne;
+  p.topk = top_k > 0 && top_k < V;
+  p.klist = (p.topk && top_k <= kListMax) ? top_k : 0;
+  if (!p.topk) {
+    split(B * gamma, nvec, &p.nch, &p.cv);
+    split(B, nvec, &p.nch2, &p.cv2);
+  }
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  p.off_part = take(p.topk ? 0 : (size_t)B * gamma * p.nch * sizeof(float4));
+  p.off_seqstat = take((size_t)B * sizeof(float4));
+  p.off_nseq = take((size_t)B * sizeof(int32_t));
+  p.off_cnt1 = take((size_t)B * sizeof(uint32_t));
+  p.off_cnt2 = take((size_t)B * sizeof(uint32_t));
+  p.off_cnt3 = take((size_t)B * sizeof(uint32_t));
+  p.off_best = take((size_t)B * sizeof(unsigned long long));
+  const size_t slots = (size_t)B * (2 * gamma + 1);
+  p.off_rowinfo = take(p.topk ? slots * sizeof(uint4) : 0);
+  p.off_lists = take(p.klist ? slots * (size_t)p.klist * sizeof(int2) : 0);
+  p.total = off;
+  return p;
+}
+
+template <int DT>
+struct Launches {
+  static sv_status run(const Args &a, const Plan &p, hipStream_t stream, void *const *events, int n_events,
+                       int *n_launches) {
+    int li = 0;
+    auto before = [&]() {
+      if (events && 2 * li < n_events) (void)hipEventRecord((hipEvent_t)events[2 * li], stream);
+    };
+    auto after = [&]() -> bool {
+      if (events && 2 * li + 1 < n_events) (void)hipEventRecord((hipEvent_t)events[2 * li + 1], stream);
+      ++li;
+      return hipGetLastError() == hipSuccess;
+    };
+    bool ok = true;
+    if (!p.topk) {
+      before();
+      hipLaunchKernelGGL(k_stats<DT>, dim3(a.B * a.gamma * p.nch), dim3(kThreads), 0, stream, a);
+      ok = ok && after();
+      before();
+      hipLaunchKernelGGL(k_sample<DT>, dim3(a.B * p.nch2), dim3(kThreads), 0, stream, a);
+      ok = ok && after();
+    } else {
+      before();
+      hipLaunchKernelGGL(k_topk_rows<DT>, dim3(a.B * 2 * a.gamma), dim3(kTopkThreads), 0, stream, a);
+      ok = ok && after();
+      before();
+      hipLaunchKernelGGL(k_topk_bonus<DT>, dim3(a.B), dim3(kTopkThreads), 0, stream, a);
+      ok = ok && after();
+    }
+    if (n_launches) *n_launches = li;
+    return ok ? SV_OK : SV_EHIP;
+  }
+};
+
+sv_status verify_impl(const void *target, const void *draft, const int32_t *tokens, int32_t B, int32_t gamma,
+                      int32_t V, int32_t dtype, float temperature, int32_t top_k, uint64_t seed,
+                      uint64_t seq_offset, int32_t *out_tokens, int32_t *n_accepted, void *workspace,
+                      size_t workspace_bytes, void *stream, float *token_probs, float *accept_ur,
+                      void *const *events, int32_t n_events, int32_t *n_launches) {
+  if (n_launches) *n_launches = 0;
+  if (!target || !draft || !tokens || !out_tokens || !n_accepted || !workspace) return SV_EINVAL;
+  if (!shape_ok(B, gamma, V, dtype)) return SV_EINVAL;
+  if (!std::isfinite(temperature) || !(temperature > 0.0f)) return SV_EINVAL;
+  const uintptr_t elem = dtype == SV_BF16 ? 2 : 4;
+  if (((uintptr_t)target % elem) || ((uintptr_t)draft % elem)) return SV_EINVAL;
+  if (((uintptr_t)tokens % 4) || ((uintptr_t)out_tokens % 4) || ((uintptr_t)n_accepted % 4)) return SV_EINVAL;
+  if ((uintptr_t)workspace % kAlign) return SV_EINVAL;
+  const Plan p = make_plan(B, gamma, V, top_k, dtype);
+  if (workspace_bytes < p.total) return SV_EINVAL;
+  if (events && n_events < 0) return SV_EINVAL;
+
+  char *ws = (char *)workspace;
+  Args a{};
+  a.target = target;
+  a.draft = draft;
+  a.tokens = tokens;
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.top_k = p.topk ? top_k : 0;
+  a.c = (float)(1.4426950408889634 / (double)temperature);
+  a.key0 = (uint32_t)seed;
+  a.key1 = (uint32_t)(seed >> 32);
+  a.seq_offset = seq_offset;
+  a.out_tokens = out_tokens;
+  a.n_accepted = n_accepted;
+  a.token_probs = token_probs;
+  a.accept_ur = accept_ur;
+  a.part = (float4 *)(ws + p.off_part);
+  a.seqstat = (float4 *)(ws + p.off_seqstat);
+  a.nseq = (int32_t *)(ws + p.off_nseq);
+  a.cnt1 = (unsigned int *)(ws + p.off_cnt1);
+  a.cnt2 = (unsigned int *)(ws + p.off_cnt2);
+  a.cnt3 = (unsigned int *)(ws + p.off_cnt3);
+  a.best = (unsigned long long *)(ws + p.off_best);
+  a.nch = p.nch;
+  a.cv = p.cv;
+  a.nch2 = p.nch2;
+  a.cv2 = p.cv2;
+  a.rowinfo = p.topk ? (uint4 *)(ws + p.off_rowinfo) : nullptr;
+  a.lists = p.klist ? (int2 *)(ws + p.off_lists) : nullptr;
+  a.klist = p.klist;
+
+  (void)hipGetLastError();  // start from a clean error state
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == SV_BF16) return Launches<DT_BF16>::run(a, p, s, events, n_events, n_launches);
+  return Launches<DT_F32>::run(a, p, s, events, n_events, n_launches);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sv_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype) {
+  if (!shape_ok(B, gamma, V, dtype)) return 0;
+  return make_plan(B, gamma, V, top_k, dtype).total;
+}
+
+sv_status sv_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
+  if (!workspace || ((uintptr_t)workspace % 16)) return SV_EINVAL;
+  if (workspace_bytes == 0) return SV_OK;
+  const size_t n16 = workspace_bytes / 16;
+  const size_t ntail = (workspace_bytes % 16) / 4;
+  const size_t n = std::max(n16, ntail);
+  const int threads = 256;
+  const size_t blocks = (n + threads - 1) / threads;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(threads), 0, (hipStream_t)stream, (u32x4 *)workspace,
+                     n16, (uint32_t *)((char *)workspace + n16 * 16), ntail);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+sv_status sv_verify(const void *target_logits, const void *draft_logits, const int32_t *draft_tokens, int32_t B,
+                    int32_t gamma, int32_t V, int32_t dtype, float temperature, int32_t top_k, uint64_t seed,
+                    uint64_t seq_offset, int32_t *out_tokens, int32_t *n_accepted, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+  return verify_impl(target_logits, draft_logits, draft_tokens, B, gamma, V, dtype, temperature, top_k, seed,
+                     seq_offset, out_tokens, n_accepted, workspace, workspace_bytes, stream, nullptr, nullptr,
+                     nullptr, 0, nullptr);
+}
+
+sv_status sv_verify_debug(const void *target_logits, const void *draft_logits, const int32_t *draft_tokens,
+                          int32_t B, int32_t gamma, int32_t V, int32_t dtype, float temperature, int32_t top_k,
+                          uint64_t seed, uint64_t seq_offset, int32_t *out_tokens, int32_t *n_accepted,
+                          void *workspace, size_t workspace_bytes, void *stream, float *token_probs,
+                          float *accept_ur) {
+  return verify_impl(target_logits, draft_logits, draft_tokens, B, gamma, V, dtype, temperature, top_k, seed,
+                     seq_offset, out_tokens, n_accepted, workspace, workspace_bytes, stream, token_probs,
+                     accept_ur, nullptr, 0, nullptr);
+}
+
+sv_status sv_verify_timed(const void *target_logits, const void *draft_logits, const int32_t *draft_tokens,
+                          int32_t B, int32_t gamma, int32_t V, int32_t dtype, float temperature, int32_t top_k,
+                          uint64_t seed, uint64_t seq_offset, int32_t *out_tokens, int32_t *n_accepted,
+                          void *workspace, size_t workspace_bytes, void *stream, void *const *events,
+                          int32_t n_events, int32_t *n_launches) {
+  return verify_impl(target_logits, draft_logits, draft_tokens, B, gamma, V, dtype, temperature, top_k, seed,
+                     seq_offset, out_tokens, n_accepted, workspace, workspace_bytes, stream, nullptr, nullptr,
+                     events, n_events, n_launches);
+}
+
+const char *sv_launch_name(int32_t B, int32_t gamma, int32_t V, int32_t dtype, int32_t top_k, int32_t i) {
+  if (!shape_ok(B, gamma, V, dtype)) return nullptr;
+  const bool topk = top_k > 0 && top_k < V;
+  static const char *dense[] = {"k_stats", "k_sample"};
+  static const char *filt[] = {"k_topk_rows", "k_topk_bonus"};
+  if (i < 0 || i >= 2) return nullptr;
+  return topk ? filt[i] : dense[i];
+}
+
+const char *sv_status_string(sv_status s) {
+  switch (s) {
+    case SV_OK: return "ok";
+    case SV_EINVAL: return "invalid argument";
+    case SV_EHIP: return "HIP launch failure";
+  }
+  return "unknown status";
+}
+
+const char *sv_version(void) { return "specverify 0.1 (gfx950)"; }
+
+}  // extern "C"

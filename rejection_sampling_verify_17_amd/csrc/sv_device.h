@@ -1,0 +1,308 @@
+// Device primitives for the verification kernels (gfx950, wave64).
+//
+// Philox4x32-10, the two variates drawn from it, logit decoding, bounds-checked
+// buffer loads and wave/block reductions.  Nothing here is shared with the
+// CPU oracle; the two are written separately from the same published
+// definitions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kWave = 64;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+enum { PURPOSE_ACCEPT = 0u, PURPOSE_SAMPLE = 1u };
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
+// as 1, 2, 3", SC'11).  Per round: multiply counter words 0 and 2 by the two
+// round multipliers, keep both halves of each 64-bit product, and rebuild the
+// counter from them and the key; the key then advances by the two Weyl
+// increments.  Ten rounds.
+// ---------------------------------------------------------------------------
+struct Philox4 {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ Philox4 philox(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                          uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint32_t mA = 0xD2511F53u, mB = 0xCD9E8D57u;
+    const uint32_t hiA = __umulhi(mA, c0), loA = mA * c0;
+    const uint32_t hiB = __umulhi(mB, c2), loB = mB * c2;
+    const uint32_t n0 = hiB ^ c1 ^ k0;
+    const uint32_t n2 = hiA ^ c3 ^ k1;
+    c0 = n0;
+    c1 = loB;
+    c2 = n2;
+    c3 = loA;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  Philox4 r;
+  r.w[0] = c0;
+  r.w[1] = c1;
+  r.w[2] = c2;
+  r.w[3] = c3;
+  return r;
+}
+
+// The four words of vocabulary group g (entries 4g .. 4g+3) at (seq, pos, purpose).
+__device__ __forceinline__ Philox4 stream_block(uint32_t k0, uint32_t k1, uint32_t seq, uint32_t pos,
+                                                uint32_t group, uint32_t purpose) {
+  return philox(group, pos, seq, purpose, k0, k1);
+}
+
+// Acceptance uniform: top 24 bits of the word times 2^-24, in [0, 1); exact in fp32.
+__device__ __forceinline__ float accept_uniform(uint32_t w) {
+  return (float)(w >> 8) * 0x1p-24f;
+}
+
+// Exponential variate E = -ln U, U = (2 (w >> 9) + 1) 2^-24 (an odd multiple of
+// 2^-24 inside (0, 1), exact in fp32).  For U >= 1/2 it is evaluated as
+// -log1p(-(1 - U)) with 1 - U exact, so E keeps its relative accuracy as U -> 1,
+// where E is smallest and the Gumbel key largest.
+__device__ __forceinline__ float exponential_variate(uint32_t w) {
+  const uint32_t k = w >> 9;
+  if (k < (1u << 22)) {
+    const float U = (float)(2u * k + 1u) * 0x1p-24f;
+    return -logf(U);
+  }
+  const float d = (float)((1u << 24) - 2u * k - 1u) * 0x1p-24f;
+  return -log1pf(-d);
+}
+
+// Order-preserving map of a float onto uint32 (larger float -> larger integer).
+__device__ __forceinline__ uint32_t orderable(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+}
+__device__ __forceinline__ float from_orderable(uint32_t u) {
+  const uint32_t b = (u & 0x80000000u) ? (u ^ 0x80000000u) : ~u;
+  return __uint_as_float(b);
+}
+
+// Key of entry v for an arg-max with ties to the smaller index.
+__device__ __forceinline__ unsigned long long pack_key(float key, uint32_t v) {
+  return ((unsigned long long)orderable(key) << 32) | (unsigned long long)(0xFFFFFFFFu - v);
+}
+__device__ __forceinline__ uint32_t packed_index(unsigned long long k) {
+  return 0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull);
+}
+
+// ---------------------------------------------------------------------------
+// Logits
+// ---------------------------------------------------------------------------
+template <int DT> struct Elem;
+template <> struct Elem<DT_F32> {
+  static constexpr int kSize = 4;  // bytes per logit
+  static constexpr int kVec = 4;   // logits per 16-byte load
+};
+template <> struct Elem<DT_BF16> {
+  static constexpr int kSize = 2;
+  static constexpr int kVec = 8;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <int DT>
+__device__ __forceinline__ void decode(const u32x4 v, float (&z)[Elem<DT>::kVec]) {
+  if constexpr (DT == DT_F32) {
+    z[0] = __uint_as_float(v.x);
+    z[1] = __uint_as_float(v.y);
+    z[2] = __uint_as_float(v.z);
+    z[3] = __uint_as_float(v.w);
+  } else {
+    z[0] = bf16_lo(v.x); z[1] = bf16_hi(v.x);
+    z[2] = bf16_lo(v.y); z[3] = bf16_hi(v.y);
+    z[4] = bf16_lo(v.z); z[5] = bf16_hi(v.z);
+    z[6] = bf16_lo(v.w); z[7] = bf16_hi(v.w);
+  }
+}
+
+// A row of V logits behind a buffer resource.  Loads past the row's last
+// 4-byte word return zeros instead of touching memory; callers mask entries
+// >= V themselves.  The range is the row rounded up to whole 4-byte words, so
+// an odd-length bf16 row's last entry stays readable (the extra two bytes lie
+// in the same word, never on another page).
+template <int DT> struct Row {
+  __amdgpu_buffer_rsrc_t rsrc;
+  const char *base;
+  bool aligned;  // row start is 4-byte aligned: vector loads allowed
+
+  __device__ __forceinline__ Row(const void *p, int V) {
+    base = (const char *)p;
+    const uint32_t bytes = ((uint32_t)V * Elem<DT>::kSize + 3u) & ~3u;
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, 0x00020000);
+    aligned = (((uintptr_t)base) & 3u) == 0;
+  }
+
+  // Logits [NE*iv, NE*iv + NE) of the row (entries past V are garbage-free zeros
+  // or neighbours; mask by index).
+  __device__ __forceinline__ void load_vec(int iv, float (&z)[Elem<DT>::kVec]) const {
+    constexpr int NE = Elem<DT>::kVec;
+    if (aligned) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, iv * 16, 0, 0);
+      decode<DT>(v, z);
+    } else {
+      // 2-byte-aligned bf16 row: entry by entry
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const uint16_t h = __builtin_amdgcn_raw_buffer_load_b16(rsrc, (iv * NE + e) * 2, 0, 0);
+        z[e] = __uint_as_float((uint32_t)h << 16);
+      }
+    }
+  }
+
+  __device__ __forceinline__ float load_one(int v) const {
+    if constexpr (DT == DT_F32) {
+      return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, v * 4, 0, 0));
+    } else {
+      const uint16_t h = __builtin_amdgcn_raw_buffer_load_b16(rsrc, v * 2, 0, 0);
+      return __uint_as_float((uint32_t)h << 16);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Softmax statistics in base 2.  A row's (R, S) means
+//   S = sum_v 2^(z_v c - R),  c = log2(e) / T,
+// with R an integer-valued float >= max z_v c (rounded), so merging two
+// partial sums rescales by an exact power of two.  R = -inf, S = 0: empty.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float scale_pow2(float S, float dR) {
+  // S * 2^dR for integer-valued dR <= 0
+  return ldexpf(S, (int)fmaxf(dR, -1000.0f));
+}
+
+__device__ __forceinline__ void merge_stats(float &R, float &S, float R2, float S2) {
+  const float Rn = fmaxf(R, R2);
+  if (Rn == -INFINITY) {
+    R = Rn;
+    S = 0.0f;
+    return;
+  }
+  const float a = (R == -INFINITY) ? 0.0f : scale_pow2(S, R - Rn);
+  const float b = (R2 == -INFINITY) ? 0.0f : scale_pow2(S2, R2 - Rn);
+  R = Rn;
+  S = a + b;
+}
+
+// Fold NE logits (already masked: -inf for entries outside the row) into (R, S).
+template <int NE>
+__device__ __forceinline__ void accumulate(float &R, float &S, const float (&z)[NE], float c) {
+  float m = z[0];
+#pragma unroll
+  for (int e = 1; e < NE; ++e) m = fmaxf(m, z[e]);
+  const float mc = m * c;
+  if (mc > R) {
+    const float Rn = ceilf(mc);
+    S = (R == -INFINITY) ? 0.0f : scale_pow2(S, R - Rn);
+    R = Rn;
+  }
+  if (R != -INFINITY) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) S += __builtin_amdgcn_exp2f(fmaf(z[e], c, -R));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Reductions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void wave_merge_stats(float &R, float &S) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    const float R2 = __shfl_xor(R, off, kWave);
+    const float S2 = __shfl_xor(S, off, kWave);
+    merge_stats(R, S, R2, S2);
+  }
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    const unsigned long long y = __shfl_xor(x, off, kWave);
+    x = y > x ? y : x;
+  }
+  return x;
+}
+
+__device__ __forceinline__ float wave_max_f(float x) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum_f(float x) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+// Block-wide merge of two (R, S) pairs; the result is valid in every thread.
+template <int NT>
+__device__ __forceinline__ void block_merge_stats2(float &R1, float &S1, float &R2, float &S2) {
+  constexpr int NW = NT / kWave;
+  __shared__ float sh[4][NW];
+  wave_merge_stats(R1, S1);
+  wave_merge_stats(R2, S2);
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  if (lane == 0) {
+    sh[0][w] = R1; sh[1][w] = S1; sh[2][w] = R2; sh[3][w] = S2;
+  }
+  __syncthreads();
+  R1 = sh[0][0]; S1 = sh[1][0]; R2 = sh[2][0]; S2 = sh[3][0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) {
+    merge_stats(R1, S1, sh[0][i], sh[1][i]);
+    merge_stats(R2, S2, sh[2][i], sh[3][i]);
+  }
+  __syncthreads();
+}
+
+template <int NT>
+__device__ __forceinline__ unsigned long long block_max_u64(unsigned long long x) {
+  constexpr int NW = NT / kWave;
+  __shared__ unsigned long long sh[NW];
+  x = wave_max_u64(x);
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  if (lane == 0) sh[w] = x;
+  __syncthreads();
+  x = sh[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) x = sh[i] > x ? sh[i] : x;
+  __syncthreads();
+  return x;
+}
+
+// Last-arriver election: every block of a group calls this once after its
+// results are stored; exactly one block (the last) gets true, and it then sees
+// the stores of all others.  The counter is left for the caller to reset.
+__device__ __forceinline__ bool arrive_last(unsigned int *counter, unsigned int total) {
+  __shared__ int last;
+  __threadfence();  // every thread's stores (not only thread 0's) precede the count
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const unsigned int prev = atomicAdd(counter, 1u);
+    last = (prev == total - 1u);
+  }
+  __syncthreads();
+  if (last) __threadfence();
+  return last != 0;
+}
+
+}  // namespace sv

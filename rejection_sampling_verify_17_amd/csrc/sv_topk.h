@@ -1,0 +1,431 @@
+// Verification kernels with the top-k filter (0 < K < V).
+//
+// Top-k keeps exactly the K entries of a row with the largest raw logit; among
+// equal logits the smaller vocabulary index is kept.  Every entry gets the
+// 64-bit key  (orderable(z) << 32) | (2^32 - 1 - v),  unique per row and
+// ordered like "larger logit, then smaller index"; the kept set is the K
+// largest keys, i.e. all keys >= the K-th largest ("threshold").
+//
+//   k_topk_rows   one block per row (draft rows 0..gamma-1, target rows
+//                 0..gamma-1 of a sequence).  Finds the row's threshold by an
+//                 LDS radix select, then the base-2 softmax statistics (R, S)
+//                 over the kept entries and, for small K, the kept list.  The
+//                 last block of a sequence judges the drafts (in registers,
+//                 wave ballot) and resamples a rejected position from the
+//                 residual over the target row's kept list.
+//   k_topk_bonus  one block per sequence whose drafts were all kept: top-k of
+//                 target row gamma and a Gumbel-max draw over its kept entries.
+//
+// Selection: a lower bound L on the K-th largest logit comes from the
+// per-thread maxima (K threads each own an entry >= their maximum's K-th
+// largest, so at least K entries are >= L); entries >= L are gathered into LDS
+// and the exact K-th largest key is selected among them.  If more than kCap
+// entries pass the bound (heavy ties), the select runs over the row itself.
+//
+// Page "추측 디코딩: 큰 모델을 빠르게 돌리는 법" (ai-trend.me), section
+// "어떻게 작동하나": top-k sampling reduces to sampling from an adjusted
+// distribution, which this filter builds for both p and q.
+#pragma once
+
+#include "sv_kernels.h"
+
+namespace sv {
+
+constexpr int kTopkThreads = 512;
+constexpr int kCap = 2048;  // candidate entries held in LDS
+
+struct TopkShared {
+  unsigned long long cand[kCap];
+  unsigned int hist[256];
+  unsigned int tmax[kTopkThreads];
+  unsigned int ncand;
+  unsigned int nkept;
+  unsigned long long sel_prefix;
+  unsigned int sel_k;
+  int sel_done;
+  float red_f[kTopkThreads / kWave];
+  unsigned long long red_u[kTopkThreads / kWave];
+  int bcast_n;
+};
+
+__device__ __forceinline__ unsigned long long entry_key(float z, uint32_t v) {
+  return ((unsigned long long)orderable(z) << 32) | (unsigned long long)(0xFFFFFFFFu - v);
+}
+
+// Radix select, most significant byte first: the K-th largest (1-based, with
+// multiplicity) of the keys `src` enumerates, over bits [lo, hi) (multiples of
+// 8; bits >= hi are equal across all keys).  If at some byte exactly the
+// remaining rank's worth of keys share the prefix, it stops early with the low
+// bits cleared: every key that shares the prefix is then within the K largest,
+// so "key >= result" still selects exactly the K largest when keys are unique.
+template <class Src>
+__device__ unsigned long long radix_select(TopkShared &sh, const Src &src, unsigned int K, int hi, int lo) {
+  const int tid = threadIdx.x;
+  unsigned long long prefix = 0ull, mask = 0ull;
+  unsigned int k = K;
+  for (int shift = hi - 8; shift >= lo; shift -= 8) {
+    for (int i = tid; i < 256; i += kTopkThreads) sh.hist[i] = 0u;
+    __syncthreads();
+    src.for_each([&](unsigned long long key) {
+      if ((key & mask) == prefix) atomicAdd(&sh.hist[(unsigned int)(key >> shift) & 255u], 1u);
+    });
+    __syncthreads();
+    if (tid < kWave) {
+      const int lane = tid;
+      const unsigned int h0 = sh.hist[4 * lane], h1 = sh.hist[4 * lane + 1];
+      const unsigned int h2 = sh.hist[4 * lane + 2], h3 = sh.hist[4 * lane + 3];
+      const unsigned int s = h0 + h1 + h2 + h3;
+      // inclusive suffix sum over lanes (higher lanes hold higher digits)
+      unsigned int incl = s;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const unsigned int y = __shfl_down(incl, off, kWave);
+        if (lane + off < kWave) incl += y;
+      }
+      unsigned int above = incl - s;  // keys with a digit in a higher lane
+      if (above < k && k <= incl) {
+        const unsigned int hs[4] = {h0, h1, h2, h3};
+        for (int i = 3; i >= 0; --i) {
+          if (above + hs[i] >= k) {
+            sh.sel_prefix = (unsigned long long)(4 * lane + i);
+            sh.sel_k = k - above;
+            sh.sel_done = (hs[i] == k - above);
+            break;
+          }
+          above += hs[i];
+        }
+      }
+    }
+    __syncthreads();
+    const unsigned long long d = sh.sel_prefix;
+    k = sh.sel_k;
+    const int done = sh.sel_done;
+    __syncthreads();
+    prefix |= d << shift;
+    mask |= 255ull << shift;
+    if (done) break;
+  }
+  return prefix;
+}
+
+struct LdsKeys {
+  const unsigned long long *keys;
+  unsigned int n;
+  template <class F> __device__ void for_each(F f) const {
+    for (unsigned int i = threadIdx.x; i < n; i += kTopkThreads) f(keys[i]);
+  }
+};
+
+struct LdsMax32 {  // per-thread maxima as 32-bit keys in the high word
+  const unsigned int *m;
+  template <class F> __device__ void for_each(F f) const {
+    for (unsigned int i = threadIdx.x; i < (unsigned int)kTopkThreads; i += kTopkThreads)
+      f((unsigned long long)m[i] << 32);
+  }
+};
+
+template <int DT> struct RowKeys {  // every entry of a global row
+  const Row<DT> *row;
+  int V;
+  template <class F> __device__ void for_each(F f) const {
+    constexpr int NE = Elem<DT>::kVec;
+    const int nvec = (V + NE - 1) / NE;
+    for (int iv = threadIdx.x; iv < nvec; iv += kTopkThreads) {
+      float z[NE];
+      row->load_vec(iv, z);
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const int v = iv * NE + e;
+        if (v < V) f(entry_key(z[e], (uint32_t)v));
+      }
+    }
+  }
+};
+
+// Result of selecting a row: the threshold key and the base-2 statistics over
+// the kept entries.  If `list` is given (K <= klist), the kept entries are
+// written there as (index, logit bits) in no particular order.
+struct TopkRow {
+  unsigned long long thr;
+  float R, S;
+};
+
+template <int DT>
+__device__ TopkRow topk_row(TopkShared &sh, const Row<DT> &row, int V, int K, float c, int2 *list) {
+  constexpr int NE = Elem<DT>::kVec;
+  const int tid = threadIdx.x;
+  const int nvec = (V + NE - 1) / NE;
+
+  // Phase A: per-thread maxima.
+  unsigned int mymax = 0u;
+  for (int iv = tid; iv < nvec; iv += kTopkThreads) {
+    float z[NE];
+    row.load_vec(iv, z);
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+      if (iv * NE + e < V) mymax = max(mymax, orderable(z[e]));
+  }
+  sh.tmax[tid] = mymax;
+  if (tid == 0) { sh.ncand = 0u; sh.nkept = 0u; }
+  __syncthreads();
+
+  // Phase B: lower bound L = K-th largest per-thread maximum.
+  unsigned int L = 0u;
+  if (K <= kTopkThreads) L = (unsigned int)(radix_select(sh, LdsMax32{sh.tmax}, (unsigned)K, 64, 32) >> 32);
+
+  // Phase C: gather entries with orderable(z) >= L.
+  for (int iv = tid; iv < nvec; iv += kTopkThreads) {
+    float z[NE];
+    row.load_vec(iv, z);
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      const int v = iv * NE + e;
+      if (v < V && orderable(z[e]) >= L) {
+        const unsigned int slot = atomicAdd(&sh.ncand, 1u);
+        if (slot < (unsigned int)kCap) sh.cand[slot] = entry_key(z[e], (uint32_t)v);
+      }
+    }
+  }
+  __syncthreads();
+  const unsigned int ncand = sh.ncand;
+  const bool in_lds = ncand <= (unsigned int)kCap;
+
+  // Phase D: exact threshold.
+  unsigned long long thr;
+  if (in_lds) thr = radix_select(sh, LdsKeys{sh.cand, ncand}, (unsigned)K, 64, 0);
+  else thr = radix_select(sh, RowKeys<DT>{&row, V}, (unsigned)K, 64, 0);
+
+  // Phase E: statistics over kept entries (and the list).
+  float zmax = -INFINITY;
+  auto visit_max = [&](unsigned long long key) {
+    if (key >= thr) zmax = fmaxf(zmax, from_orderable((uint32_t)(key >> 32)));
+  };
+  if (in_lds) LdsKeys{sh.cand, ncand}.for_each(visit_max);
+  else RowKeys<DT>{&row, V}.for_each(visit_max);
+  zmax = wave_max_f(zmax);
+  if ((tid % kWave) == 0) sh.red_f[tid / kWave] = zmax;
+  __syncthreads();
+  zmax = sh.red_f[0];
+  for (int i = 1; i < kTopkThreads / kWave; ++i) zmax = fmaxf(zmax, sh.red_f[i]);
+  __syncthreads();
+  const float R = (zmax == -INFINITY) ? -INFINITY : ceilf(zmax * c);
+
+  float S = 0.0f;
+  auto visit_sum = [&](unsigned long long key) {
+    if (key >= thr) {
+      const float z = from_orderable((uint32_t)(key >> 32));
+      if (z != -INFINITY) S += __builtin_amdgcn_exp2f(fmaf(z, c, -R));
+      if (list) {
+        const unsigned int slot = atomicAdd(&sh.nkept, 1u);
+        list[slot] = make_int2((int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull)), (int)__float_as_uint(z));
+      }
+    }
+  };
+  if (in_lds) LdsKeys{sh.cand, ncand}.for_each(visit_sum);
+  else RowKeys<DT>{&row, V}.for_each(visit_sum);
+  S = wave_sum_f(S);
+  if ((tid % kWave) == 0) sh.red_f[tid / kWave] = S;
+  __syncthreads();
+  S = 0.0f;
+  for (int i = 0; i < kTopkThreads / kWave; ++i) S += sh.red_f[i];
+  __syncthreads();
+  return TopkRow{thr, R, S};
+}
+
+__device__ __forceinline__ uint4 pack_rowinfo(const TopkRow &r) {
+  return make_uint4((uint32_t)(r.thr & 0xFFFFFFFFull), (uint32_t)(r.thr >> 32), __float_as_uint(r.R),
+                    __float_as_uint(r.S));
+}
+__device__ __forceinline__ TopkRow unpack_rowinfo(uint4 u) {
+  return TopkRow{((unsigned long long)u.y << 32) | u.x, __uint_as_float(u.z), __uint_as_float(u.w)};
+}
+
+// p or q of entry (z, v) under a selected row's statistics: 0 outside the kept set.
+__device__ __forceinline__ float kept_prob(const TopkRow &r, float z, uint32_t v, float c) {
+  if (entry_key(z, v) < r.thr || z == -INFINITY) return 0.0f;
+  return __builtin_amdgcn_exp2f(fmaf(z, c, -r.R)) / r.S;
+}
+
+template <int NT>
+__device__ unsigned long long block_max_u64_sh(unsigned long long x, unsigned long long *red) {
+  x = wave_max_u64(x);
+  if ((threadIdx.x % kWave) == 0) red[threadIdx.x / kWave] = x;
+  __syncthreads();
+  x = red[0];
+  for (int i = 1; i < NT / kWave; ++i) x = red[i] > x ? red[i] : x;
+  __syncthreads();
+  return x;
+}
+
+// Gumbel-max over the kept entries of target row `pos` (weights q): used for
+// the bonus token and for an empty residual.  `list` holds the kept entries
+// when K <= klist; otherwise the row is scanned with the threshold.
+template <int DT>
+__device__ unsigned long long gumbel_over_kept_q(TopkShared &sh, const Args &a, int b, int pos,
+                                                 const TopkRow &qr, const int2 *list, const Row<DT> &Q) {
+  const uint32_t seq = seq_of(a, b);
+  unsigned long long best = 0ull;
+  auto consider = [&](float z, uint32_t v) {
+    if (z == -INFINITY || entry_key(z, v) < qr.thr) return;
+    const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)pos, v >> 2, PURPOSE_SAMPLE);
+    const float E = exponential_variate(blk.w[v & 3u]);
+    const unsigned long long k = pack_key(fmaf(z, a.c, -__builtin_amdgcn_logf(E)), v);
+    best = k > best ? k : best;
+  };
+  if (list) {
+    for (int i = threadIdx.x; i < a.top_k; i += kTopkThreads)
+      consider(__int_as_float(list[i].y), (uint32_t)list[i].x);
+  } else {
+    for (int v = threadIdx.x; v < a.V; v += kTopkThreads) consider(Q.load_one(v), (uint32_t)v);
+  }
+  return block_max_u64_sh<kTopkThreads>(best, sh.red_u);
+}
+
+// Residual draw at rejected position n: weights max(0, q_n - p_n) over the
+// target row's kept entries (outside them q_n = 0 and the weight is 0).
+template <int DT>
+__device__ unsigned long long gumbel_residual_topk(TopkShared &sh, const Args &a, int b, int n,
+                                                   const TopkRow &pr, const TopkRow &qr, const int2 *qlist,
+                                                   const Row<DT> &P, const Row<DT> &Q) {
+  const uint32_t seq = seq_of(a, b);
+  const float c = a.c;
+  unsigned long long best = 0ull;
+  auto consider = [&](float zq, uint32_t v) {
+    const float qv = kept_prob(qr, zq, v, c);
+    if (qv <= 0.0f) return;
+    const float pv = kept_prob(pr, P.load_one((int)v), v, c);
+    const float r = qv - pv;
+    if (!(r > 0.0f)) return;
+    const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)n, v >> 2, PURPOSE_SAMPLE);
+    const unsigned long long k = pack_key(r / exponential_variate(blk.w[v & 3u]), v);
+    best = k > best ? k : best;
+  };
+  if (qlist) {
+    for (int i = threadIdx.x; i < a.top_k; i += kTopkThreads)
+      consider(__int_as_float(qlist[i].y), (uint32_t)qlist[i].x);
+  } else {
+    for (int v = threadIdx.x; v < a.V; v += kTopkThreads) consider(Q.load_one(v), (uint32_t)v);
+  }
+  return block_max_u64_sh<kTopkThreads>(best, sh.red_u);
+}
+
+// rowinfo / lists slot of a sequence's rows: draft j -> j, target j -> gamma + j
+// (j <= gamma; target row gamma is slot 2 gamma).
+__device__ __forceinline__ size_t slot_of(const Args &a, int b, int s) {
+  return (size_t)b * (2 * a.gamma + 1) + s;
+}
+
+template <int DT>
+__device__ void finalize_topk(TopkShared &sh, const Args &a, int b) {
+  const int gamma = a.gamma;
+  const int tid = threadIdx.x;
+  const uint32_t seq = seq_of(a, b);
+  const float c = a.c;
+  int32_t *out = a.out_tokens + (size_t)b * (gamma + 1);
+
+  if (tid < kWave) {
+    const int lane = tid;
+    const bool active = lane < gamma;
+    int t = 0;
+    bool ok = true;
+    if (active) {
+      t = a.tokens[(size_t)b * gamma + lane];
+      ok = (t >= 0) && (t < a.V);
+    }
+    const bool invalid = __ballot(active && !ok) != 0ull;
+    int nn = -1;
+    if (!invalid) {
+      bool accept = false;
+      if (active) {
+        const TopkRow pr = unpack_rowinfo(a.rowinfo[slot_of(a, b, lane)]);
+        const TopkRow qr = unpack_rowinfo(a.rowinfo[slot_of(a, b, gamma + lane)]);
+        const float zp = Row<DT>(draft_row<DT>(a, b, lane), a.V).load_one(t);
+        const float zq = Row<DT>(target_row<DT>(a, b, lane), a.V).load_one(t);
+        const bool qzero = zq == -INFINITY || entry_key(zq, (uint32_t)t) < qr.thr;
+        const bool pzero = zp == -INFINITY || entry_key(zp, (uint32_t)t) < pr.thr;
+        const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)lane, 0u, PURPOSE_ACCEPT);
+        const float u = accept_uniform(blk.w[0]);
+        float ratio;
+        if (qzero) ratio = 0.0f;
+        else if (pzero) ratio = INFINITY;
+        else ratio = __builtin_amdgcn_exp2f(c * (zq - zp) - (qr.R - pr.R)) * (pr.S / qr.S);
+        accept = !qzero && (pzero || u < ratio);
+        if (a.token_probs) {
+          a.token_probs[((size_t)b * gamma + lane) * 2 + 0] = pzero ? 0.0f : __builtin_amdgcn_exp2f(fmaf(zp, c, -pr.R)) / pr.S;
+          a.token_probs[((size_t)b * gamma + lane) * 2 + 1] = qzero ? 0.0f : __builtin_amdgcn_exp2f(fmaf(zq, c, -qr.R)) / qr.S;
+        }
+        if (a.accept_ur) {
+          a.accept_ur[((size_t)b * gamma + lane) * 2 + 0] = u;
+          a.accept_ur[((size_t)b * gamma + lane) * 2 + 1] = ratio;
+        }
+      }
+      const unsigned long long mask = __ballot(active && accept);
+      const int n = (mask == ~0ull) ? kWave : __builtin_ctzll(~mask);
+      nn = n < gamma ? n : gamma;
+      for (int i = lane; i <= gamma; i += kWave) {
+        if (i < nn) out[i] = a.tokens[(size_t)b * gamma + i];
+        else if (i > nn) out[i] = -1;
+      }
+    } else {
+      for (int i = lane; i <= gamma; i += kWave) out[i] = -1;
+      if (active) {
+        if (a.token_probs) {
+          a.token_probs[((size_t)b * gamma + lane) * 2 + 0] = NAN;
+          a.token_probs[((size_t)b * gamma + lane) * 2 + 1] = NAN;
+        }
+        if (a.accept_ur) {
+          a.accept_ur[((size_t)b * gamma + lane) * 2 + 0] = NAN;
+          a.accept_ur[((size_t)b * gamma + lane) * 2 + 1] = NAN;
+        }
+      }
+    }
+    if (lane == 0) {
+      a.n_accepted[b] = nn;
+      a.nseq[b] = nn;
+      a.cnt3[b] = 0u;
+      sh.bcast_n = nn;
+    }
+  }
+  __syncthreads();
+  const int n = sh.bcast_n;
+  if (n < 0 || n >= gamma) return;  // invalid, or every draft kept (bonus kernel)
+
+  const TopkRow pr = unpack_rowinfo(a.rowinfo[slot_of(a, b, n)]);
+  const TopkRow qr = unpack_rowinfo(a.rowinfo[slot_of(a, b, gamma + n)]);
+  const int2 *qlist = a.lists ? a.lists + slot_of(a, b, gamma + n) * (size_t)a.klist : nullptr;
+  const Row<DT> P(draft_row<DT>(a, b, n), a.V);
+  const Row<DT> Q(target_row<DT>(a, b, n), a.V);
+  unsigned long long k = gumbel_residual_topk<DT>(sh, a, b, n, pr, qr, qlist, P, Q);
+  if (k == 0ull) k = gumbel_over_kept_q<DT>(sh, a, b, n, qr, qlist, Q);
+  if (tid == 0) out[n] = (int32_t)packed_index(k);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kTopkThreads) void k_topk_rows(Args a) {
+  __shared__ TopkShared sh;
+  const int nrow = 2 * a.gamma;
+  const int b = blockIdx.x / nrow;
+  const int s = blockIdx.x - b * nrow;  // slot: draft j = s (s < gamma), target j = s - gamma
+  const void *ptr = s < a.gamma ? draft_row<DT>(a, b, s) : target_row<DT>(a, b, s - a.gamma);
+  const Row<DT> row(ptr, a.V);
+  int2 *list = a.lists ? a.lists + slot_of(a, b, s) * (size_t)a.klist : nullptr;
+  const TopkRow r = topk_row<DT>(sh, row, a.V, a.top_k, a.c, list);
+  if (threadIdx.x == 0) a.rowinfo[slot_of(a, b, s)] = pack_rowinfo(r);
+  if (arrive_last(&a.cnt3[b], (unsigned int)nrow)) finalize_topk<DT>(sh, a, b);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kTopkThreads) void k_topk_bonus(Args a) {
+  __shared__ TopkShared sh;
+  const int b = blockIdx.x;
+  if (a.nseq[b] != a.gamma) return;
+  const int gamma = a.gamma;
+  const Row<DT> Q(target_row<DT>(a, b, gamma), a.V);
+  int2 *list = a.lists ? a.lists + slot_of(a, b, 2 * gamma) * (size_t)a.klist : nullptr;
+  const TopkRow qr = topk_row<DT>(sh, Q, a.V, a.top_k, a.c, list);
+  __syncthreads();
+  const unsigned long long k = gumbel_over_kept_q<DT>(sh, a, b, gamma, qr, list, Q);
+  if (threadIdx.x == 0) a.out_tokens[(size_t)b * (gamma + 1) + gamma] = (int32_t)packed_index(k);
+}
+
+}  // namespace sv

@@ -1,0 +1,178 @@
+"""GPU-versus-oracle comparison used by the GPU parity tests, smoke() and bench.
+
+Bar (per sequence, against the fp64 oracle on the same stored inputs and the
+same Philox streams):
+  * n_accepted and out_tokens equal bit for bit, except
+      - from the first judged position j where the oracle's |u_j - ratio_j| <
+        1e-5 onward (a knife-edge acceptance; everything after it depends on
+        it), and
+      - the sampled token when the oracle's two best Gumbel keys are within
+        1e-5 (a knife-edge arg-max);
+  * the rate of non-exempt mismatches is <= 1e-4;
+  * p_j(t_j), q_j(t_j) within 1e-5 relative of the oracle where the oracle's
+    value is >= 1e-30; the acceptance uniforms equal exactly.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from oracle import oracle as O
+
+KNIFE = 1e-5
+PROB_RTOL = 1e-5
+PROB_FLOOR = 1e-30
+
+
+@dataclass
+class GpuResult:
+    out_tokens: np.ndarray
+    n_accepted: np.ndarray
+    token_probs: np.ndarray | None = None   # [B, gamma, 2]
+    accept_ur: np.ndarray | None = None     # [B, gamma, 2]
+
+
+@dataclass
+class Report:
+    sequences: int = 0
+    exempt_accept: int = 0
+    exempt_token: int = 0
+    mismatches: int = 0
+    mismatch_examples: list = field(default_factory=list)
+    prob_checked: int = 0
+    prob_max_rel: float = 0.0
+    prob_failures: int = 0
+    u_failures: int = 0
+
+    def merge(self, o: "Report") -> "Report":
+        self.sequences += o.sequences
+        self.exempt_accept += o.exempt_accept
+        self.exempt_token += o.exempt_token
+        self.mismatches += o.mismatches
+        self.mismatch_examples += o.mismatch_examples[: max(0, 10 - len(self.mismatch_examples))]
+        self.prob_checked += o.prob_checked
+        self.prob_max_rel = max(self.prob_max_rel, o.prob_max_rel)
+        self.prob_failures += o.prob_failures
+        self.u_failures += o.u_failures
+        return self
+
+    @property
+    def mismatch_rate(self) -> float:
+        return self.mismatches / max(1, self.sequences)
+
+    def ok(self) -> bool:
+        return self.mismatch_rate <= 1e-4 and self.prob_failures == 0 and self.u_failures == 0
+
+    def summary(self) -> dict:
+        return {"sequences": self.sequences, "mismatches": self.mismatches,
+                "mismatch_rate": self.mismatch_rate, "exempt_accept": self.exempt_accept,
+                "exempt_token": self.exempt_token, "prob_checked": self.prob_checked,
+                "prob_max_rel": self.prob_max_rel, "prob_failures": self.prob_failures,
+                "u_failures": self.u_failures, "examples": self.mismatch_examples[:5]}
+
+
+def to_device(w, device="cuda"):
+    """Workload arrays as torch tensors on the GPU (bf16 bits reinterpreted)."""
+    import torch
+    if w.target.dtype == np.uint16:
+        tgt = torch.from_numpy(w.target.view(np.int16)).view(torch.bfloat16)
+        drf = torch.from_numpy(w.draft.view(np.int16)).view(torch.bfloat16)
+    else:
+        tgt = torch.from_numpy(w.target)
+        drf = torch.from_numpy(w.draft)
+    tok = torch.from_numpy(w.tokens)
+    return tgt.to(device), drf.to(device), tok.to(device)
+
+
+def run_gpu(w, seed: int, seq_offset: int = 0, debug: bool = True, tensors=None) -> GpuResult:
+    import torch
+    import rejection_sampling_verify_17_amd as S
+    tgt, drf, tok = tensors if tensors is not None else to_device(w)
+    if debug:
+        out, n, tp, ur = S.verify_debug(tgt, drf, tok, w.temperature, w.top_k, seed=seed, seq_offset=seq_offset)
+        torch.cuda.synchronize()
+        return GpuResult(out.cpu().numpy(), n.cpu().numpy(), tp.cpu().numpy(), ur.cpu().numpy())
+    out, n = S.verify(tgt, drf, tok, w.temperature, w.top_k, seed=seed, seq_offset=seq_offset)
+    torch.cuda.synchronize()
+    return GpuResult(out.cpu().numpy(), n.cpu().numpy())
+
+
+def compare(w, seed: int, g: GpuResult, seq_offset: int = 0, rows=None, nthreads: int = 0,
+            check_probs: bool = True) -> Report:
+    """Compare GPU results for sequences `rows` (default: all) with the oracle."""
+    B = w.tokens.shape[0]
+    rows = np.arange(B) if rows is None else np.asarray(rows)
+    rep = Report()
+    # the oracle runs the selected sequences with their own stream indices
+    if len(rows) == B:
+        groups = [(0, B)]
+    else:
+        groups = [(int(r), int(r) + 1) for r in rows]
+    for lo, hi in groups:
+        res = O.verify(w.target[lo:hi], w.draft[lo:hi], w.tokens[lo:hi], w.temperature, w.top_k, seed=seed,
+                       seq_offset=seq_offset + lo, nthreads=nthreads)
+        if check_probs and g.token_probs is not None:
+            pt, qt = O.token_probs(w.target[lo:hi], w.draft[lo:hi], w.tokens[lo:hi], w.temperature, w.top_k,
+                                   nthreads=nthreads)
+        for i in range(hi - lo):
+            b = lo + i
+            rep.sequences += 1
+            _compare_seq(rep, w, b, i, res, g)
+            if check_probs and g.token_probs is not None:
+                _compare_probs(rep, w, seed, seq_offset, b, pt[i], qt[i], g)
+    return rep
+
+
+def _compare_seq(rep: Report, w, b: int, i: int, res, g: GpuResult):
+    gamma = w.tokens.shape[1]
+    n_o = int(res.n_accepted[i])
+    n_g = int(g.n_accepted[b])
+    if n_o < 0 or n_g < 0:
+        if n_o != n_g or not np.array_equal(res.out_tokens[i], g.out_tokens[b]):
+            rep.mismatches += 1
+            rep.mismatch_examples.append(("invalid-flag", b, n_o, n_g))
+        return
+    judged = min(n_o + 1, gamma)
+    edge = [j for j in range(judged) if abs(res.u[i, j] - res.ratio[i, j]) < KNIFE]
+    if edge:
+        j0 = edge[0]
+        rep.exempt_accept += 1
+        # positions before j0 are still exact
+        if not np.array_equal(res.out_tokens[i, :j0], g.out_tokens[b, :j0]) or min(n_g, n_o) < j0:
+            rep.mismatches += 1
+            rep.mismatch_examples.append(("prefix-before-knife-edge", b, j0, n_o, n_g))
+        return
+    if n_o != n_g:
+        rep.mismatches += 1
+        rep.mismatch_examples.append(("n", b, n_o, n_g))
+        return
+    if not np.array_equal(res.out_tokens[i, :n_o], g.out_tokens[b, :n_o]) or \
+            not np.all(g.out_tokens[b, n_o + 1:] == -1):
+        rep.mismatches += 1
+        rep.mismatch_examples.append(("prefix", b))
+        return
+    if res.out_tokens[i, n_o] != g.out_tokens[b, n_o]:
+        if res.gap[i] < KNIFE:
+            rep.exempt_token += 1
+        else:
+            rep.mismatches += 1
+            rep.mismatch_examples.append(("token", b, n_o, int(res.out_tokens[i, n_o]),
+                                          int(g.out_tokens[b, n_o]), float(res.gap[i])))
+
+
+def _compare_probs(rep: Report, w, seed: int, seq_offset: int, b: int, pt, qt, g: GpuResult):
+    gamma = w.tokens.shape[1]
+    for j in range(gamma):
+        for o_val, g_val in ((pt[j], g.token_probs[b, j, 0]), (qt[j], g.token_probs[b, j, 1])):
+            if o_val >= PROB_FLOOR:
+                rel = abs(float(g_val) - o_val) / o_val
+                rep.prob_checked += 1
+                rep.prob_max_rel = max(rep.prob_max_rel, rel)
+                if not rel <= PROB_RTOL:
+                    rep.prob_failures += 1
+                    if len(rep.mismatch_examples) < 10:
+                        rep.mismatch_examples.append(("prob", b, j, o_val, float(g_val)))
+        u_o = O.uniform_accept(O.word(seed, seq_offset + b, j, 0, O.ACCEPT))
+        if float(g.accept_ur[b, j, 0]) != u_o:
+            rep.u_failures += 1

@@ -1,0 +1,214 @@
+"""Parity of the HIP path (through the C ABI) with the oracle, on the GPU.
+
+Small-size cases compare every sequence and every per-position probability;
+full-size workloads run in the launch configuration the benchmark times and
+compare against the oracle on every sequence (the oracle is fast enough with
+all host threads).  The bar is documented in tests/parity.py."""
+import sys
+
+import numpy as np
+import pytest
+
+import parity as PT
+from oracle import oracle as O
+from rejection_sampling_verify_17_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _check(rep, label):
+    s = rep.summary()
+    _say(label, s)
+    assert rep.ok(), f"{label}: {s}"
+    assert rep.mismatches == 0, f"{label}: {s}"
+
+
+SMALL = [("c0", None, [3000, 3001, 3002, 3003]),
+         ("c1", None, [3001, 3101, 3201]),
+         ("c2", 6, [3002, 3102]),
+         ("c3", 3, [3003, 3103]),
+         ("c4a", 48, [3004]),
+         ("c4b", 48, [3004, 3104]),
+         ("c4c", 48, [3004])]
+
+
+@pytest.mark.parametrize("name,B,seeds", SMALL, ids=[s[0] for s in SMALL])
+def test_parity_small(name, B, seeds):
+    w = I.make(name, B=B)
+    _say(f"case {name} B={w.B} gamma={w.gamma} V={w.V} dtype={w.spec.dtype} T={w.temperature} K={w.top_k}")
+    tensors = PT.to_device(w)
+    for seed in seeds:
+        g = PT.run_gpu(w, seed, tensors=tensors)
+        _check(PT.compare(w, seed, g), f"{name} seed {seed}")
+
+
+FULL = ["c2", "c3", "c4a", "c4b", "c4c"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_parity_full_size(name):
+    """Full workload, benchmark launch geometry, every sequence against the oracle."""
+    w = I.make(name)
+    _say(f"case {name} full B={w.B} gamma={w.gamma} V={w.V}")
+    tensors = PT.to_device(w)
+    seed = 3000 + int(name[1])
+    g = PT.run_gpu(w, seed, tensors=tensors)
+    rep = PT.compare(w, seed, g)
+    _check(rep, f"{name} full")
+    n = g.n_accepted
+    _say(f"{name}: mean accepted {n.mean():.3f}, all-kept {np.mean(n == w.gamma):.3f}")
+
+
+def test_60k_total_variation_on_gpu():
+    """The page's 60,000-draw TV test (blog post 46, §4) on GPU outputs: at the
+    most divergent position of c0, TV(empirical, q) <= the direct-sampling p99,
+    and the 60,000 outputs equal the oracle's."""
+    import oracle_checks as C
+    w = I.make("c0")
+    tvs = [C.tv(O.row_probs(w.draft[0, j], 1.0), O.row_probs(w.target[0, j], 1.0)) for j in range(w.gamma)]
+    jstar = int(np.argmax(tvs))
+    rep_w = I.replicate_position(w, 0, jstar, 60_000, seed=3001)
+    _say(f"case c0-60k j*={jstar} TV(p,q)={tvs[jstar]:.4f}")
+    g = PT.run_gpu(rep_w, 3000, debug=False)
+    q = O.row_probs(w.target[0, jstar], 1.0)
+    counts = np.bincount(g.out_tokens[:, 0], minlength=w.V)
+    got = C.tv(counts / 60_000, q)
+    thr = C.direct_tv_threshold(q)
+    _say(f"TV(gpu samples, q) = {got:.5f}; direct-sampling p99 = {thr:.5f}")
+    assert got <= thr
+    _check(PT.compare(rep_w, 3000, g, check_probs=False), "c0-60k")
+
+
+def test_deterministic_and_geometry_independent():
+    """Same call twice is bit-identical; a sub-batch with seq_offset reproduces
+    the full batch's rows although its launch geometry differs."""
+    w = I.make("c2", B=24)
+    t = PT.to_device(w)
+    a = PT.run_gpu(w, 77, tensors=t, debug=False)
+    b = PT.run_gpu(w, 77, tensors=t, debug=False)
+    assert np.array_equal(a.out_tokens, b.out_tokens) and np.array_equal(a.n_accepted, b.n_accepted)
+    sub = I.from_arrays(w.target[5:9], w.draft[5:9], w.tokens[5:9], w.temperature, w.top_k)
+    c = PT.run_gpu(sub, 77, seq_offset=5, debug=False)
+    assert np.array_equal(c.out_tokens, a.out_tokens[5:9])
+
+
+def test_invalid_tokens_flagged():
+    w = I.make("c1")
+    tok = w.tokens.copy()
+    tok[2, 1] = w.V
+    tok[5, 0] = -7
+    w2 = I.from_arrays(w.target, w.draft, tok, w.temperature, w.top_k)
+    g = PT.run_gpu(w2, 5)
+    assert g.n_accepted[2] == -1 and np.all(g.out_tokens[2] == -1)
+    assert g.n_accepted[5] == -1 and np.all(g.out_tokens[5] == -1)
+    _check(PT.compare(w2, 5, g, check_probs=False), "invalid tokens")
+
+
+def _edge_workloads():
+    rng = np.random.default_rng(123)
+    out = []
+    # V = 2, gamma = 1
+    t = rng.normal(0, 1, (16, 2, 2)).astype(np.float32)
+    d = rng.normal(0, 1, (16, 1, 2)).astype(np.float32)
+    out.append(("V2", I.from_arrays(t, d, rng.integers(0, 2, (16, 1)).astype(np.int32))))
+    # gamma = 64 (the maximum), small V
+    t = rng.normal(0, 1, (3, 65, 100)).astype(np.float32)
+    d = (t[:, :64] + rng.normal(0, 0.05, (3, 64, 100))).astype(np.float32)
+    w = I.from_arrays(t, d, np.zeros((3, 64), np.int32))
+    w.tokens[:] = I.sample_rows(d.reshape(-1, 100), 1.0, 0, rng).reshape(3, 64)
+    out.append(("gamma64", w))
+    # -inf logits (masked vocabulary) in both inputs
+    t = rng.normal(0, 2, (8, 4, 300)).astype(np.float32)
+    d = rng.normal(0, 2, (8, 3, 300)).astype(np.float32)
+    t[:, :, 50:120] = -np.inf
+    d[:, :, 100:200] = -np.inf
+    w = I.from_arrays(t, d, np.zeros((8, 3), np.int32))
+    w.tokens[:] = I.sample_rows(d.reshape(-1, 300), 1.0, 0, rng).reshape(8, 3)
+    out.append(("neg-inf", w))
+    # constant rows: uniform distributions
+    t = np.full((4, 3, 257), 0.5, np.float32)
+    out.append(("constant", I.from_arrays(t, t[:, :2].copy(), rng.integers(0, 257, (4, 2)).astype(np.int32))))
+    # bf16 with odd V: rows start on 2-byte boundaries every other row
+    t = rng.normal(0, 3, (5, 3, 4099)).astype(np.float32)
+    d = (t[:, :2] + rng.normal(0, 1, (5, 2, 4099))).astype(np.float32)
+    tb, db = I.f32_to_bf16_bits(t), I.f32_to_bf16_bits(d)
+    w = I.from_arrays(tb, db, np.zeros((5, 2), np.int32), temperature=0.9)
+    w.tokens[:] = I.sample_rows(I.bf16_bits_to_f32(db).reshape(-1, 4099), 0.9, 0, rng).reshape(5, 2)
+    out.append(("bf16-oddV", w))
+    # top-k with heavy ties (integer logits), K = 1, 7, V - 1, both dtypes
+    for K in (1, 7, 499):
+        t = rng.integers(-4, 5, (6, 3, 500)).astype(np.float32)
+        d = rng.integers(-4, 5, (6, 2, 500)).astype(np.float32)
+        w = I.from_arrays(t, d, np.zeros((6, 2), np.int32), top_k=K)
+        w.tokens[:] = I.sample_rows(d.reshape(-1, 500), 1.0, K, rng).reshape(6, 2)
+        out.append((f"ties-topk{K}", w))
+        tb, db = I.f32_to_bf16_bits(t), I.f32_to_bf16_bits(d)
+        out.append((f"ties-topk{K}-bf16", I.from_arrays(tb, db, w.tokens.copy(), top_k=K)))
+    # top-k larger than the lists the library keeps (1024): scans rows instead
+    t = rng.normal(0, 2, (2, 3, 6000)).astype(np.float32)
+    d = (t[:, :2] + rng.normal(0, 1, (2, 2, 6000))).astype(np.float32)
+    w = I.from_arrays(t, d, np.zeros((2, 2), np.int32), top_k=3000)
+    w.tokens[:] = I.sample_rows(d.reshape(-1, 6000), 1.0, 3000, rng).reshape(2, 2)
+    out.append(("topk-large", w))
+    # top-k where more than the LDS candidate capacity tie at the threshold
+    t = np.zeros((2, 3, 20000), np.float32)
+    t[:, :, ::7] = 1.0
+    d = t[:, :2].copy()
+    d[:, :, ::11] = 2.0
+    w = I.from_arrays(t, d, np.zeros((2, 2), np.int32), top_k=40)
+    w.tokens[:] = I.sample_rows(d.reshape(-1, 20000), 1.0, 40, rng).reshape(2, 2)
+    out.append(("topk-overflow", w))
+    # p == q: everything kept, bonus from row gamma
+    t = rng.normal(0, 2, (32, 4, 1000)).astype(np.float32)
+    w = I.from_arrays(t, t[:, :3].copy(), np.zeros((32, 3), np.int32))
+    w.tokens[:] = I.sample_rows(t[:, :3].reshape(-1, 1000), 1.0, 0, rng).reshape(32, 3)
+    out.append(("p-equals-q", w))
+    return out
+
+
+EDGES = _edge_workloads()
+
+
+@pytest.mark.parametrize("name,w", EDGES, ids=[e[0] for e in EDGES])
+def test_edge_cases(name, w):
+    _say(f"case edge {name} B={w.B} gamma={w.gamma} V={w.V} K={w.top_k} dtype={w.target.dtype}")
+    for seed in (11, 12):
+        g = PT.run_gpu(w, seed)
+        _check(PT.compare(w, seed, g), f"edge {name} seed {seed}")
+    if name == "p-equals-q":
+        assert np.all(g.n_accepted == w.gamma)
+
+
+def test_workspace_reuse_across_shapes():
+    """One workspace, calls of different shapes back to back: each call leaves
+    it ready for the next."""
+    import torch
+    import rejection_sampling_verify_17_amd as S
+    ws = torch.zeros(S.workspace_bytes(256, 8, 152064, 50, S.SV_BF16) + (1 << 20), dtype=torch.uint8,
+                     device="cuda")
+    for name, B, seed in (("c1", 8, 1), ("c3", 2, 2), ("c2", 4, 3), ("c1", 8, 4), ("c4b", 16, 5)):
+        w = I.make(name, B=B)
+        tgt, drf, tok = PT.to_device(w)
+        out, n = S.verify(tgt, drf, tok, w.temperature, w.top_k, seed=seed, workspace=ws)
+        torch.cuda.synchronize()
+        g = PT.GpuResult(out.cpu().numpy(), n.cpu().numpy())
+        _check(PT.compare(w, seed, g, check_probs=False), f"reuse {name}")
+    assert int(ws.count_nonzero()) == 0
+
+
+def test_non_default_stream():
+    import torch
+    import rejection_sampling_verify_17_amd as S
+    w = I.make("c1")
+    tgt, drf, tok = PT.to_device(w)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out, n = S.verify(tgt, drf, tok, w.temperature, seed=9)
+    s.synchronize()
+    g = PT.GpuResult(out.cpu().numpy(), n.cpu().numpy())
+    _check(PT.compare(w, 9, g, check_probs=False), "stream")
