@@ -180,7 +180,7 @@ def run_workload(name: str, steps: int, warmup: int, hip: Hip, seed: int = 3000)
     n_acc = nacc.cpu().numpy()
     ab = algorithmic_bytes(w, n_acc)
     positions = w.B * w.gamma
-    dominant = names[0]
+    dominant = "k_topk_rows" if "k_topk_rows" in names else "k_stats"
     dom_bytes = ab["pass1"]
     dom_us = per_kernel[dominant]["avg_us"]
     res = {

@@ -52,17 +52,17 @@
  * HIP device, or memory the device can address).  The library allocates
  * nothing and keeps no state between calls beyond the workspace contents.
  *
- * Workspace: sv_workspace_bytes() bytes of device memory.  It must be
- * zero-filled before its first use (sv_workspace_init does that on the
- * stream); every call that returns SV_OK leaves it zero-filled again for the
- * next call.  One workspace serves one call at a time: calls that overlap
- * (different streams, same workspace) race.
+ * Workspace: sv_workspace_bytes() bytes of device memory, 256-byte aligned.
+ * Its contents before a call do not matter (each call first clears the part
+ * it counts in), and one workspace may serve calls of any shape in turn.  One
+ * workspace serves one call at a time: calls that overlap (different streams,
+ * same workspace) race.
  *
  * Errors: argument errors return SV_EINVAL before anything is enqueued
  * (null pointer, B < 1, gamma not in [1, 64], V < 2 or V > 2^28, temperature
  * not finite or <= 0, unknown dtype, a logits pointer not aligned to its
- * element size, workspace too small).  A failed launch returns SV_EHIP (the
- * workspace must then be re-initialised).  Calls never synchronise.
+ * element size, workspace too small or misaligned).  A failed launch returns
+ * SV_EHIP.  Calls never synchronise.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -85,10 +85,6 @@ typedef enum { SV_OK = 0, SV_EINVAL = 1, SV_EHIP = 2 } sv_status;
 
 /* Bytes of device workspace sv_verify needs for this shape (0 on bad shape). */
 SV_API size_t sv_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype);
-
-/* Zero-fill `workspace_bytes` bytes of `workspace` on `stream` (a hipStream_t;
- * NULL = the default stream), with a kernel of this library.  Async. */
-SV_API sv_status sv_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
 
 /* One verification step; see the top of this file.  All pointers are device
  * pointers; `stream` is a hipStream_t (NULL = default stream). */

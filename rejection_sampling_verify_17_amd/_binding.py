@@ -1,7 +1,7 @@
 """ctypes binding of libspecverify.so: argument marshalling only.
 
 Every step of the verification runs in the library's HIP kernels; this module
-checks tensors, allocates outputs and a zero-filled workspace with torch, and
+checks tensors, allocates outputs and a workspace with torch, and
 passes raw device pointers plus the current HIP stream.  If the library is
 missing it raises: there is no fallback path.
 """
@@ -46,8 +46,6 @@ def lib() -> ctypes.CDLL:
                 common = [vp, vp, vp, i32, i32, i32, i32, flt, i32, u64, u64, vp, vp, vp, sz, vp]
                 L.sv_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
                 L.sv_workspace_bytes.restype = sz
-                L.sv_workspace_init.argtypes = [vp, sz, vp]
-                L.sv_workspace_init.restype = i32
                 L.sv_verify.argtypes = common
                 L.sv_verify.restype = i32
                 L.sv_verify_debug.argtypes = common + [vp, vp]
@@ -113,8 +111,8 @@ def _stream_ptr(device, stream=None) -> int:
 
 
 def get_workspace(device, nbytes: int, stream=None):
-    """A zero-filled workspace of at least nbytes for (device, stream), reused
-    across calls (each successful call leaves it zero-filled)."""
+    """A workspace of at least nbytes for (device, stream), reused across calls
+    (its contents between calls do not matter)."""
     torch = _torch()
     key = (device.index, _stream_ptr(device, stream))
     ws = _workspaces.get(key)

@@ -25,8 +25,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
   bool topk;
-  int nch, cv, nch2, cv2, klist;
-  size_t off_part, off_seqstat, off_nseq, off_cnt1, off_cnt2, off_cnt3, off_best, off_rowinfo, off_lists;
+  int nvec, nch, cv, ngb, nch2, cv2, klist;
+  size_t off_part, off_bestpart, off_nseq, off_rowinfo, off_lists;
   size_t total;
 };
 
@@ -35,37 +35,37 @@ bool shape_ok(int32_t B, int32_t gamma, int32_t V, int32_t dtype) {
          (dtype == SV_F32 || dtype == SV_BF16);
 }
 
-// Split a row of nvec 16-byte vectors into chunks so that `rows` rows give
-// about kTargetTiles blocks, each thread keeping at least two vectors.
-void split(int rows, int nvec, int *nch, int *cv) {
-  const int max_ch = std::max(1, nvec / (2 * kThreads));
-  int n = (kTargetTiles + rows - 1) / rows;
-  n = std::max(1, std::min(n, max_ch));
-  int per = (nvec + n - 1) / n;
-  *cv = per;
-  *nch = (nvec + per - 1) / per;
+// Split a row of n units (16-byte vectors or group blocks) into chunks so that
+// `rows` rows give about kTargetTiles blocks, each thread keeping at least two
+// units.
+void split(int rows, int n, int *nch, int *per_chunk) {
+  const int max_ch = std::max(1, n / (2 * kThreads));
+  int k = (kTargetTiles + rows - 1) / rows;
+  k = std::max(1, std::min(k, max_ch));
+  const int per = (n + k - 1) / k;
+  *per_chunk = per;
+  *nch = (n + per - 1) / per;
 }
 
 Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype) {
   Plan p{};
   const int ne = dtype == SV_BF16 ? 8 : 4;
-  const int nvec = (V + ne - 1) / ne;
+  p.nvec = (V + 2 * ne - 2) / ne;  // vectors covering a row at any 16-byte offset
+  p.ngb = (V + ne - 1) / ne;       // group blocks of ne entries
   p.topk = top_k > 0 && top_k < V;
   p.klist = (p.topk && top_k <= kListMax) ? top_k : 0;
   if (!p.topk) {
-    split(B * gamma, nvec, &p.nch, &p.cv);
-    split(B, nvec, &p.nch2, &p.cv2);
+    split(B * gamma, p.nvec, &p.nch, &p.cv);
+    split(B, p.ngb, &p.nch2, &p.cv2);
   }
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  // Nothing here is read before this call writes it: the workspace needs no
+  // initialisation and may serve calls of any shape in turn.
   p.off_part = take(p.topk ? 0 : (size_t)B * gamma * p.nch * sizeof(float4));
-  p.off_seqstat = take((size_t)B * sizeof(float4));
+  p.off_bestpart = take(p.topk ? 0 : (size_t)B * p.nch2 * sizeof(unsigned long long));
   p.off_nseq = take((size_t)B * sizeof(int32_t));
-  p.off_cnt1 = take((size_t)B * sizeof(uint32_t));
-  p.off_cnt2 = take((size_t)B * sizeof(uint32_t));
-  p.off_cnt3 = take((size_t)B * sizeof(uint32_t));
-  p.off_best = take((size_t)B * sizeof(unsigned long long));
-  const size_t slots = (size_t)B * (2 * gamma + 1);
+  const size_t slots = (size_t)B * (2 * gamma);
   p.off_rowinfo = take(p.topk ? slots * sizeof(uint4) : 0);
   p.off_lists = take(p.klist ? slots * (size_t)p.klist * sizeof(int2) : 0);
   p.total = off;
@@ -93,12 +93,16 @@ struct Launches {
       before();
       hipLaunchKernelGGL(k_sample<DT>, dim3(a.B * p.nch2), dim3(kThreads), 0, stream, a);
       ok = ok && after();
+      before();
+      const int waves = kThreads / kWave;
+      hipLaunchKernelGGL(k_pick<DT>, dim3((a.B + waves - 1) / waves), dim3(kThreads), 0, stream, a);
+      ok = ok && after();
     } else {
       before();
       hipLaunchKernelGGL(k_topk_rows<DT>, dim3(a.B * 2 * a.gamma), dim3(kTopkThreads), 0, stream, a);
       ok = ok && after();
       before();
-      hipLaunchKernelGGL(k_topk_bonus<DT>, dim3(a.B), dim3(kTopkThreads), 0, stream, a);
+      hipLaunchKernelGGL(k_topk_finish<DT>, dim3(a.B), dim3(kTopkThreads), 0, stream, a);
       ok = ok && after();
     }
     if (n_launches) *n_launches = li;
@@ -141,14 +145,12 @@ sv_status verify_impl(const void *target, const void *draft, const int32_t *toke
   a.token_probs = token_probs;
   a.accept_ur = accept_ur;
   a.part = (float4 *)(ws + p.off_part);
-  a.seqstat = (float4 *)(ws + p.off_seqstat);
+  a.bestpart = (unsigned long long *)(ws + p.off_bestpart);
   a.nseq = (int32_t *)(ws + p.off_nseq);
-  a.cnt1 = (unsigned int *)(ws + p.off_cnt1);
-  a.cnt2 = (unsigned int *)(ws + p.off_cnt2);
-  a.cnt3 = (unsigned int *)(ws + p.off_cnt3);
-  a.best = (unsigned long long *)(ws + p.off_best);
+  a.nvec = p.nvec;
   a.nch = p.nch;
   a.cv = p.cv;
+  a.ngb = p.ngb;
   a.nch2 = p.nch2;
   a.cv2 = p.cv2;
   a.rowinfo = p.topk ? (uint4 *)(ws + p.off_rowinfo) : nullptr;
@@ -168,20 +170,6 @@ extern "C" {
 size_t sv_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype) {
   if (!shape_ok(B, gamma, V, dtype)) return 0;
   return make_plan(B, gamma, V, top_k, dtype).total;
-}
-
-sv_status sv_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
-  if (!workspace || ((uintptr_t)workspace % 16)) return SV_EINVAL;
-  if (workspace_bytes == 0) return SV_OK;
-  const size_t n16 = workspace_bytes / 16;
-  const size_t ntail = (workspace_bytes % 16) / 4;
-  const size_t n = std::max(n16, ntail);
-  const int threads = 256;
-  const size_t blocks = (n + threads - 1) / threads;
-  (void)hipGetLastError();
-  hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(threads), 0, (hipStream_t)stream, (u32x4 *)workspace,
-                     n16, (uint32_t *)((char *)workspace + n16 * 16), ntail);
-  return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }
 
 sv_status sv_verify(const void *target_logits, const void *draft_logits, const int32_t *draft_tokens, int32_t B,
@@ -216,9 +204,9 @@ sv_status sv_verify_timed(const void *target_logits, const void *draft_logits, c
 const char *sv_launch_name(int32_t B, int32_t gamma, int32_t V, int32_t dtype, int32_t top_k, int32_t i) {
   if (!shape_ok(B, gamma, V, dtype)) return nullptr;
   const bool topk = top_k > 0 && top_k < V;
-  static const char *dense[] = {"k_stats", "k_sample"};
-  static const char *filt[] = {"k_topk_rows", "k_topk_bonus"};
-  if (i < 0 || i >= 2) return nullptr;
+  static const char *dense[] = {"k_stats", "k_sample", "k_pick"};
+  static const char *filt[] = {"k_topk_rows", "k_topk_finish"};
+  if (i < 0 || i >= (topk ? 2 : 3)) return nullptr;
   return topk ? filt[i] : dense[i];
 }
 

@@ -127,45 +127,67 @@ __device__ __forceinline__ void decode(const u32x4 v, float (&z)[Elem<DT>::kVec]
   }
 }
 
-// A row of V logits behind a buffer resource.  Loads past the row's last
-// 4-byte word return zeros instead of touching memory; callers mask entries
-// >= V themselves.  The range is the row rounded up to whole 4-byte words, so
-// an odd-length bf16 row's last entry stays readable (the extra two bytes lie
-// in the same word, never on another page).
+// A row of V logits read through a buffer resource with 16-byte-aligned loads.
+// The resource starts at the row's address rounded down to 16 bytes, so the
+// row sits `s` entries into its first vector: vector iv holds entries
+// [NE*iv - s, NE*iv - s + NE).  The few bytes before the row share a 16-byte
+// block (hence a page) with its first entry, so reading them is always safe;
+// the range ends at the row's last 4-byte word and loads beyond it return
+// zeros without touching memory.  Callers mask entries outside [0, V).
 template <int DT> struct Row {
+  static constexpr int NE = Elem<DT>::kVec;
+  static constexpr int ESZ = Elem<DT>::kSize;
   __amdgpu_buffer_rsrc_t rsrc;
-  const char *base;
-  bool aligned;  // row start is 4-byte aligned: vector loads allowed
+  int s;  // entries of the first vector that precede the row
 
   __device__ __forceinline__ Row(const void *p, int V) {
-    base = (const char *)p;
-    const uint32_t bytes = ((uint32_t)V * Elem<DT>::kSize + 3u) & ~3u;
-    rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, 0x00020000);
-    aligned = (((uintptr_t)base) & 3u) == 0;
+    const uintptr_t addr = (uintptr_t)p;
+    const uintptr_t a16 = addr & ~(uintptr_t)15;
+    s = (int)((addr - a16) / ESZ);
+    const uint32_t bytes = ((uint32_t)(addr - a16) + (uint32_t)V * ESZ + 3u) & ~3u;
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)a16, (short)0, (int)bytes, 0x00020000);
   }
 
-  // Logits [NE*iv, NE*iv + NE) of the row (entries past V are garbage-free zeros
-  // or neighbours; mask by index).
-  __device__ __forceinline__ void load_vec(int iv, float (&z)[Elem<DT>::kVec]) const {
-    constexpr int NE = Elem<DT>::kVec;
-    if (aligned) {
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, iv * 16, 0, 0);
-      decode<DT>(v, z);
-    } else {
-      // 2-byte-aligned bf16 row: entry by entry
-#pragma unroll
-      for (int e = 0; e < NE; ++e) {
-        const uint16_t h = __builtin_amdgcn_raw_buffer_load_b16(rsrc, (iv * NE + e) * 2, 0, 0);
-        z[e] = __uint_as_float((uint32_t)h << 16);
-      }
+  // vectors covering the row
+  __device__ __forceinline__ int nvec(int V) const { return (s + V + NE - 1) / NE; }
+
+  __device__ __forceinline__ u32x4 raw(int iv) const {
+    return __builtin_amdgcn_raw_buffer_load_b128(rsrc, iv * 16, 0, 0);
+  }
+
+  // Vector iv: z[e] is entry NE*iv + e - s.
+  __device__ __forceinline__ void load_vec(int iv, float (&z)[NE]) const { decode<DT>(raw(iv), z); }
+
+  // Entries [NE*g, NE*g + NE) in order (a "group block": NE/4 Philox groups),
+  // assembled from vectors g and g+1 with a funnel shift by s entries.
+  __device__ __forceinline__ void load_block(int g, float (&z)[NE]) const {
+    if (s == 0) {
+      decode<DT>(raw(g), z);
+      return;
     }
+    const u32x4 A = raw(g), B = raw(g + 1);
+    const uint32_t d[8] = {A.x, A.y, A.z, A.w, B.x, B.y, B.z, B.w};
+    const int sb = s * ESZ;           // byte shift, 1..15
+    const int q = sb >> 2, r = sb & 3;  // whole words, then bytes (0 or 2)
+    uint32_t w[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const uint32_t a0 = d[i], a1 = d[i + 1], a2 = d[i + 2], a3 = d[i + 3];
+      w[i] = q == 0 ? a0 : q == 1 ? a1 : q == 2 ? a2 : a3;
+    }
+    u32x4 o;
+    o.x = r ? __builtin_amdgcn_alignbyte(w[1], w[0], (uint32_t)r) : w[0];
+    o.y = r ? __builtin_amdgcn_alignbyte(w[2], w[1], (uint32_t)r) : w[1];
+    o.z = r ? __builtin_amdgcn_alignbyte(w[3], w[2], (uint32_t)r) : w[2];
+    o.w = r ? __builtin_amdgcn_alignbyte(w[4], w[3], (uint32_t)r) : w[3];
+    decode<DT>(o, z);
   }
 
   __device__ __forceinline__ float load_one(int v) const {
     if constexpr (DT == DT_F32) {
-      return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, v * 4, 0, 0));
+      return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, (v + s) * 4, 0, 0));
     } else {
-      const uint16_t h = __builtin_amdgcn_raw_buffer_load_b16(rsrc, v * 2, 0, 0);
+      const uint16_t h = __builtin_amdgcn_raw_buffer_load_b16(rsrc, (v + s) * 2, 0, 0);
       return __uint_as_float((uint32_t)h << 16);
     }
   }
@@ -286,23 +308,6 @@ __device__ __forceinline__ unsigned long long block_max_u64(unsigned long long x
   for (int i = 1; i < NW; ++i) x = sh[i] > x ? sh[i] : x;
   __syncthreads();
   return x;
-}
-
-// Last-arriver election: every block of a group calls this once after its
-// results are stored; exactly one block (the last) gets true, and it then sees
-// the stores of all others.  The counter is left for the caller to reset.
-__device__ __forceinline__ bool arrive_last(unsigned int *counter, unsigned int total) {
-  __shared__ int last;
-  __threadfence();  // every thread's stores (not only thread 0's) precede the count
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    const unsigned int prev = atomicAdd(counter, 1u);
-    last = (prev == total - 1u);
-  }
-  __syncthreads();
-  if (last) __threadfence();
-  return last != 0;
 }
 
 }  // namespace sv

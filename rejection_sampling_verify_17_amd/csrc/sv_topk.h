@@ -6,15 +6,15 @@
 // ordered like "larger logit, then smaller index"; the kept set is the K
 // largest keys, i.e. all keys >= the K-th largest ("threshold").
 //
-//   k_topk_rows   one block per row (draft rows 0..gamma-1, target rows
-//                 0..gamma-1 of a sequence).  Finds the row's threshold by an
-//                 LDS radix select, then the base-2 softmax statistics (R, S)
-//                 over the kept entries and, for small K, the kept list.  The
-//                 last block of a sequence judges the drafts (in registers,
-//                 wave ballot) and resamples a rejected position from the
-//                 residual over the target row's kept list.
-//   k_topk_bonus  one block per sequence whose drafts were all kept: top-k of
-//                 target row gamma and a Gumbel-max draw over its kept entries.
+//   k_topk_rows    one block per row (draft rows 0..gamma-1, target rows
+//                  0..gamma-1 of a sequence).  Finds the row's threshold by an
+//                  LDS radix select, then the base-2 softmax statistics (R, S)
+//                  over the kept entries and, for small K, the kept list.
+//   k_topk_finish  one block per sequence: judges the drafts (in registers,
+//                  wave ballot), then draws the replacement from the residual
+//                  over the target row's kept list, or, when every draft was
+//                  kept, selects target row gamma's top-k and draws the bonus
+//                  token over its kept entries.
 //
 // Selection: a lower bound L on the K-th largest logit comes from the
 // per-thread maxima (K threads each own an entry >= their maximum's K-th
@@ -57,7 +57,9 @@ __device__ __forceinline__ unsigned long long entry_key(float z, uint32_t v) {
 // 8; bits >= hi are equal across all keys).  If at some byte exactly the
 // remaining rank's worth of keys share the prefix, it stops early with the low
 // bits cleared: every key that shares the prefix is then within the K largest,
-// so "key >= result" still selects exactly the K largest when keys are unique.
+// so among the keys `src` enumerates (when unique) "key >= result" still selects
+// exactly the K largest.  Keys outside that set may also pass the cleared
+// threshold, so callers that test other keys need the exact K-th largest.
 template <class Src>
 __device__ unsigned long long radix_select(TopkShared &sh, const Src &src, unsigned int K, int hi, int lo) {
   const int tid = threadIdx.x;
@@ -129,14 +131,14 @@ template <int DT> struct RowKeys {  // every entry of a global row
   int V;
   template <class F> __device__ void for_each(F f) const {
     constexpr int NE = Elem<DT>::kVec;
-    const int nvec = (V + NE - 1) / NE;
+    const int nvec = row->nvec(V);
     for (int iv = threadIdx.x; iv < nvec; iv += kTopkThreads) {
       float z[NE];
       row->load_vec(iv, z);
 #pragma unroll
       for (int e = 0; e < NE; ++e) {
-        const int v = iv * NE + e;
-        if (v < V) f(entry_key(z[e], (uint32_t)v));
+        const int v = iv * NE + e - row->s;
+        if (v >= 0 && v < V) f(entry_key(z[e], (uint32_t)v));
       }
     }
   }
@@ -148,13 +150,15 @@ template <int DT> struct RowKeys {  // every entry of a global row
 struct TopkRow {
   unsigned long long thr;
   float R, S;
+  bool in_lds;          // kept entries are among sh.cand[0..ncand) (else scan the row)
+  unsigned int ncand;
 };
 
 template <int DT>
 __device__ TopkRow topk_row(TopkShared &sh, const Row<DT> &row, int V, int K, float c, int2 *list) {
   constexpr int NE = Elem<DT>::kVec;
   const int tid = threadIdx.x;
-  const int nvec = (V + NE - 1) / NE;
+  const int nvec = row.nvec(V);
 
   // Phase A: per-thread maxima.
   unsigned int mymax = 0u;
@@ -162,8 +166,10 @@ __device__ TopkRow topk_row(TopkShared &sh, const Row<DT> &row, int V, int K, fl
     float z[NE];
     row.load_vec(iv, z);
 #pragma unroll
-    for (int e = 0; e < NE; ++e)
-      if (iv * NE + e < V) mymax = max(mymax, orderable(z[e]));
+    for (int e = 0; e < NE; ++e) {
+      const int v = iv * NE + e - row.s;
+      if (v >= 0 && v < V) mymax = max(mymax, orderable(z[e]));
+    }
   }
   sh.tmax[tid] = mymax;
   if (tid == 0) { sh.ncand = 0u; sh.nkept = 0u; }
@@ -179,8 +185,8 @@ __device__ TopkRow topk_row(TopkShared &sh, const Row<DT> &row, int V, int K, fl
     row.load_vec(iv, z);
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
-      const int v = iv * NE + e;
-      if (v < V && orderable(z[e]) >= L) {
+      const int v = iv * NE + e - row.s;
+      if (v >= 0 && v < V && orderable(z[e]) >= L) {
         const unsigned int slot = atomicAdd(&sh.ncand, 1u);
         if (slot < (unsigned int)kCap) sh.cand[slot] = entry_key(z[e], (uint32_t)v);
       }
@@ -190,24 +196,40 @@ __device__ TopkRow topk_row(TopkShared &sh, const Row<DT> &row, int V, int K, fl
   const unsigned int ncand = sh.ncand;
   const bool in_lds = ncand <= (unsigned int)kCap;
 
-  // Phase D: exact threshold.
+  // Phase D: threshold among the candidates.
   unsigned long long thr;
   if (in_lds) thr = radix_select(sh, LdsKeys{sh.cand, ncand}, (unsigned)K, 64, 0);
   else thr = radix_select(sh, RowKeys<DT>{&row, V}, (unsigned)K, 64, 0);
 
-  // Phase E: statistics over kept entries (and the list).
+  // Phase E: statistics over kept entries (and the list).  The select may stop
+  // with the low bits of `thr` cleared; that separates the K kept entries from
+  // the other candidates but not from every entry of the row, so the stored
+  // threshold is made exact: the smallest kept key.
   float zmax = -INFINITY;
+  unsigned long long kmin = ~0ull;
   auto visit_max = [&](unsigned long long key) {
-    if (key >= thr) zmax = fmaxf(zmax, from_orderable((uint32_t)(key >> 32)));
+    if (key >= thr) {
+      zmax = fmaxf(zmax, from_orderable((uint32_t)(key >> 32)));
+      kmin = key < kmin ? key : kmin;
+    }
   };
   if (in_lds) LdsKeys{sh.cand, ncand}.for_each(visit_max);
   else RowKeys<DT>{&row, V}.for_each(visit_max);
   zmax = wave_max_f(zmax);
-  if ((tid % kWave) == 0) sh.red_f[tid / kWave] = zmax;
+  kmin = ~wave_max_u64(~kmin);
+  if ((tid % kWave) == 0) {
+    sh.red_f[tid / kWave] = zmax;
+    sh.red_u[tid / kWave] = kmin;
+  }
   __syncthreads();
   zmax = sh.red_f[0];
-  for (int i = 1; i < kTopkThreads / kWave; ++i) zmax = fmaxf(zmax, sh.red_f[i]);
+  kmin = sh.red_u[0];
+  for (int i = 1; i < kTopkThreads / kWave; ++i) {
+    zmax = fmaxf(zmax, sh.red_f[i]);
+    kmin = sh.red_u[i] < kmin ? sh.red_u[i] : kmin;
+  }
   __syncthreads();
+  thr = kmin;
   const float R = (zmax == -INFINITY) ? -INFINITY : ceilf(zmax * c);
 
   float S = 0.0f;
@@ -216,8 +238,9 @@ __device__ TopkRow topk_row(TopkShared &sh, const Row<DT> &row, int V, int K, fl
       const float z = from_orderable((uint32_t)(key >> 32));
       if (z != -INFINITY) S += __builtin_amdgcn_exp2f(fmaf(z, c, -R));
       if (list) {
-        const unsigned int slot = atomicAdd(&sh.nkept, 1u);
-        list[slot] = make_int2((int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull)), (int)__float_as_uint(z));
+        const unsigned int slot = atomicAdd(&sh.nkept, 1u);  // exactly K kept entries
+        if (slot < (unsigned int)K)
+          list[slot] = make_int2((int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull)), (int)__float_as_uint(z));
       }
     }
   };
@@ -229,7 +252,7 @@ __device__ TopkRow topk_row(TopkShared &sh, const Row<DT> &row, int V, int K, fl
   S = 0.0f;
   for (int i = 0; i < kTopkThreads / kWave; ++i) S += sh.red_f[i];
   __syncthreads();
-  return TopkRow{thr, R, S};
+  return TopkRow{thr, R, S, in_lds, ncand};
 }
 
 __device__ __forceinline__ uint4 pack_rowinfo(const TopkRow &r) {
@@ -237,7 +260,7 @@ __device__ __forceinline__ uint4 pack_rowinfo(const TopkRow &r) {
                     __float_as_uint(r.S));
 }
 __device__ __forceinline__ TopkRow unpack_rowinfo(uint4 u) {
-  return TopkRow{((unsigned long long)u.y << 32) | u.x, __uint_as_float(u.z), __uint_as_float(u.w)};
+  return TopkRow{((unsigned long long)u.y << 32) | u.x, __uint_as_float(u.z), __uint_as_float(u.w), false, 0u};
 }
 
 // p or q of entry (z, v) under a selected row's statistics: 0 outside the kept set.
@@ -257,24 +280,37 @@ __device__ unsigned long long block_max_u64_sh(unsigned long long x, unsigned lo
   return x;
 }
 
-// Gumbel-max over the kept entries of target row `pos` (weights q): used for
-// the bonus token and for an empty residual.  `list` holds the kept entries
-// when K <= klist; otherwise the row is scanned with the threshold.
+// Bonus key of kept entry (z, v) at position pos: z c - log2 E_v, monotone in
+// ln q_v - ln E_v; 0 for entries outside the kept set.
+__device__ __forceinline__ unsigned long long bonus_key(const Args &a, uint32_t seq, int pos,
+                                                       const TopkRow &qr, float z, uint32_t v) {
+  if (z == -INFINITY || entry_key(z, v) < qr.thr) return 0ull;
+  const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)pos, v >> 2, PURPOSE_SAMPLE);
+  const float E = exponential_variate(blk.w[v & 3u]);
+  return pack_key(fmaf(z, a.c, -__builtin_amdgcn_logf(E)), v);
+}
+
+// Gumbel-max over the kept entries of target row `pos` (weights q): the bonus
+// token, or the replacement when the residual is empty.  The kept entries come
+// from `list` (K entries), from the LDS candidates of a row just selected, or
+// from a scan of the row with the threshold.
 template <int DT>
 __device__ unsigned long long gumbel_over_kept_q(TopkShared &sh, const Args &a, int b, int pos,
                                                  const TopkRow &qr, const int2 *list, const Row<DT> &Q) {
   const uint32_t seq = seq_of(a, b);
   unsigned long long best = 0ull;
   auto consider = [&](float z, uint32_t v) {
-    if (z == -INFINITY || entry_key(z, v) < qr.thr) return;
-    const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)pos, v >> 2, PURPOSE_SAMPLE);
-    const float E = exponential_variate(blk.w[v & 3u]);
-    const unsigned long long k = pack_key(fmaf(z, a.c, -__builtin_amdgcn_logf(E)), v);
+    const unsigned long long k = bonus_key(a, seq, pos, qr, z, v);
     best = k > best ? k : best;
   };
   if (list) {
     for (int i = threadIdx.x; i < a.top_k; i += kTopkThreads)
       consider(__int_as_float(list[i].y), (uint32_t)list[i].x);
+  } else if (qr.in_lds) {
+    for (unsigned int i = threadIdx.x; i < qr.ncand; i += kTopkThreads) {
+      const unsigned long long key = sh.cand[i];
+      consider(from_orderable((uint32_t)(key >> 32)), 0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
+    }
   } else {
     for (int v = threadIdx.x; v < a.V; v += kTopkThreads) consider(Q.load_one(v), (uint32_t)v);
   }
@@ -309,95 +345,9 @@ __device__ unsigned long long gumbel_residual_topk(TopkShared &sh, const Args &a
   return block_max_u64_sh<kTopkThreads>(best, sh.red_u);
 }
 
-// rowinfo / lists slot of a sequence's rows: draft j -> j, target j -> gamma + j
-// (j <= gamma; target row gamma is slot 2 gamma).
+// rowinfo / lists slot of a sequence's rows: draft j -> j, target j -> gamma + j.
 __device__ __forceinline__ size_t slot_of(const Args &a, int b, int s) {
-  return (size_t)b * (2 * a.gamma + 1) + s;
-}
-
-template <int DT>
-__device__ void finalize_topk(TopkShared &sh, const Args &a, int b) {
-  const int gamma = a.gamma;
-  const int tid = threadIdx.x;
-  const uint32_t seq = seq_of(a, b);
-  const float c = a.c;
-  int32_t *out = a.out_tokens + (size_t)b * (gamma + 1);
-
-  if (tid < kWave) {
-    const int lane = tid;
-    const bool active = lane < gamma;
-    int t = 0;
-    bool ok = true;
-    if (active) {
-      t = a.tokens[(size_t)b * gamma + lane];
-      ok = (t >= 0) && (t < a.V);
-    }
-    const bool invalid = __ballot(active && !ok) != 0ull;
-    int nn = -1;
-    if (!invalid) {
-      bool accept = false;
-      if (active) {
-        const TopkRow pr = unpack_rowinfo(a.rowinfo[slot_of(a, b, lane)]);
-        const TopkRow qr = unpack_rowinfo(a.rowinfo[slot_of(a, b, gamma + lane)]);
-        const float zp = Row<DT>(draft_row<DT>(a, b, lane), a.V).load_one(t);
-        const float zq = Row<DT>(target_row<DT>(a, b, lane), a.V).load_one(t);
-        const bool qzero = zq == -INFINITY || entry_key(zq, (uint32_t)t) < qr.thr;
-        const bool pzero = zp == -INFINITY || entry_key(zp, (uint32_t)t) < pr.thr;
-        const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)lane, 0u, PURPOSE_ACCEPT);
-        const float u = accept_uniform(blk.w[0]);
-        float ratio;
-        if (qzero) ratio = 0.0f;
-        else if (pzero) ratio = INFINITY;
-        else ratio = __builtin_amdgcn_exp2f(c * (zq - zp) - (qr.R - pr.R)) * (pr.S / qr.S);
-        accept = !qzero && (pzero || u < ratio);
-        if (a.token_probs) {
-          a.token_probs[((size_t)b * gamma + lane) * 2 + 0] = pzero ? 0.0f : __builtin_amdgcn_exp2f(fmaf(zp, c, -pr.R)) / pr.S;
-          a.token_probs[((size_t)b * gamma + lane) * 2 + 1] = qzero ? 0.0f : __builtin_amdgcn_exp2f(fmaf(zq, c, -qr.R)) / qr.S;
-        }
-        if (a.accept_ur) {
-          a.accept_ur[((size_t)b * gamma + lane) * 2 + 0] = u;
-          a.accept_ur[((size_t)b * gamma + lane) * 2 + 1] = ratio;
-        }
-      }
-      const unsigned long long mask = __ballot(active && accept);
-      const int n = (mask == ~0ull) ? kWave : __builtin_ctzll(~mask);
-      nn = n < gamma ? n : gamma;
-      for (int i = lane; i <= gamma; i += kWave) {
-        if (i < nn) out[i] = a.tokens[(size_t)b * gamma + i];
-        else if (i > nn) out[i] = -1;
-      }
-    } else {
-      for (int i = lane; i <= gamma; i += kWave) out[i] = -1;
-      if (active) {
-        if (a.token_probs) {
-          a.token_probs[((size_t)b * gamma + lane) * 2 + 0] = NAN;
-          a.token_probs[((size_t)b * gamma + lane) * 2 + 1] = NAN;
-        }
-        if (a.accept_ur) {
-          a.accept_ur[((size_t)b * gamma + lane) * 2 + 0] = NAN;
-          a.accept_ur[((size_t)b * gamma + lane) * 2 + 1] = NAN;
-        }
-      }
-    }
-    if (lane == 0) {
-      a.n_accepted[b] = nn;
-      a.nseq[b] = nn;
-      a.cnt3[b] = 0u;
-      sh.bcast_n = nn;
-    }
-  }
-  __syncthreads();
-  const int n = sh.bcast_n;
-  if (n < 0 || n >= gamma) return;  // invalid, or every draft kept (bonus kernel)
-
-  const TopkRow pr = unpack_rowinfo(a.rowinfo[slot_of(a, b, n)]);
-  const TopkRow qr = unpack_rowinfo(a.rowinfo[slot_of(a, b, gamma + n)]);
-  const int2 *qlist = a.lists ? a.lists + slot_of(a, b, gamma + n) * (size_t)a.klist : nullptr;
-  const Row<DT> P(draft_row<DT>(a, b, n), a.V);
-  const Row<DT> Q(target_row<DT>(a, b, n), a.V);
-  unsigned long long k = gumbel_residual_topk<DT>(sh, a, b, n, pr, qr, qlist, P, Q);
-  if (k == 0ull) k = gumbel_over_kept_q<DT>(sh, a, b, n, qr, qlist, Q);
-  if (tid == 0) out[n] = (int32_t)packed_index(k);
+  return (size_t)b * (2 * a.gamma) + s;
 }
 
 template <int DT>
@@ -411,21 +361,83 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_rows(Args a) {
   int2 *list = a.lists ? a.lists + slot_of(a, b, s) * (size_t)a.klist : nullptr;
   const TopkRow r = topk_row<DT>(sh, row, a.V, a.top_k, a.c, list);
   if (threadIdx.x == 0) a.rowinfo[slot_of(a, b, s)] = pack_rowinfo(r);
-  if (arrive_last(&a.cnt3[b], (unsigned int)nrow)) finalize_topk<DT>(sh, a, b);
+}
+
+// Wave 0 judges sequence b against the selected rows; returns n (or -1).
+template <int DT>
+__device__ int judge_topk(const Args &a, int b) {
+  const int lane = threadIdx.x;
+  const int gamma = a.gamma;
+  const bool active = lane < gamma;
+  const uint32_t seq = seq_of(a, b);
+  const float c = a.c;
+  int t = 0;
+  bool ok = true;
+  if (active) {
+    t = a.tokens[(size_t)b * gamma + lane];
+    ok = (t >= 0) && (t < a.V);
+  }
+  if (__ballot(active && !ok) != 0ull) {
+    write_invalid(a, b, lane);
+    return -1;
+  }
+  bool accept = false;
+  if (active) {
+    const TopkRow pr = unpack_rowinfo(a.rowinfo[slot_of(a, b, lane)]);
+    const TopkRow qr = unpack_rowinfo(a.rowinfo[slot_of(a, b, gamma + lane)]);
+    const float zp = Row<DT>(draft_row<DT>(a, b, lane), a.V).load_one(t);
+    const float zq = Row<DT>(target_row<DT>(a, b, lane), a.V).load_one(t);
+    const bool qzero = zq == -INFINITY || entry_key(zq, (uint32_t)t) < qr.thr;
+    const bool pzero = zp == -INFINITY || entry_key(zp, (uint32_t)t) < pr.thr;
+    const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)lane, 0u, PURPOSE_ACCEPT);
+    const float u = accept_uniform(blk.w[0]);
+    float ratio;
+    if (qzero) ratio = 0.0f;
+    else if (pzero) ratio = INFINITY;
+    else ratio = __builtin_amdgcn_exp2f(c * (zq - zp) - (qr.R - pr.R)) * (pr.S / qr.S);
+    accept = !qzero && (pzero || u < ratio);
+    if (a.token_probs) {
+      a.token_probs[((size_t)b * gamma + lane) * 2 + 0] = pzero ? 0.0f : __builtin_amdgcn_exp2f(fmaf(zp, c, -pr.R)) / pr.S;
+      a.token_probs[((size_t)b * gamma + lane) * 2 + 1] = qzero ? 0.0f : __builtin_amdgcn_exp2f(fmaf(zq, c, -qr.R)) / qr.S;
+    }
+    if (a.accept_ur) {
+      a.accept_ur[((size_t)b * gamma + lane) * 2 + 0] = u;
+      a.accept_ur[((size_t)b * gamma + lane) * 2 + 1] = ratio;
+    }
+  }
+  const int n = first_rejection(__ballot(active && accept), gamma);
+  write_judged(a, b, lane, n);
+  return n;
 }
 
 template <int DT>
-__global__ __launch_bounds__(kTopkThreads) void k_topk_bonus(Args a) {
+__global__ __launch_bounds__(kTopkThreads) void k_topk_finish(Args a) {
   __shared__ TopkShared sh;
   const int b = blockIdx.x;
-  if (a.nseq[b] != a.gamma) return;
   const int gamma = a.gamma;
-  const Row<DT> Q(target_row<DT>(a, b, gamma), a.V);
-  int2 *list = a.lists ? a.lists + slot_of(a, b, 2 * gamma) * (size_t)a.klist : nullptr;
-  const TopkRow qr = topk_row<DT>(sh, Q, a.V, a.top_k, a.c, list);
+  if (threadIdx.x < kWave) {
+    const int n = judge_topk<DT>(a, b);
+    if (threadIdx.x == 0) sh.bcast_n = n;
+  }
   __syncthreads();
-  const unsigned long long k = gumbel_over_kept_q<DT>(sh, a, b, gamma, qr, list, Q);
-  if (threadIdx.x == 0) a.out_tokens[(size_t)b * (gamma + 1) + gamma] = (int32_t)packed_index(k);
+  const int n = sh.bcast_n;
+  if (n < 0) return;
+  int32_t *out = a.out_tokens + (size_t)b * (gamma + 1);
+  const Row<DT> Q(target_row<DT>(a, b, n), a.V);
+  unsigned long long k;
+  if (n < gamma) {
+    const TopkRow pr = unpack_rowinfo(a.rowinfo[slot_of(a, b, n)]);
+    const TopkRow qr = unpack_rowinfo(a.rowinfo[slot_of(a, b, gamma + n)]);
+    const int2 *qlist = a.lists ? a.lists + slot_of(a, b, gamma + n) * (size_t)a.klist : nullptr;
+    const Row<DT> P(draft_row<DT>(a, b, n), a.V);
+    k = gumbel_residual_topk<DT>(sh, a, b, n, pr, qr, qlist, P, Q);
+    if (k == 0ull) k = gumbel_over_kept_q<DT>(sh, a, b, n, qr, qlist, Q);
+  } else {
+    // every draft kept: top-k of target row gamma, then the bonus draw
+    const TopkRow qr = topk_row<DT>(sh, Q, a.V, a.top_k, a.c, nullptr);
+    k = gumbel_over_kept_q<DT>(sh, a, b, gamma, qr, nullptr, Q);
+  }
+  if (threadIdx.x == 0) out[n] = (int32_t)packed_index(k);
 }
 
 }  // namespace sv
