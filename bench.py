@@ -226,6 +226,9 @@ def read_traffic(kernel: str, workload: str) -> float | None:
 # CPU baseline: the oracle, as it stands, on a bounded sample
 # ---------------------------------------------------------------------------
 def cpu_baseline(w, seed: int, budget_s: float = 12.0) -> dict:
+    """The oracle on this host's cores: the first n sequences of the workload
+    (all of them if they fit the budget), repeated until about budget_s of
+    CPU work, reported in verified positions per second."""
     from oracle import oracle as O
     cores = len(os.sched_getaffinity(0))
     B = w.B
@@ -234,12 +237,122 @@ def cpu_baseline(w, seed: int, budget_s: float = 12.0) -> dict:
     O.verify(w.target[:n], w.draft[:n], w.tokens[:n], w.temperature, w.top_k, seed=seed, nthreads=cores)
     t1 = time.perf_counter() - t0
     if t1 < budget_s / 4 and n < B:
-        n = int(min(B, max(n + 1, n * (budget_s / max(t1, 1e-3)) * 0.8)))
+        n = int(min(B, max(n + 1, n * (budget_s / 2 / max(t1, 1e-3)))))
         t0 = time.perf_counter()
         O.verify(w.target[:n], w.draft[:n], w.tokens[:n], w.temperature, w.top_k, seed=seed, nthreads=cores)
         t1 = time.perf_counter() - t0
-    return {"value": n * w.gamma / t1, "unit": "verified draft positions/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {n} of {B} sequences of {w.spec.name} (seed {seed}), {t1:.2f} s on {cores} threads"}
+    reps = max(1, int(budget_s / max(t1, 1e-3)))
+    t0 = time.perf_counter()
+    for r in range(reps):
+        O.verify(w.target[:n], w.draft[:n], w.tokens[:n], w.temperature, w.top_k, seed=seed + r, nthreads=cores)
+    t = time.perf_counter() - t0
+    return {"value": reps * n * w.gamma / t, "unit": "verified draft positions/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"first {n} of {B} sequences of {w.spec.name}, {reps} verify seeds from {seed}, "
+                      f"{t:.1f} s on {cores} threads"}
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 CSV -> short text summaries (what profiles/ holds)
+# ---------------------------------------------------------------------------
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(d, suffix):
+    out = []
+    for root, _, files in os.walk(d):
+        out += [os.path.join(root, f) for f in files if f.endswith(suffix)]
+    return sorted(out)
+
+
+def _short(name: str) -> str:
+    for k in ("k_stats", "k_sample", "k_pick", "k_topk_rows", "k_topk_finish"):
+        if k in name:
+            return k
+    return name[:60]
+
+
+def kernel_stats_summary(d: str) -> list[str]:
+    lines = ["kernel | calls | avg_us | min_us | max_us | total_us | percent"]
+    for path in _find(d, "kernel_stats.csv"):
+        for r in _csv_rows(path):
+            lines.append(f"{_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                         f"{float(r['TotalDurationNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}")
+    return lines
+
+
+def counter_means(d: str) -> dict:
+    """{(kernel short name, counter): (mean per dispatch, dispatches)} from counter_collection.csv."""
+    acc = {}
+    for path in _find(d, "counter_collection.csv"):
+        for r in _csv_rows(path):
+            key = (_short(r["Kernel_Name"]), r["Counter_Name"])
+            acc.setdefault(key, {})
+            disp = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            acc[key][disp] = acc[key].get(disp, 0.0) + float(r["Counter_Value"])
+    return {k: (float(np.mean(list(v.values()))), len(v)) for k, v in acc.items()}
+
+
+def rocprof_summary(args) -> None:
+    """Summaries for profiles/: --rocprof-summary DIR with sub-directories
+    trace/ (kernel trace + stats), fetch/ and write/ (FETCH_SIZE, WRITE_SIZE on
+    the workload), cfetch/ and cwrite/ (the same counters on a plain copy of
+    --copy-calib-mb MiB)."""
+    d = args.rocprof_summary
+    wl = args.workload
+    out = []
+    out.append(f"# rocprofv3 kernel trace, workload {wl}")
+    out.append(f"command: rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace -o run -- "
+               f"python3 bench.py --workload {wl} --steps {args.steps} --warmup {args.warmup} --no-cpu --no-sweep")
+    out.append(f"source_digest: {source_digest()}")
+    out += kernel_stats_summary(os.path.join(d, "trace"))
+    with open(os.path.join(d, f"kernel_trace_{wl}.txt"), "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+    fetch = counter_means(os.path.join(d, "fetch"))
+    write = counter_means(os.path.join(d, "write"))
+    cf = counter_means(os.path.join(d, "cfetch"))
+    cw = counter_means(os.path.join(d, "cwrite"))
+    if not (fetch and write and cf and cw):
+        print("no counter data")
+        return
+    copy_bytes = args.copy_calib_mb << 20
+
+    def copy_factor(means, counter):
+        vals = [(v, n) for (k, c), (v, n) in means.items() if c == counter and "copy" in k.lower()]
+        if not vals:
+            vals = [(v, n) for (k, c), (v, n) in means.items() if c == counter]
+        v = max(vals)[0]
+        return copy_bytes / (v * 1024.0), v
+
+    ff, fv = copy_factor(cf, "FETCH_SIZE")
+    wf, wv = copy_factor(cw, "WRITE_SIZE")
+    for (k, c), (v, n) in sorted(fetch.items()):
+        if c != "FETCH_SIZE" or not k.startswith("k_"):
+            continue
+        wkib = write.get((k, "WRITE_SIZE"), (0.0, 0))[0]
+        hbm = v * 1024.0 * ff + wkib * 1024.0 * wf
+        lines = [f"# HBM traffic of {k}, workload {wl}",
+                 f"command: rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch -o run -- python3 bench.py "
+                 f"--workload {wl} --steps {args.steps} --warmup {args.warmup} --no-cpu --no-sweep ; the same with "
+                 f"--pmc WRITE_SIZE ; and both counters on: python3 bench.py --copy-calib-mb {args.copy_calib_mb}",
+                 f"source_digest: {source_digest()}",
+                 f"dispatches: {n}",
+                 f"fetch_kib_per_launch: {v:.1f}",
+                 f"write_kib_per_launch: {wkib:.1f}",
+                 f"copy_calib_bytes: {copy_bytes}",
+                 f"copy_fetch_kib: {fv:.1f}",
+                 f"copy_write_kib: {wv:.1f}",
+                 f"fetch_scale: {ff:.4f}",
+                 f"write_scale: {wf:.4f}",
+                 f"hbm_bytes_per_launch: {hbm:.0f}"]
+        with open(os.path.join(d, f"{k}_{wl}_pmc.txt"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print("\n".join(lines))
 
 
 def main():
@@ -252,7 +365,12 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration) and exit")
+    ap.add_argument("--rocprof-summary", metavar="DIR", default=None,
+                    help="summarise rocprofv3 CSV output under DIR (see rocprof_summary) and exit")
     args = ap.parse_args()
+    if args.rocprof_summary:
+        rocprof_summary(args)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))

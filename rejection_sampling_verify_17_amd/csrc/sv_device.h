@@ -64,18 +64,16 @@ __device__ __forceinline__ float accept_uniform(uint32_t w) {
   return (float)(w >> 8) * 0x1p-24f;
 }
 
-// Exponential variate E = -ln U, U = (2 (w >> 9) + 1) 2^-24 (an odd multiple of
-// 2^-24 inside (0, 1), exact in fp32).  For U >= 1/2 it is evaluated as
-// -log1p(-(1 - U)) with 1 - U exact, so E keeps its relative accuracy as U -> 1,
-// where E is smallest and the Gumbel key largest.
-__device__ __forceinline__ float exponential_variate(uint32_t w) {
-  const uint32_t k = w >> 9;
-  if (k < (1u << 22)) {
-    const float U = (float)(2u * k + 1u) * 0x1p-24f;
-    return -logf(U);
-  }
-  const float d = (float)((1u << 24) - 2u * k - 1u) * 0x1p-24f;
-  return -log1pf(-d);
+// Exponential variate in base 2: E2 = -log2 U = E / ln 2, with E = -ln U the
+// exponential variate and U = (2 (w >> 9) + 1) 2^-24 (an odd multiple of 2^-24
+// inside (0, 1), exact in fp32).  Scaling every E of an arg-max by the same
+// 1/ln 2 leaves the arg-max unchanged: r / E2 orders like r / E, and
+// z c - log2 E2 = (ln q - ln E) / ln 2 + const.  The native log2 (v_log_f32)
+// is within 1 ulp of log2 U for every one of the 2^23 possible U, including
+// U -> 1 where E is smallest and the key largest.
+__device__ __forceinline__ float exp2_variate(uint32_t w) {
+  const float U = (float)(2u * (w >> 9) + 1u) * 0x1p-24f;
+  return -__builtin_amdgcn_logf(U);
 }
 
 // Order-preserving map of a float onto uint32 (larger float -> larger integer).

@@ -223,7 +223,7 @@ __device__ int judge_dense(const Args &a, int b, bool write, float4 &st) {
 // ---------------------------------------------------------------------------
 // Pass 2: judge, then the Gumbel-max winner of one vocabulary chunk of the row
 // to sample.  Residual key r_v / E_v (the exponential race, monotone in
-// ln r_v - ln E_v); bonus key z_v c - log2 E_v (monotone in ln q_v - ln E_v).
+// ln r_v - ln E_v); bonus key z_v c - log2 E2_v (monotone in ln q_v - ln E_v).
 // ---------------------------------------------------------------------------
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_sample(Args a) {
@@ -290,10 +290,10 @@ __global__ __launch_bounds__(kThreads) void k_sample(Args a) {
         const uint32_t idx = group * 4u + (uint32_t)e;
         unsigned long long k = 0ull;
         if (residual) {
-          if (w[e] > 0.0f) k = pack_key(w[e] / exponential_variate(blk.w[e]), idx);
+          if (w[e] > 0.0f) k = pack_key(w[e] * __builtin_amdgcn_rcpf(exp2_variate(blk.w[e])), idx);
         } else {
           if (w[e] != -INFINITY)
-            k = pack_key(fmaf(w[e], c, -__builtin_amdgcn_logf(exponential_variate(blk.w[e]))), idx);
+            k = pack_key(fmaf(w[e], c, -__builtin_amdgcn_logf(exp2_variate(blk.w[e]))), idx);
         }
         best = k > best ? k : best;
       }
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void k_pick(Args a) {
       const float z = Q.load_one(v);
       if (z == -INFINITY) continue;
       const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)n, (uint32_t)v >> 2, PURPOSE_SAMPLE);
-      const float E = exponential_variate(blk.w[v & 3]);
+      const float E = exp2_variate(blk.w[v & 3]);
       const unsigned long long k = pack_key(fmaf(z, a.c, -__builtin_amdgcn_logf(E)), (uint32_t)v);
       best = k > best ? k : best;
     }

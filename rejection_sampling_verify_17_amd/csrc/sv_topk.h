@@ -280,13 +280,13 @@ __device__ unsigned long long block_max_u64_sh(unsigned long long x, unsigned lo
   return x;
 }
 
-// Bonus key of kept entry (z, v) at position pos: z c - log2 E_v, monotone in
+// Bonus key of kept entry (z, v) at position pos: z c - log2 E2_v, monotone in
 // ln q_v - ln E_v; 0 for entries outside the kept set.
 __device__ __forceinline__ unsigned long long bonus_key(const Args &a, uint32_t seq, int pos,
                                                        const TopkRow &qr, float z, uint32_t v) {
   if (z == -INFINITY || entry_key(z, v) < qr.thr) return 0ull;
   const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)pos, v >> 2, PURPOSE_SAMPLE);
-  const float E = exponential_variate(blk.w[v & 3u]);
+  const float E = exp2_variate(blk.w[v & 3u]);
   return pack_key(fmaf(z, a.c, -__builtin_amdgcn_logf(E)), v);
 }
 
@@ -333,7 +333,7 @@ __device__ unsigned long long gumbel_residual_topk(TopkShared &sh, const Args &a
     const float r = qv - pv;
     if (!(r > 0.0f)) return;
     const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)n, v >> 2, PURPOSE_SAMPLE);
-    const unsigned long long k = pack_key(r / exponential_variate(blk.w[v & 3u]), v);
+    const unsigned long long k = pack_key(r * __builtin_amdgcn_rcpf(exp2_variate(blk.w[v & 3u])), v);
     best = k > best ? k : best;
   };
   if (qlist) {
