@@ -79,24 +79,23 @@ def source_digest() -> str:
 # Algorithmic bytes
 # ---------------------------------------------------------------------------
 def algorithmic_bytes(w, n_accepted: np.ndarray) -> dict:
-    """Bytes the method must move ("Roofline"):
-    pass 1 reads every draft row and target row 0..gamma-1 once (2 V b per
-    verified position); the sampling pass re-reads the rejected row pair
-    (2 V b) or the bonus row (V b) of each sequence; with top-k the rejected
-    position is resampled from the kept lists (no re-read) and only bonus rows
-    are read again.  Plus tokens in and outputs out."""
+    """Bytes the method must move ("Roofline"), from the step's own
+    outcome n_b.  The drafts are judged left to right and nothing after the
+    first rejection is needed, so the statistics read row pairs 0..n_b
+    (min(n_b + 1, gamma) pairs, 2 V b bytes each); the resample then reads
+    row pair n_b again (2 V b; with top-k it works from the kept lists
+    instead) or the bonus row (V b).  Plus tokens in and outputs out."""
     B, gamma, V = w.B, w.gamma, w.V
     b = 2 if w.is_bf16 else 4
-    pass1 = 2 * B * gamma * V * b + 4 * B * gamma
-    valid = n_accepted >= 0
-    rej = int(np.sum(valid & (n_accepted < gamma)))
-    bonus = int(np.sum(valid & (n_accepted == gamma)))
-    if 0 < w.top_k < V:
-        pass2 = bonus * V * b
-    else:
-        pass2 = rej * 2 * V * b + bonus * V * b
-    out = 4 * B * (gamma + 1) + 4 * B
-    return {"pass1": pass1, "pass2": pass2, "outputs": out, "total": pass1 + pass2 + out}
+    n = n_accepted[n_accepted >= 0].astype(np.int64)
+    stats = int(np.sum(np.minimum(n + 1, gamma))) * 2 * V * b
+    rej = int(np.sum(n < gamma))
+    bonus = int(np.sum(n == gamma))
+    sample = (0 if 0 < w.top_k < V else rej * 2 * V * b) + bonus * V * b
+    io = 4 * B * gamma + 4 * B * (gamma + 1) + 4 * B
+    all_rows = 2 * B * gamma * V * b  # every draft and target row 0..gamma-1 once
+    return {"stats": stats, "sample": sample, "io": io, "total": stats + sample + io,
+            "all_rows_once": all_rows}
 
 
 # ---------------------------------------------------------------------------
@@ -167,9 +166,12 @@ def run_workload(name: str, steps: int, warmup: int, hip: Hip, seed: int = 3000)
     hip.sync(f1)
     torch.cuda.synchronize()
     per_kernel = {}
-    for li, kname in enumerate(names):
-        d = [hip.ms(evs[i][2 * li], evs[i][2 * li + 1]) for i in range(steps)]
-        per_kernel[kname] = {"avg_us": 1e3 * float(np.mean(d)), "min_us": 1e3 * float(np.min(d))}
+    for kname in dict.fromkeys(names):
+        idx = [li for li, nm in enumerate(names) if nm == kname]
+        per_step = [sum(hip.ms(evs[i][2 * li], evs[i][2 * li + 1]) for li in idx) for i in range(steps)]
+        per_kernel[kname] = {"launches_per_step": len(idx), "us_per_step": 1e3 * float(np.mean(per_step)),
+                             "avg_us": 1e3 * float(np.mean(per_step)) / len(idx),
+                             "min_step_us": 1e3 * float(np.min(per_step))}
     ms_step_evented = hip.ms(f0, f1) / steps
     for row in evs:
         for e in row:
@@ -180,8 +182,9 @@ def run_workload(name: str, steps: int, warmup: int, hip: Hip, seed: int = 3000)
     n_acc = nacc.cpu().numpy()
     ab = algorithmic_bytes(w, n_acc)
     positions = w.B * w.gamma
-    dominant = "k_topk_rows" if "k_topk_rows" in names else "k_stats"
-    dom_bytes = ab["pass1"]
+    dominant = names[0]  # the per-position kernel: every byte of the rows goes through it
+    dom_launches = per_kernel[dominant]["launches_per_step"]
+    dom_bytes = ab["stats"] + ab["sample"] + 4 * w.B * w.gamma
     dom_us = per_kernel[dominant]["avg_us"]
     res = {
         "workload": name, "B": w.B, "gamma": w.gamma, "V": w.V, "dtype": "bf16" if w.is_bf16 else "f32",
@@ -191,7 +194,8 @@ def run_workload(name: str, steps: int, warmup: int, hip: Hip, seed: int = 3000)
         "algorithmic_bytes": ab, "GBps_step": ab["total"] / (ms_step * 1e-3) / 1e9,
         "frac_peak_step": ab["total"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kernels": per_kernel, "dominant": dominant,
-        "dominant_GBps": dom_bytes / (dom_us * 1e-6) / 1e9,
+        "dominant_GBps": dom_bytes / (dom_us * dom_launches * 1e-6) / 1e9,
+        "dominant_bytes_per_launch": dom_bytes / dom_launches, "dominant_launches": dom_launches,
         "mean_accepted": float(n_acc[n_acc >= 0].mean()), "all_kept": float(np.mean(n_acc == w.gamma)),
         "gen_s": gen_s,
     }
@@ -269,7 +273,7 @@ def _find(d, suffix):
 
 
 def _short(name: str) -> str:
-    for k in ("k_stats", "k_sample", "k_pick", "k_topk_rows", "k_topk_finish"):
+    for k in ("k_topk_step", "k_step", "k_pick"):
         if k in name:
             return k
     return name[:60]
@@ -398,7 +402,8 @@ def main():
     traffic = read_traffic(dom, args.workload)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": head["dominant_GBps"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": head["dominant_GBps"] / HBM_PEAK_GBS, "traffic": traffic,
-                "algorithmic_bytes_per_launch": head["algorithmic_bytes"]["pass1"], "avg_launch_us": dom_us}
+                "algorithmic_bytes_per_launch": head["dominant_bytes_per_launch"], "avg_launch_us": dom_us,
+                "launches_per_step": head["dominant_launches"]}
     cpu = None if args.no_cpu else cpu_baseline(w, 3000)
     sweep = []
     if not args.no_sweep:

@@ -18,33 +18,24 @@ using namespace sv;
 constexpr int kMaxGamma = 64;           // one wave ballots all positions
 constexpr int kMaxV = 1 << 28;          // byte offsets of a row fit 32 bits
 constexpr int kListMax = 1024;          // top-k lists kept up to this K
-constexpr int kTargetTiles = 2048;      // pass-1 / pass-2 blocks to aim for (8 per CU)
+#ifndef SV_TARGET_TILES
+#define SV_TARGET_TILES 4096
+#endif
+constexpr int kTargetTiles = SV_TARGET_TILES;  // blocks per launch to aim for
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
   bool topk;
-  int nvec, nch, cv, ngb, nch2, cv2, klist;
-  size_t off_part, off_bestpart, off_nseq, off_rowinfo, off_lists;
+  int nch, nvec, cv, ngb, cv2, klist;
+  size_t off_part, off_bestpart, off_nseq, off_state, off_rowinfo, off_lists;
   size_t total;
 };
 
 bool shape_ok(int32_t B, int32_t gamma, int32_t V, int32_t dtype) {
   return B >= 1 && gamma >= 1 && gamma <= kMaxGamma && V >= 2 && V <= kMaxV &&
          (dtype == SV_F32 || dtype == SV_BF16);
-}
-
-// Split a row of n units (16-byte vectors or group blocks) into chunks so that
-// `rows` rows give about kTargetTiles blocks, each thread keeping at least two
-// units.
-void split(int rows, int n, int *nch, int *per_chunk) {
-  const int max_ch = std::max(1, n / (2 * kThreads));
-  int k = (kTargetTiles + rows - 1) / rows;
-  k = std::max(1, std::min(k, max_ch));
-  const int per = (n + k - 1) / k;
-  *per_chunk = per;
-  *nch = (n + per - 1) / per;
 }
 
 Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype) {
@@ -55,16 +46,21 @@ Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype
   p.topk = top_k > 0 && top_k < V;
   p.klist = (p.topk && top_k <= kListMax) ? top_k : 0;
   if (!p.topk) {
-    split(B * gamma, p.nvec, &p.nch, &p.cv);
-    split(B, p.ngb, &p.nch2, &p.cv2);
+    // blocks per sequence: about kTargetTiles blocks per launch, each thread
+    // keeping at least two vectors of a row
+    const int max_ch = std::max(1, p.nvec / (2 * kThreads));
+    p.nch = std::max(1, std::min((kTargetTiles + B - 1) / B, max_ch));
+    p.cv = (p.nvec + p.nch - 1) / p.nch;
+    p.cv2 = (p.ngb + p.nch - 1) / p.nch;
   }
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
   // Nothing here is read before this call writes it: the workspace needs no
   // initialisation and may serve calls of any shape in turn.
   p.off_part = take(p.topk ? 0 : (size_t)B * gamma * p.nch * sizeof(float4));
-  p.off_bestpart = take(p.topk ? 0 : (size_t)B * p.nch2 * sizeof(unsigned long long));
+  p.off_bestpart = take(p.topk ? 0 : (size_t)B * p.nch * sizeof(unsigned long long));
   p.off_nseq = take((size_t)B * sizeof(int32_t));
+  p.off_state = take((size_t)2 * B * sizeof(int32_t));
   const size_t slots = (size_t)B * (2 * gamma);
   p.off_rowinfo = take(p.topk ? slots * sizeof(uint4) : 0);
   p.off_lists = take(p.klist ? slots * (size_t)p.klist * sizeof(int2) : 0);
@@ -74,6 +70,8 @@ Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype
 
 template <int DT>
 struct Launches {
+  // gamma + 2 launches (dense) or gamma + 1 (top-k): one per position, then
+  // the pick.
   static sv_status run(const Args &a, const Plan &p, hipStream_t stream, void *const *events, int n_events,
                        int *n_launches) {
     int li = 0;
@@ -87,23 +85,21 @@ struct Launches {
     };
     bool ok = true;
     if (!p.topk) {
-      before();
-      hipLaunchKernelGGL(k_stats<DT>, dim3(a.B * a.gamma * p.nch), dim3(kThreads), 0, stream, a);
-      ok = ok && after();
-      before();
-      hipLaunchKernelGGL(k_sample<DT>, dim3(a.B * p.nch2), dim3(kThreads), 0, stream, a);
-      ok = ok && after();
+      for (int j = 0; j <= a.gamma; ++j) {
+        before();
+        hipLaunchKernelGGL(k_step<DT>, dim3(a.B * p.nch), dim3(kThreads), 0, stream, a, j);
+        ok = ok && after();
+      }
       before();
       const int waves = kThreads / kWave;
       hipLaunchKernelGGL(k_pick<DT>, dim3((a.B + waves - 1) / waves), dim3(kThreads), 0, stream, a);
       ok = ok && after();
     } else {
-      before();
-      hipLaunchKernelGGL(k_topk_rows<DT>, dim3(a.B * 2 * a.gamma), dim3(kTopkThreads), 0, stream, a);
-      ok = ok && after();
-      before();
-      hipLaunchKernelGGL(k_topk_finish<DT>, dim3(a.B), dim3(kTopkThreads), 0, stream, a);
-      ok = ok && after();
+      for (int j = 0; j <= a.gamma; ++j) {
+        before();
+        hipLaunchKernelGGL(k_topk_step<DT>, dim3(a.B * 2), dim3(kTopkThreads), 0, stream, a, j);
+        ok = ok && after();
+      }
     }
     if (n_launches) *n_launches = li;
     return ok ? SV_OK : SV_EHIP;
@@ -147,11 +143,11 @@ sv_status verify_impl(const void *target, const void *draft, const int32_t *toke
   a.part = (float4 *)(ws + p.off_part);
   a.bestpart = (unsigned long long *)(ws + p.off_bestpart);
   a.nseq = (int32_t *)(ws + p.off_nseq);
-  a.nvec = p.nvec;
+  a.state = (int32_t *)(ws + p.off_state);
   a.nch = p.nch;
+  a.nvec = p.nvec;
   a.cv = p.cv;
   a.ngb = p.ngb;
-  a.nch2 = p.nch2;
   a.cv2 = p.cv2;
   a.rowinfo = p.topk ? (uint4 *)(ws + p.off_rowinfo) : nullptr;
   a.lists = p.klist ? (int2 *)(ws + p.off_lists) : nullptr;
@@ -204,10 +200,10 @@ sv_status sv_verify_timed(const void *target_logits, const void *draft_logits, c
 const char *sv_launch_name(int32_t B, int32_t gamma, int32_t V, int32_t dtype, int32_t top_k, int32_t i) {
   if (!shape_ok(B, gamma, V, dtype)) return nullptr;
   const bool topk = top_k > 0 && top_k < V;
-  static const char *dense[] = {"k_stats", "k_sample", "k_pick"};
-  static const char *filt[] = {"k_topk_rows", "k_topk_finish"};
-  if (i < 0 || i >= (topk ? 2 : 3)) return nullptr;
-  return topk ? filt[i] : dense[i];
+  if (i < 0) return nullptr;
+  if (i <= gamma) return topk ? "k_topk_step" : "k_step";
+  if (!topk && i == gamma + 1) return "k_pick";
+  return nullptr;
 }
 
 const char *sv_status_string(sv_status s) {

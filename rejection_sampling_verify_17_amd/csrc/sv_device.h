@@ -59,6 +59,13 @@ __device__ __forceinline__ Philox4 stream_block(uint32_t k0, uint32_t k1, uint32
   return philox(group, pos, seq, purpose, k0, k1);
 }
 
+// Word i (0..3, run-time) of a block, by selects (no indexed private memory).
+__device__ __forceinline__ uint32_t word_of(const Philox4 &b, uint32_t i) {
+  const uint32_t lo = (i & 1u) ? b.w[1] : b.w[0];
+  const uint32_t hi = (i & 1u) ? b.w[3] : b.w[2];
+  return (i & 2u) ? hi : lo;
+}
+
 // Acceptance uniform: top 24 bits of the word times 2^-24, in [0, 1); exact in fp32.
 __device__ __forceinline__ float accept_uniform(uint32_t w) {
   return (float)(w >> 8) * 0x1p-24f;

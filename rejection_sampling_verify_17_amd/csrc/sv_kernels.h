@@ -1,19 +1,27 @@
 // Verification kernels, dense path (no top-k filter).
 //
-//   k_stats   one block per (row pair, vocabulary chunk): streams draft row j and
-//             target row j of a sequence and writes partial base-2 softmax
-//             statistics (R, S) of both.
-//   k_sample  one block per (sequence, vocabulary chunk).  Its first wave
-//             merges the sequence's partials, evaluates every acceptance ratio
-//             in registers and ballots the accept bits to find the first
-//             rejection n (each block of the sequence does this small step
-//             itself, so no block waits on another).  The block then draws the
-//             Gumbel-max winner of its chunk: over the residual max(0, q_n - p_n),
-//             or over target row gamma when every draft was kept.
-//   k_pick    one wave per sequence: the best chunk winner is the token.
+// The rule judges drafts left to right and discards everything after the
+// first rejection, so rows after it are never read.  One launch per position:
 //
-// Blocks never signal each other inside a kernel: results cross kernel
-// boundaries only (on this GPU an agent-scope fence is a write-back and
+//   k_step(j = 0)   every sequence: partial base-2 softmax statistics (R, S) of
+//                   draft row 0 and target row 0, one vocabulary chunk per block.
+//   k_step(j >= 1)  every block of a sequence still alive at j-1 first judges
+//                   position j-1 itself (wave 0 merges that row pair's
+//                   partials, evaluates q(t)/p(t) in registers and draws u),
+//                   then, on its chunk:
+//                     accepted, j < gamma:  statistics of row pair j;
+//                     accepted, j = gamma:  Gumbel-max winner over target row
+//                                           gamma (the bonus token);
+//                     rejected:             Gumbel-max winner over the residual
+//                                           max(0, q - p) of row pair j-1.
+//                   Memory-bound statistics of live sequences and VALU-bound
+//                   sampling of finished ones share each launch.
+//   k_pick          one wave per sequence: the best chunk winner is the token.
+//
+// A per-sequence state (double-buffered by launch parity, so blocks of one
+// launch read what the previous launch wrote) says whether the sequence is
+// alive at j-1.  Blocks never signal each other inside a launch: results cross
+// launch boundaries only (on this GPU an agent-scope fence is a write-back and
 // invalidation of the whole L2, far too dear to pay per block).
 //
 // The rule is that of page "스펙큘러티브 디코딩 — 작은 모델이 먼저 쓰고 큰 모델이
@@ -26,6 +34,11 @@
 namespace sv {
 
 constexpr int kThreads = 256;
+
+// Per-sequence state between launches: j >= 0 means "alive: rows 0..j-1
+// accepted and row pair j's statistics written"; anything else means done.
+constexpr int kDone = -1;
+constexpr int kInvalid = -2;
 
 struct Args {
   const void *target;      // [B][gamma+1][V]
@@ -40,11 +53,13 @@ struct Args {
   float *token_probs;      // [B][gamma][2] or null
   float *accept_ur;        // [B][gamma][2] or null
   // workspace
-  float4 *part;            // [B*gamma*nch] {Rp, Sp, Rq, Sq}
-  unsigned long long *bestpart;  // [B*nch2] chunk winners (0 = none)
+  float4 *part;            // [B][gamma][nch] {Rp, Sp, Rq, Sq}
+  unsigned long long *bestpart;  // [B][nch] chunk winners (0 = none)
   int32_t *nseq;           // [B] n, or -1 for an invalid sequence
-  int32_t nvec, nch, cv;   // pass 1: vectors per row (any alignment), chunks, vectors per chunk
-  int32_t ngb, nch2, cv2;  // pass 2: group blocks per row, chunks, group blocks per chunk
+  int32_t *state;          // [2][B] launch-parity double buffer
+  int32_t nch;             // blocks (vocabulary chunks) per sequence
+  int32_t nvec, cv;        // statistics: 16-byte vectors per row (any alignment), per chunk
+  int32_t ngb, cv2;        // sampling: group blocks per row, per chunk
   // top-k path
   uint4 *rowinfo;          // [B][2*gamma] {thr lo, thr hi, R bits, S bits}
   int2 *lists;             // [B][2*gamma][K] (index, logit bits) or null
@@ -64,6 +79,7 @@ __device__ __forceinline__ const void *draft_row(const Args &a, int b, int j) {
   return (const char *)a.draft + ((size_t)b * a.gamma + j) * (size_t)a.V * Elem<DT>::kSize;
 }
 
+// Whole row of outputs for an invalid sequence (wave-cooperative).
 __device__ __forceinline__ void write_invalid(const Args &a, int b, int lane) {
   const int gamma = a.gamma;
   int32_t *out = a.out_tokens + (size_t)b * (gamma + 1);
@@ -72,20 +88,10 @@ __device__ __forceinline__ void write_invalid(const Args &a, int b, int lane) {
     a.n_accepted[b] = -1;
     a.nseq[b] = -1;
   }
-  for (int j = lane; j < gamma; j += kWave) {
-    if (a.token_probs) {
-      a.token_probs[((size_t)b * gamma + j) * 2 + 0] = NAN;
-      a.token_probs[((size_t)b * gamma + j) * 2 + 1] = NAN;
-    }
-    if (a.accept_ur) {
-      a.accept_ur[((size_t)b * gamma + j) * 2 + 0] = NAN;
-      a.accept_ur[((size_t)b * gamma + j) * 2 + 1] = NAN;
-    }
-  }
 }
 
-// Prefix, padding and n of a judged sequence (the sampled slot n is written
-// by the pick step).
+// Prefix, padding and n of a judged sequence (wave-cooperative; the sampled
+// slot n is written by the pick step).
 __device__ __forceinline__ void write_judged(const Args &a, int b, int lane, int n) {
   const int gamma = a.gamma;
   int32_t *out = a.out_tokens + (size_t)b * (gamma + 1);
@@ -99,32 +105,66 @@ __device__ __forceinline__ void write_judged(const Args &a, int b, int lane, int
   }
 }
 
-// Ballot result -> first rejected position (gamma if all gamma accepted).
-__device__ __forceinline__ int first_rejection(unsigned long long mask, int gamma) {
-  const int n = (mask == ~0ull) ? kWave : __builtin_ctzll(~mask);
-  return n < gamma ? n : gamma;
+// Diagnostics of a judged position (NaN-filled first for every position, so
+// positions after the first rejection stay NaN).
+__device__ __forceinline__ void write_diag(const Args &a, int b, int j, float pt, float qt, float u, float ratio) {
+  const size_t i = ((size_t)b * a.gamma + j) * 2;
+  if (a.token_probs) {
+    a.token_probs[i] = pt;
+    a.token_probs[i + 1] = qt;
+  }
+  if (a.accept_ur) {
+    a.accept_ur[i] = u;
+    a.accept_ur[i + 1] = ratio;
+  }
+}
+
+// Are all drafted tokens of sequence b in [0, V)?  (wave 0)
+__device__ __forceinline__ bool tokens_valid(const Args &a, int b) {
+  const int lane = threadIdx.x;
+  bool ok = true;
+  for (int j = lane; j < a.gamma; j += kWave) {
+    const int t = a.tokens[(size_t)b * a.gamma + j];
+    ok = ok && (t >= 0) && (t < a.V);
+  }
+  return __ballot(!ok) == 0ull;
+}
+
+// Keep-decision of draft t at one position from its stored logits and the two
+// rows' statistics: keep iff q(t) > 0 and (p(t) = 0 or u < q(t)/p(t)).
+// q(t)/p(t) = 2^(c (zq - zp) - (Rq - Rp)) * Sp / Sq: the large terms cancel
+// before rounding (Rq - Rp is an exact integer difference).
+struct Judged {
+  bool accept;
+  float u, ratio, pt, qt;
+};
+__device__ __forceinline__ Judged judge_one(const Args &a, uint32_t seq, int j, float zp, float zq, bool pzero,
+                                            bool qzero, float Rp, float Sp, float Rq, float Sq) {
+  Judged r;
+  const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)j, 0u, PURPOSE_ACCEPT);
+  r.u = accept_uniform(blk.w[0]);
+  if (qzero) r.ratio = 0.0f;
+  else if (pzero) r.ratio = INFINITY;
+  else r.ratio = __builtin_amdgcn_exp2f(a.c * (zq - zp) - (Rq - Rp)) * (Sp / Sq);
+  r.accept = !qzero && (pzero || r.u < r.ratio);
+  r.pt = pzero ? 0.0f : __builtin_amdgcn_exp2f(fmaf(zp, a.c, -Rp)) / Sp;
+  r.qt = qzero ? 0.0f : __builtin_amdgcn_exp2f(fmaf(zq, a.c, -Rq)) / Sq;
+  return r;
 }
 
 // ---------------------------------------------------------------------------
-// Pass 1: partial softmax statistics of draft row j and target row j.
+// Block pieces
 // ---------------------------------------------------------------------------
+
+// Partial statistics of draft row j and target row j over vectors [v0, v1).
 template <int DT>
-__global__ __launch_bounds__(kThreads) void k_stats(Args a) {
+__device__ float4 chunk_stats(const Args &a, int b, int j, int v0, int v1) {
   constexpr int NE = Elem<DT>::kVec;
   constexpr int U = 4;  // vectors in flight per row per thread
-  const int tile = blockIdx.x;
-  const int row = tile / a.nch;
-  const int ch = tile - row * a.nch;
-  const int b = row / a.gamma;
-  const int j = row - b * a.gamma;
-
   const Row<DT> P(draft_row<DT>(a, b, j), a.V);
   const Row<DT> Q(target_row<DT>(a, b, j), a.V);
-  const int v0 = ch * a.cv;
-  const int v1 = min(a.nvec, v0 + a.cv);
   const int V = a.V;
   const float c = a.c;
-
   float Rp = -INFINITY, Sp = 0.0f, Rq = -INFINITY, Sq = 0.0f;
   for (int base = v0 + (int)threadIdx.x; base < v1; base += kThreads * U) {
     float zp[U][NE], zq[U][NE];
@@ -137,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void k_stats(Args a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int iv = base + u * kThreads;
-      const int ep = iv * NE - P.s, eq = iv * NE - Q.s;  // entry of lane 0
+      const int ep = iv * NE - P.s, eq = iv * NE - Q.s;  // entry of element 0
       if (iv >= v1 || ep < 0 || eq < 0 || ep + NE > V || eq + NE > V) {
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
@@ -150,157 +190,160 @@ __global__ __launch_bounds__(kThreads) void k_stats(Args a) {
     }
   }
   block_merge_stats2<kThreads>(Rp, Sp, Rq, Sq);
-  if (threadIdx.x == 0) a.part[tile] = make_float4(Rp, Sp, Rq, Sq);
+  return make_float4(Rp, Sp, Rq, Sq);
 }
 
-// ---------------------------------------------------------------------------
-// Judging a sequence (wave 0 of a block).  Lane j holds position j: it merges
-// that position's partial statistics, evaluates q_j(t_j) / p_j(t_j) and draws
-// u_j; a 64-wide ballot of the accept bits gives the first rejection n.
-// Returns n (or -1 for an invalid sequence) in every lane; `st` receives the
-// statistics of row n in every lane.  Writes the outputs if `write`.
-// ---------------------------------------------------------------------------
+// Gumbel-max winner of group blocks [g0, g1) of row `pos`: residual weights
+// q - p (statistics st of that row pair) when `residual`, else the bonus row
+// (weights q).  Residual key r / E2 (the exponential race, monotone in
+// ln r - ln E); bonus key z c - log2 E2 (monotone in ln q - ln E).
 template <int DT>
-__device__ int judge_dense(const Args &a, int b, bool write, float4 &st) {
-  const int lane = threadIdx.x;
-  const int gamma = a.gamma;
-  const bool active = lane < gamma;
-  const uint32_t seq = seq_of(a, b);
-
-  float Rp = -INFINITY, Sp = 0.0f, Rq = -INFINITY, Sq = 0.0f;
-  int t = 0;
-  bool ok = true;
-  if (active) {
-    const float4 *pp = a.part + ((size_t)b * gamma + lane) * a.nch;
-    for (int c = 0; c < a.nch; ++c) {
-      const float4 v = pp[c];
-      merge_stats(Rp, Sp, v.x, v.y);
-      merge_stats(Rq, Sq, v.z, v.w);
-    }
-    t = a.tokens[(size_t)b * gamma + lane];
-    ok = (t >= 0) && (t < a.V);
-  }
-  if (__ballot(active && !ok) != 0ull) {
-    if (write) write_invalid(a, b, lane);
-    return -1;
-  }
-
-  bool accept = false;
-  if (active) {
-    const float zp = Row<DT>(draft_row<DT>(a, b, lane), a.V).load_one(t);
-    const float zq = Row<DT>(target_row<DT>(a, b, lane), a.V).load_one(t);
-    const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)lane, 0u, PURPOSE_ACCEPT);
-    const float u = accept_uniform(blk.w[0]);
-    const bool qzero = (zq == -INFINITY);
-    const bool pzero = (zp == -INFINITY);
-    // q(t)/p(t) = 2^(c (zq - zp) - (Rq - Rp)) * Sp / Sq: the large terms cancel
-    // before rounding (Rq - Rp is an exact integer difference).
-    float ratio;
-    if (qzero) ratio = 0.0f;
-    else if (pzero) ratio = INFINITY;
-    else ratio = __builtin_amdgcn_exp2f(a.c * (zq - zp) - (Rq - Rp)) * (Sp / Sq);
-    accept = !qzero && (pzero || u < ratio);
-    if (write && a.token_probs) {
-      const float pt = pzero ? 0.0f : __builtin_amdgcn_exp2f(fmaf(zp, a.c, -Rp)) / Sp;
-      const float qt = qzero ? 0.0f : __builtin_amdgcn_exp2f(fmaf(zq, a.c, -Rq)) / Sq;
-      a.token_probs[((size_t)b * gamma + lane) * 2 + 0] = pt;
-      a.token_probs[((size_t)b * gamma + lane) * 2 + 1] = qt;
-    }
-    if (write && a.accept_ur) {
-      a.accept_ur[((size_t)b * gamma + lane) * 2 + 0] = u;
-      a.accept_ur[((size_t)b * gamma + lane) * 2 + 1] = ratio;
-    }
-  }
-  const int n = first_rejection(__ballot(active && accept), gamma);
-  // statistics of row n, from lane n (unused when n == gamma)
-  const int src = n < gamma ? n : 0;
-  st = make_float4(__shfl(Rp, src, kWave), __shfl(Sp, src, kWave), __shfl(Rq, src, kWave),
-                   __shfl(Sq, src, kWave));
-  if (write) write_judged(a, b, lane, n);
-  return n;
-}
-
-// ---------------------------------------------------------------------------
-// Pass 2: judge, then the Gumbel-max winner of one vocabulary chunk of the row
-// to sample.  Residual key r_v / E_v (the exponential race, monotone in
-// ln r_v - ln E_v); bonus key z_v c - log2 E2_v (monotone in ln q_v - ln E_v).
-// ---------------------------------------------------------------------------
-template <int DT>
-__global__ __launch_bounds__(kThreads) void k_sample(Args a) {
+__device__ unsigned long long chunk_winner(const Args &a, int b, int pos, bool residual, float4 st, int g0,
+                                           int g1) {
   constexpr int NE = Elem<DT>::kVec;
-  const int tile = blockIdx.x;
-  const int b = tile / a.nch2;
-  const int ch = tile - b * a.nch2;
-  const int gamma = a.gamma;
+  const uint32_t seq = seq_of(a, b);
+  const float c = a.c;
+  const int V = a.V;
+  const Row<DT> Q(target_row<DT>(a, b, pos), V);
+  const Row<DT> P(draft_row<DT>(a, b, residual ? pos : 0), V);
+  const float invSp = 1.0f / st.y, invSq = 1.0f / st.w;
+  constexpr int U = 2;  // group blocks in flight per thread
+  unsigned long long best = 0ull;
+  for (int base = g0 + (int)threadIdx.x; base < g1; base += kThreads * U) {
+    float zq[U][NE], zp[U][NE];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      Q.load_block(base + u * kThreads, zq[u]);  // past the chunk: masked below
+      if (residual) P.load_block(base + u * kThreads, zp[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int gb = base + u * kThreads;
+      if (gb >= g1) continue;
+#pragma unroll
+      for (int g = 0; g < NE / 4; ++g) {
+        float w[4];
+        bool any = false;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int idx = gb * NE + g * 4 + e;
+          const float zqe = zq[u][g * 4 + e];
+          if (residual) {
+            const float qv = (zqe == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(fmaf(zqe, c, -st.z)) * invSq;
+            const float zpe = zp[u][g * 4 + e];
+            const float pv = (zpe == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(fmaf(zpe, c, -st.x)) * invSp;
+            w[e] = (idx < V) ? qv - pv : 0.0f;
+            any |= w[e] > 0.0f;
+          } else {
+            w[e] = (idx < V && zqe != -INFINITY) ? zqe : -INFINITY;
+            any |= w[e] != -INFINITY;
+          }
+        }
+        if (!any) continue;
+        const uint32_t group = (uint32_t)(gb * (NE / 4) + g);
+        const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)pos, group, PURPOSE_SAMPLE);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t idx = group * 4u + (uint32_t)e;
+          unsigned long long k = 0ull;
+          if (residual) {
+            if (w[e] > 0.0f) k = pack_key(w[e] * __builtin_amdgcn_rcpf(exp2_variate(blk.w[e])), idx);
+          } else {
+            if (w[e] != -INFINITY)
+              k = pack_key(fmaf(w[e], c, -__builtin_amdgcn_logf(exp2_variate(blk.w[e]))), idx);
+          }
+          best = k > best ? k : best;
+        }
+      }
+    }
+  }
+  return block_max_u64<kThreads>(best);
+}
 
+// ---------------------------------------------------------------------------
+// One launch per position j = 0..gamma (see the top of this file).
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_step(Args a, int j) {
+  const int b = blockIdx.x / a.nch;
+  const int ch = blockIdx.x - b * a.nch;
+  const int gamma = a.gamma;
+  const bool lead = ch == 0;  // writes the sequence's outputs and state
+  int32_t *state_in = a.state + (size_t)((j + 1) & 1) * a.B;
+  int32_t *state_out = a.state + (size_t)(j & 1) * a.B;
+
+  __shared__ int sh_mode;   // 0 stats of row j, 1 residual of row j-1, 2 bonus, -1 nothing
   __shared__ float4 sh_st;
-  __shared__ int sh_n;
   if (threadIdx.x < kWave) {
-    float4 st;
-    const int n = judge_dense<DT>(a, b, ch == 0, st);
-    if (threadIdx.x == 0) {
-      sh_n = n;
+    const int lane = threadIdx.x;
+    int mode = 0;
+    float4 st = make_float4(0.f, 1.f, 0.f, 1.f);
+    if (j == 0) {
+      if (!tokens_valid(a, b)) {
+        mode = -1;
+        if (lead) {
+          write_invalid(a, b, lane);
+          for (int k = lane; k < gamma; k += kWave) write_diag(a, b, k, NAN, NAN, NAN, NAN);
+          if (lane == 0) state_out[b] = kInvalid;
+        }
+      } else if (lead) {
+        for (int k = lane; k < gamma; k += kWave) write_diag(a, b, k, NAN, NAN, NAN, NAN);
+        if (lane == 0) state_out[b] = 0;
+      }
+    } else {
+      const int s = state_in[b];
+      if (s != j - 1) {
+        mode = -1;  // finished (or invalid) before position j-1
+        if (lead && lane == 0) state_out[b] = s;
+      } else {
+        // judge position j-1: merge its row pair's partial statistics (lanes
+        // stride over chunks), then one lane evaluates the ratio
+        float Rp = -INFINITY, Sp = 0.0f, Rq = -INFINITY, Sq = 0.0f;
+        const float4 *pp = a.part + ((size_t)b * gamma + (j - 1)) * a.nch;
+        for (int k = lane; k < a.nch; k += kWave) {
+          const float4 v = pp[k];
+          merge_stats(Rp, Sp, v.x, v.y);
+          merge_stats(Rq, Sq, v.z, v.w);
+        }
+        wave_merge_stats(Rp, Sp);
+        wave_merge_stats(Rq, Sq);
+        st = make_float4(Rp, Sp, Rq, Sq);
+        const int t = a.tokens[(size_t)b * gamma + (j - 1)];
+        const float zp = Row<DT>(draft_row<DT>(a, b, j - 1), a.V).load_one(t);
+        const float zq = Row<DT>(target_row<DT>(a, b, j - 1), a.V).load_one(t);
+        const Judged r = judge_one(a, seq_of(a, b), j - 1, zp, zq, zp == -INFINITY, zq == -INFINITY, Rp, Sp, Rq, Sq);
+        if (lead && lane == 0) write_diag(a, b, j - 1, r.pt, r.qt, r.u, r.ratio);
+        if (!r.accept) {
+          mode = 1;
+          if (lead) write_judged(a, b, lane, j - 1);
+          if (lead && lane == 0) state_out[b] = kDone;
+        } else if (j == gamma) {
+          mode = 2;
+          if (lead) write_judged(a, b, lane, gamma);
+          if (lead && lane == 0) state_out[b] = kDone;
+        } else if (lead && lane == 0) {
+          state_out[b] = j;
+        }
+      }
+    }
+    if (lane == 0) {
+      sh_mode = mode;
       sh_st = st;
     }
   }
   __syncthreads();
-  const int n = sh_n;
-  if (n < 0) return;
-  const float4 st = sh_st;
-  const bool residual = n < gamma;
-  const uint32_t seq = seq_of(a, b);
-  const float c = a.c;
-  const int V = a.V;
-
-  const Row<DT> Q(target_row<DT>(a, b, n), V);
-  const Row<DT> P(draft_row<DT>(a, b, residual ? n : 0), V);
-  const float invSp = 1.0f / st.y, invSq = 1.0f / st.w;
-
-  const int g0 = ch * a.cv2;
-  const int g1 = min(a.ngb, g0 + a.cv2);
-  unsigned long long best = 0ull;
-  for (int gb = g0 + (int)threadIdx.x; gb < g1; gb += kThreads) {
-    float zq[NE], zp[NE];
-    Q.load_block(gb, zq);
-    if (residual) P.load_block(gb, zp);
-#pragma unroll
-    for (int g = 0; g < NE / 4; ++g) {
-      float w[4];
-      bool any = false;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int idx = gb * NE + g * 4 + e;
-        const float zqe = zq[g * 4 + e];
-        if (residual) {
-          const float qv = (zqe == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(fmaf(zqe, c, -st.z)) * invSq;
-          const float zpe = zp[g * 4 + e];
-          const float pv = (zpe == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(fmaf(zpe, c, -st.x)) * invSp;
-          w[e] = (idx < V) ? qv - pv : 0.0f;
-          any |= w[e] > 0.0f;
-        } else {
-          w[e] = (idx < V && zqe != -INFINITY) ? zqe : -INFINITY;
-          any |= w[e] != -INFINITY;
-        }
-      }
-      if (!any) continue;
-      const uint32_t group = (uint32_t)(gb * (NE / 4) + g);
-      const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)n, group, PURPOSE_SAMPLE);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t idx = group * 4u + (uint32_t)e;
-        unsigned long long k = 0ull;
-        if (residual) {
-          if (w[e] > 0.0f) k = pack_key(w[e] * __builtin_amdgcn_rcpf(exp2_variate(blk.w[e])), idx);
-        } else {
-          if (w[e] != -INFINITY)
-            k = pack_key(fmaf(w[e], c, -__builtin_amdgcn_logf(exp2_variate(blk.w[e]))), idx);
-        }
-        best = k > best ? k : best;
-      }
-    }
+  const int mode = sh_mode;
+  if (mode < 0) return;
+  if (mode == 0) {
+    const int v0 = ch * a.cv;
+    const float4 p = chunk_stats<DT>(a, b, j, v0, min(a.nvec, v0 + a.cv));
+    if (threadIdx.x == 0) a.part[((size_t)b * gamma + j) * a.nch + ch] = p;
+  } else {
+    const int g0 = ch * a.cv2;
+    const unsigned long long w =
+        chunk_winner<DT>(a, b, mode == 1 ? j - 1 : gamma, mode == 1, sh_st, g0, min(a.ngb, g0 + a.cv2));
+    if (threadIdx.x == 0) a.bestpart[(size_t)b * a.nch + ch] = w;
   }
-  best = block_max_u64<kThreads>(best);
-  if (threadIdx.x == 0) a.bestpart[tile] = best;
 }
 
 // ---------------------------------------------------------------------------
@@ -316,8 +359,8 @@ __global__ __launch_bounds__(kThreads) void k_pick(Args a) {
   const int n = a.nseq[b];
   if (n < 0 || n > a.gamma) return;
   unsigned long long best = 0ull;
-  for (int i = lane; i < a.nch2; i += kWave) {
-    const unsigned long long k = a.bestpart[(size_t)b * a.nch2 + i];
+  for (int i = lane; i < a.nch; i += kWave) {
+    const unsigned long long k = a.bestpart[(size_t)b * a.nch + i];
     best = k > best ? k : best;
   }
   best = wave_max_u64(best);
@@ -328,7 +371,7 @@ __global__ __launch_bounds__(kThreads) void k_pick(Args a) {
       const float z = Q.load_one(v);
       if (z == -INFINITY) continue;
       const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)n, (uint32_t)v >> 2, PURPOSE_SAMPLE);
-      const float E = exp2_variate(blk.w[v & 3]);
+      const float E = exp2_variate(word_of(blk, (uint32_t)v & 3u));
       const unsigned long long k = pack_key(fmaf(z, a.c, -__builtin_amdgcn_logf(E)), (uint32_t)v);
       best = k > best ? k : best;
     }

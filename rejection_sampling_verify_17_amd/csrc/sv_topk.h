@@ -6,15 +6,19 @@
 // ordered like "larger logit, then smaller index"; the kept set is the K
 // largest keys, i.e. all keys >= the K-th largest ("threshold").
 //
-//   k_topk_rows    one block per row (draft rows 0..gamma-1, target rows
-//                  0..gamma-1 of a sequence).  Finds the row's threshold by an
-//                  LDS radix select, then the base-2 softmax statistics (R, S)
-//                  over the kept entries and, for small K, the kept list.
-//   k_topk_finish  one block per sequence: judges the drafts (in registers,
-//                  wave ballot), then draws the replacement from the residual
-//                  over the target row's kept list, or, when every draft was
-//                  kept, selects target row gamma's top-k and draws the bonus
-//                  token over its kept entries.
+// The drafts are judged left to right and nothing after the first rejection is
+// read.  k_topk_step(j) runs two blocks per sequence (draft row, target row):
+//   j = 0        each block selects its row 0: threshold by an LDS radix
+//                select, base-2 softmax statistics (R, S) over the kept
+//                entries and, for small K, the kept list.
+//   j >= 1       both blocks of a sequence alive at j-1 judge position j-1
+//                (wave 0: membership of t in both kept sets, ratio in
+//                registers, Philox u); accepted and j < gamma: each selects
+//                its row j; rejected: the draft-row block draws the
+//                replacement from the residual over the target row's kept
+//                list; accepted at j = gamma: the draft-row block selects
+//                target row gamma and draws the bonus token over its kept
+//                entries.  The deciding block writes the token itself.
 //
 // Selection: a lower bound L on the K-th largest logit comes from the
 // per-thread maxima (K threads each own an entry >= their maximum's K-th
@@ -61,7 +65,7 @@ __device__ __forceinline__ unsigned long long entry_key(float z, uint32_t v) {
 // exactly the K largest.  Keys outside that set may also pass the cleared
 // threshold, so callers that test other keys need the exact K-th largest.
 template <class Src>
-__device__ unsigned long long radix_select(TopkShared &sh, const Src &src, unsigned int K, int hi, int lo) {
+__device__ __forceinline__ unsigned long long radix_select(TopkShared &sh, const Src &src, unsigned int K, int hi, int lo) {
   const int tid = threadIdx.x;
   unsigned long long prefix = 0ull, mask = 0ull;
   unsigned int k = K;
@@ -84,18 +88,19 @@ __device__ unsigned long long radix_select(TopkShared &sh, const Src &src, unsig
         const unsigned int y = __shfl_down(incl, off, kWave);
         if (lane + off < kWave) incl += y;
       }
-      unsigned int above = incl - s;  // keys with a digit in a higher lane
+      const unsigned int above = incl - s;  // keys with a digit in a higher lane
       if (above < k && k <= incl) {
-        const unsigned int hs[4] = {h0, h1, h2, h3};
-        for (int i = 3; i >= 0; --i) {
-          if (above + hs[i] >= k) {
-            sh.sel_prefix = (unsigned long long)(4 * lane + i);
-            sh.sel_k = k - above;
-            sh.sel_done = (hs[i] == k - above);
-            break;
-          }
-          above += hs[i];
-        }
+        // this lane's four digits, highest first
+        const unsigned int a3 = above, a2 = a3 + h3, a1 = a2 + h2, a0 = a1 + h1;
+        int i;
+        unsigned int ab, h;
+        if (a3 + h3 >= k) { i = 3; ab = a3; h = h3; }
+        else if (a2 + h2 >= k) { i = 2; ab = a2; h = h2; }
+        else if (a1 + h1 >= k) { i = 1; ab = a1; h = h1; }
+        else { i = 0; ab = a0; h = h0; }
+        sh.sel_prefix = (unsigned long long)(4 * lane + i);
+        sh.sel_k = k - ab;
+        sh.sel_done = (h == k - ab);
       }
     }
     __syncthreads();
@@ -113,34 +118,55 @@ __device__ unsigned long long radix_select(TopkShared &sh, const Src &src, unsig
 struct LdsKeys {
   const unsigned long long *keys;
   unsigned int n;
-  template <class F> __device__ void for_each(F f) const {
+  template <class F> __device__ __forceinline__ void for_each(F f) const {
     for (unsigned int i = threadIdx.x; i < n; i += kTopkThreads) f(keys[i]);
   }
 };
 
 struct LdsMax32 {  // per-thread maxima as 32-bit keys in the high word
   const unsigned int *m;
-  template <class F> __device__ void for_each(F f) const {
+  template <class F> __device__ __forceinline__ void for_each(F f) const {
     for (unsigned int i = threadIdx.x; i < (unsigned int)kTopkThreads; i += kTopkThreads)
       f((unsigned long long)m[i] << 32);
   }
 };
 
-template <int DT> struct RowKeys {  // every entry of a global row
-  const Row<DT> *row;
+// Entry source for a row of V logits: for_each(f) calls f(z, v) once for every
+// entry of the row (any order), kU 16-byte loads in flight per thread;
+// for_own(f) visits only the entries this thread visits in for_each.
+template <int DT> struct StreamRow {
+  static constexpr int NE = Elem<DT>::kVec;
+  static constexpr int kU = 8;
+  const Row<DT> &row;
   int V;
-  template <class F> __device__ void for_each(F f) const {
-    constexpr int NE = Elem<DT>::kVec;
-    const int nvec = row->nvec(V);
-    for (int iv = threadIdx.x; iv < nvec; iv += kTopkThreads) {
-      float z[NE];
-      row->load_vec(iv, z);
+  __device__ __forceinline__ StreamRow(const Row<DT> &r, int V_) : row(r), V(V_) {}
+  template <class F> __device__ __forceinline__ void for_each(F f) const {
+    const int nvec = row.nvec(V);
+    for (int base = threadIdx.x; base < nvec; base += kTopkThreads * kU) {
+      u32x4 d[kU];
 #pragma unroll
-      for (int e = 0; e < NE; ++e) {
-        const int v = iv * NE + e - row->s;
-        if (v >= 0 && v < V) f(entry_key(z[e], (uint32_t)v));
+      for (int u = 0; u < kU; ++u) d[u] = row.raw(base + u * kTopkThreads);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        float z[NE];
+        decode<DT>(d[u], z);
+        const int e0 = (base + u * kTopkThreads) * NE - row.s;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+          const int v = e0 + e;
+          if (v >= 0 && v < V) f(z[e], v);
+        }
       }
     }
+  }
+  template <class F> __device__ __forceinline__ void for_own(F f) const { for_each(f); }
+};
+
+// Keys of every entry of a source.
+template <class Src> struct SrcKeys {
+  const Src &src;
+  template <class F> __device__ __forceinline__ void for_each(F f) const {
+    src.for_each([&](float z, int v) { f(entry_key(z, (uint32_t)v)); });
   }
 };
 
@@ -154,43 +180,48 @@ struct TopkRow {
   unsigned int ncand;
 };
 
-template <int DT>
-__device__ TopkRow topk_row(TopkShared &sh, const Row<DT> &row, int V, int K, float c, int2 *list) {
-  constexpr int NE = Elem<DT>::kVec;
+template <class Src>
+__device__ __forceinline__ TopkRow topk_row(TopkShared &sh, const Src &src, int K, float c, int2 *list) {
   const int tid = threadIdx.x;
-  const int nvec = row.nvec(V);
 
-  // Phase A: per-thread maxima.
-  unsigned int mymax = 0u;
-  for (int iv = tid; iv < nvec; iv += kTopkThreads) {
-    float z[NE];
-    row.load_vec(iv, z);
-#pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      const int v = iv * NE + e - row.s;
-      if (v >= 0 && v < V) mymax = max(mymax, orderable(z[e]));
+  // Phase A (one pass over the row): this thread's four largest keys, kept
+  // sorted t0 >= t1 >= t2 >= t3 (0 = none; every real key is > 0).
+  unsigned long long t0 = 0ull, t1 = 0ull, t2 = 0ull, t3 = 0ull;
+  src.for_each([&](float z, int v) {
+    const unsigned long long key = entry_key(z, (uint32_t)v);
+    if (key > t3) {
+      t3 = key;
+      if (t3 > t2) { const unsigned long long x = t2; t2 = t3; t3 = x; }
+      if (t2 > t1) { const unsigned long long x = t1; t1 = t2; t2 = x; }
+      if (t1 > t0) { const unsigned long long x = t0; t0 = t1; t1 = x; }
     }
-  }
-  sh.tmax[tid] = mymax;
+  });
+  sh.tmax[tid] = (unsigned int)(t0 >> 32);  // the thread's largest orderable logit
   if (tid == 0) { sh.ncand = 0u; sh.nkept = 0u; }
   __syncthreads();
 
-  // Phase B: lower bound L = K-th largest per-thread maximum.
+  // Phase B: lower bound L = K-th largest per-thread maximum: K threads own an
+  // entry >= L each, so the K-th largest logit of the row is >= L.
   unsigned int L = 0u;
   if (K <= kTopkThreads) L = (unsigned int)(radix_select(sh, LdsMax32{sh.tmax}, (unsigned)K, 64, 32) >> 32);
+  const unsigned long long Lkey = (unsigned long long)L << 32;  // smallest key with logit >= L
 
-  // Phase C: gather entries with orderable(z) >= L.
-  for (int iv = tid; iv < nvec; iv += kTopkThreads) {
-    float z[NE];
-    row.load_vec(iv, z);
-#pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      const int v = iv * NE + e - row.s;
-      if (v >= 0 && v < V && orderable(z[e]) >= L) {
-        const unsigned int slot = atomicAdd(&sh.ncand, 1u);
-        if (slot < (unsigned int)kCap) sh.cand[slot] = entry_key(z[e], (uint32_t)v);
-      }
-    }
+  // Phase C: gather every entry with key >= Lkey into LDS.  A thread's stored
+  // keys are its four largest; only if all four pass can it own more, and then
+  // it scans its own entries again for the rest (keys below t3).
+  auto append = [&](unsigned long long key) {
+    const unsigned int slot = atomicAdd(&sh.ncand, 1u);
+    if (slot < (unsigned int)kCap) sh.cand[slot] = key;
+  };
+  if (t0 >= Lkey && t0 != 0ull) append(t0);
+  if (t1 >= Lkey && t1 != 0ull) append(t1);
+  if (t2 >= Lkey && t2 != 0ull) append(t2);
+  if (t3 >= Lkey && t3 != 0ull) {
+    append(t3);
+    src.for_own([&](float z, int v) {
+      const unsigned long long key = entry_key(z, (uint32_t)v);
+      if (key >= Lkey && key < t3) append(key);
+    });
   }
   __syncthreads();
   const unsigned int ncand = sh.ncand;
@@ -199,7 +230,7 @@ __device__ TopkRow topk_row(TopkShared &sh, const Row<DT> &row, int V, int K, fl
   // Phase D: threshold among the candidates.
   unsigned long long thr;
   if (in_lds) thr = radix_select(sh, LdsKeys{sh.cand, ncand}, (unsigned)K, 64, 0);
-  else thr = radix_select(sh, RowKeys<DT>{&row, V}, (unsigned)K, 64, 0);
+  else thr = radix_select(sh, SrcKeys<Src>{src}, (unsigned)K, 64, 0);
 
   // Phase E: statistics over kept entries (and the list).  The select may stop
   // with the low bits of `thr` cleared; that separates the K kept entries from
@@ -214,7 +245,7 @@ __device__ TopkRow topk_row(TopkShared &sh, const Row<DT> &row, int V, int K, fl
     }
   };
   if (in_lds) LdsKeys{sh.cand, ncand}.for_each(visit_max);
-  else RowKeys<DT>{&row, V}.for_each(visit_max);
+  else SrcKeys<Src>{src}.for_each(visit_max);
   zmax = wave_max_f(zmax);
   kmin = ~wave_max_u64(~kmin);
   if ((tid % kWave) == 0) {
@@ -245,7 +276,7 @@ __device__ TopkRow topk_row(TopkShared &sh, const Row<DT> &row, int V, int K, fl
     }
   };
   if (in_lds) LdsKeys{sh.cand, ncand}.for_each(visit_sum);
-  else RowKeys<DT>{&row, V}.for_each(visit_sum);
+  else SrcKeys<Src>{src}.for_each(visit_sum);
   S = wave_sum_f(S);
   if ((tid % kWave) == 0) sh.red_f[tid / kWave] = S;
   __syncthreads();
@@ -270,7 +301,7 @@ __device__ __forceinline__ float kept_prob(const TopkRow &r, float z, uint32_t v
 }
 
 template <int NT>
-__device__ unsigned long long block_max_u64_sh(unsigned long long x, unsigned long long *red) {
+__device__ __forceinline__ unsigned long long block_max_u64_sh(unsigned long long x, unsigned long long *red) {
   x = wave_max_u64(x);
   if ((threadIdx.x % kWave) == 0) red[threadIdx.x / kWave] = x;
   __syncthreads();
@@ -286,7 +317,7 @@ __device__ __forceinline__ unsigned long long bonus_key(const Args &a, uint32_t 
                                                        const TopkRow &qr, float z, uint32_t v) {
   if (z == -INFINITY || entry_key(z, v) < qr.thr) return 0ull;
   const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)pos, v >> 2, PURPOSE_SAMPLE);
-  const float E = exp2_variate(blk.w[v & 3u]);
+  const float E = exp2_variate(word_of(blk, v & 3u));
   return pack_key(fmaf(z, a.c, -__builtin_amdgcn_logf(E)), v);
 }
 
@@ -295,7 +326,7 @@ __device__ __forceinline__ unsigned long long bonus_key(const Args &a, uint32_t 
 // from `list` (K entries), from the LDS candidates of a row just selected, or
 // from a scan of the row with the threshold.
 template <int DT>
-__device__ unsigned long long gumbel_over_kept_q(TopkShared &sh, const Args &a, int b, int pos,
+__device__ __forceinline__ unsigned long long gumbel_over_kept_q(TopkShared &sh, const Args &a, int b, int pos,
                                                  const TopkRow &qr, const int2 *list, const Row<DT> &Q) {
   const uint32_t seq = seq_of(a, b);
   unsigned long long best = 0ull;
@@ -320,7 +351,7 @@ __device__ unsigned long long gumbel_over_kept_q(TopkShared &sh, const Args &a, 
 // Residual draw at rejected position n: weights max(0, q_n - p_n) over the
 // target row's kept entries (outside them q_n = 0 and the weight is 0).
 template <int DT>
-__device__ unsigned long long gumbel_residual_topk(TopkShared &sh, const Args &a, int b, int n,
+__device__ __forceinline__ unsigned long long gumbel_residual_topk(TopkShared &sh, const Args &a, int b, int n,
                                                    const TopkRow &pr, const TopkRow &qr, const int2 *qlist,
                                                    const Row<DT> &P, const Row<DT> &Q) {
   const uint32_t seq = seq_of(a, b);
@@ -333,7 +364,7 @@ __device__ unsigned long long gumbel_residual_topk(TopkShared &sh, const Args &a
     const float r = qv - pv;
     if (!(r > 0.0f)) return;
     const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)n, v >> 2, PURPOSE_SAMPLE);
-    const unsigned long long k = pack_key(r * __builtin_amdgcn_rcpf(exp2_variate(blk.w[v & 3u])), v);
+    const unsigned long long k = pack_key(r * __builtin_amdgcn_rcpf(exp2_variate(word_of(blk, v & 3u))), v);
     best = k > best ? k : best;
   };
   if (qlist) {
@@ -350,94 +381,104 @@ __device__ __forceinline__ size_t slot_of(const Args &a, int b, int s) {
   return (size_t)b * (2 * a.gamma) + s;
 }
 
+// Judge position j of sequence b against its selected rows (every lane of
+// wave 0 computes the same result).
+// Top-k of one global row.
 template <int DT>
-__global__ __launch_bounds__(kTopkThreads) void k_topk_rows(Args a) {
-  __shared__ TopkShared sh;
-  const int nrow = 2 * a.gamma;
-  const int b = blockIdx.x / nrow;
-  const int s = blockIdx.x - b * nrow;  // slot: draft j = s (s < gamma), target j = s - gamma
-  const void *ptr = s < a.gamma ? draft_row<DT>(a, b, s) : target_row<DT>(a, b, s - a.gamma);
-  const Row<DT> row(ptr, a.V);
-  int2 *list = a.lists ? a.lists + slot_of(a, b, s) * (size_t)a.klist : nullptr;
-  const TopkRow r = topk_row<DT>(sh, row, a.V, a.top_k, a.c, list);
-  if (threadIdx.x == 0) a.rowinfo[slot_of(a, b, s)] = pack_rowinfo(r);
-}
-
-// Wave 0 judges sequence b against the selected rows; returns n (or -1).
-template <int DT>
-__device__ int judge_topk(const Args &a, int b) {
-  const int lane = threadIdx.x;
-  const int gamma = a.gamma;
-  const bool active = lane < gamma;
-  const uint32_t seq = seq_of(a, b);
-  const float c = a.c;
-  int t = 0;
-  bool ok = true;
-  if (active) {
-    t = a.tokens[(size_t)b * gamma + lane];
-    ok = (t >= 0) && (t < a.V);
-  }
-  if (__ballot(active && !ok) != 0ull) {
-    write_invalid(a, b, lane);
-    return -1;
-  }
-  bool accept = false;
-  if (active) {
-    const TopkRow pr = unpack_rowinfo(a.rowinfo[slot_of(a, b, lane)]);
-    const TopkRow qr = unpack_rowinfo(a.rowinfo[slot_of(a, b, gamma + lane)]);
-    const float zp = Row<DT>(draft_row<DT>(a, b, lane), a.V).load_one(t);
-    const float zq = Row<DT>(target_row<DT>(a, b, lane), a.V).load_one(t);
-    const bool qzero = zq == -INFINITY || entry_key(zq, (uint32_t)t) < qr.thr;
-    const bool pzero = zp == -INFINITY || entry_key(zp, (uint32_t)t) < pr.thr;
-    const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)lane, 0u, PURPOSE_ACCEPT);
-    const float u = accept_uniform(blk.w[0]);
-    float ratio;
-    if (qzero) ratio = 0.0f;
-    else if (pzero) ratio = INFINITY;
-    else ratio = __builtin_amdgcn_exp2f(c * (zq - zp) - (qr.R - pr.R)) * (pr.S / qr.S);
-    accept = !qzero && (pzero || u < ratio);
-    if (a.token_probs) {
-      a.token_probs[((size_t)b * gamma + lane) * 2 + 0] = pzero ? 0.0f : __builtin_amdgcn_exp2f(fmaf(zp, c, -pr.R)) / pr.S;
-      a.token_probs[((size_t)b * gamma + lane) * 2 + 1] = qzero ? 0.0f : __builtin_amdgcn_exp2f(fmaf(zq, c, -qr.R)) / qr.S;
-    }
-    if (a.accept_ur) {
-      a.accept_ur[((size_t)b * gamma + lane) * 2 + 0] = u;
-      a.accept_ur[((size_t)b * gamma + lane) * 2 + 1] = ratio;
-    }
-  }
-  const int n = first_rejection(__ballot(active && accept), gamma);
-  write_judged(a, b, lane, n);
-  return n;
+__device__ __forceinline__ TopkRow select_row(TopkShared &sh, const Row<DT> &row, int V, int K, float c, int2 *list) {
+  const StreamRow<DT> src(row, V);
+  return topk_row(sh, src, K, c, list);
 }
 
 template <int DT>
-__global__ __launch_bounds__(kTopkThreads) void k_topk_finish(Args a) {
-  __shared__ TopkShared sh;
-  const int b = blockIdx.x;
+__device__ __forceinline__ Judged judge_topk(const Args &a, int b, int j) {
   const int gamma = a.gamma;
+  const TopkRow pr = unpack_rowinfo(a.rowinfo[slot_of(a, b, j)]);
+  const TopkRow qr = unpack_rowinfo(a.rowinfo[slot_of(a, b, gamma + j)]);
+  const int t = a.tokens[(size_t)b * gamma + j];
+  const float zp = Row<DT>(draft_row<DT>(a, b, j), a.V).load_one(t);
+  const float zq = Row<DT>(target_row<DT>(a, b, j), a.V).load_one(t);
+  const bool qzero = zq == -INFINITY || entry_key(zq, (uint32_t)t) < qr.thr;
+  const bool pzero = zp == -INFINITY || entry_key(zp, (uint32_t)t) < pr.thr;
+  return judge_one(a, seq_of(a, b), j, zp, zq, pzero, qzero, pr.R, pr.S, qr.R, qr.S);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kTopkThreads) void k_topk_step(Args a, int j) {
+  __shared__ TopkShared sh;
+  const int b = blockIdx.x >> 1;
+  const int r = blockIdx.x & 1;  // 0: draft row (and the sequence's lead), 1: target row
+  const bool lead = r == 0;
+  const int gamma = a.gamma;
+  int32_t *state_in = a.state + (size_t)((j + 1) & 1) * a.B;
+  int32_t *state_out = a.state + (size_t)(j & 1) * a.B;
+
   if (threadIdx.x < kWave) {
-    const int n = judge_topk<DT>(a, b);
-    if (threadIdx.x == 0) sh.bcast_n = n;
+    const int lane = threadIdx.x;
+    int mode = 0;  // 0 select row j, 1 residual at j-1, 2 bonus, -1 nothing
+    if (j == 0) {
+      if (!tokens_valid(a, b)) {
+        mode = -1;
+        if (lead) {
+          write_invalid(a, b, lane);
+          for (int k = lane; k < gamma; k += kWave) write_diag(a, b, k, NAN, NAN, NAN, NAN);
+          if (lane == 0) state_out[b] = kInvalid;
+        }
+      } else if (lead) {
+        for (int k = lane; k < gamma; k += kWave) write_diag(a, b, k, NAN, NAN, NAN, NAN);
+        if (lane == 0) state_out[b] = 0;
+      }
+    } else {
+      const int s = state_in[b];
+      if (s != j - 1) {
+        mode = -1;
+        if (lead && lane == 0) state_out[b] = s;
+      } else {
+        const Judged jr = judge_topk<DT>(a, b, j - 1);
+        if (lead && lane == 0) write_diag(a, b, j - 1, jr.pt, jr.qt, jr.u, jr.ratio);
+        if (!jr.accept) {
+          mode = lead ? 1 : -1;
+          if (lead) write_judged(a, b, lane, j - 1);
+          if (lead && lane == 0) state_out[b] = kDone;
+        } else if (j == gamma) {
+          mode = lead ? 2 : -1;
+          if (lead) write_judged(a, b, lane, gamma);
+          if (lead && lane == 0) state_out[b] = kDone;
+        } else if (lead && lane == 0) {
+          state_out[b] = j;
+        }
+      }
+    }
+    if (lane == 0) sh.bcast_n = mode;
   }
   __syncthreads();
-  const int n = sh.bcast_n;
-  if (n < 0) return;
+  const int mode = sh.bcast_n;
+  if (mode < 0) return;
   int32_t *out = a.out_tokens + (size_t)b * (gamma + 1);
-  const Row<DT> Q(target_row<DT>(a, b, n), a.V);
-  unsigned long long k;
-  if (n < gamma) {
+  if (mode == 0) {
+    const int slot = r == 0 ? j : gamma + j;
+    const void *ptr = r == 0 ? draft_row<DT>(a, b, j) : target_row<DT>(a, b, j);
+    const Row<DT> row(ptr, a.V);
+    int2 *list = a.lists ? a.lists + slot_of(a, b, slot) * (size_t)a.klist : nullptr;
+    const TopkRow tr = select_row<DT>(sh, row, a.V, a.top_k, a.c, list);
+    if (threadIdx.x == 0) a.rowinfo[slot_of(a, b, slot)] = pack_rowinfo(tr);
+  } else if (mode == 1) {
+    const int n = j - 1;
     const TopkRow pr = unpack_rowinfo(a.rowinfo[slot_of(a, b, n)]);
     const TopkRow qr = unpack_rowinfo(a.rowinfo[slot_of(a, b, gamma + n)]);
     const int2 *qlist = a.lists ? a.lists + slot_of(a, b, gamma + n) * (size_t)a.klist : nullptr;
     const Row<DT> P(draft_row<DT>(a, b, n), a.V);
-    k = gumbel_residual_topk<DT>(sh, a, b, n, pr, qr, qlist, P, Q);
+    const Row<DT> Q(target_row<DT>(a, b, n), a.V);
+    unsigned long long k = gumbel_residual_topk<DT>(sh, a, b, n, pr, qr, qlist, P, Q);
     if (k == 0ull) k = gumbel_over_kept_q<DT>(sh, a, b, n, qr, qlist, Q);
+    if (threadIdx.x == 0) out[n] = (int32_t)packed_index(k);
   } else {
     // every draft kept: top-k of target row gamma, then the bonus draw
-    const TopkRow qr = topk_row<DT>(sh, Q, a.V, a.top_k, a.c, nullptr);
-    k = gumbel_over_kept_q<DT>(sh, a, b, gamma, qr, nullptr, Q);
+    const Row<DT> Q(target_row<DT>(a, b, gamma), a.V);
+    const TopkRow qr = select_row<DT>(sh, Q, a.V, a.top_k, a.c, nullptr);
+    const unsigned long long k = gumbel_over_kept_q<DT>(sh, a, b, gamma, qr, nullptr, Q);
+    if (threadIdx.x == 0) out[gamma] = (int32_t)packed_index(k);
   }
-  if (threadIdx.x == 0) out[n] = (int32_t)packed_index(k);
 }
 
 }  // namespace sv

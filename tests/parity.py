@@ -10,7 +10,9 @@ same Philox streams):
         1e-5 (a knife-edge arg-max);
   * the rate of non-exempt mismatches is <= 1e-4;
   * p_j(t_j), q_j(t_j) within 1e-5 relative of the oracle where the oracle's
-    value is >= 1e-30; the acceptance uniforms equal exactly.
+    value is >= 1e-30, and the acceptance uniforms equal exactly, at every
+    position both sides judged; positions the GPU did not judge (after its
+    first rejection) report NaN.
 """
 from __future__ import annotations
 
@@ -120,7 +122,10 @@ def compare(w, seed: int, g: GpuResult, seq_offset: int = 0, rows=None, nthreads
             rep.sequences += 1
             _compare_seq(rep, w, b, i, res, g)
             if check_probs and g.token_probs is not None:
-                _compare_probs(rep, w, seed, seq_offset, b, pt[i], qt[i], g)
+                n_o, n_g = int(res.n_accepted[i]), int(g.n_accepted[b])
+                if n_o >= 0 and n_g >= 0:
+                    _compare_probs(rep, w, seed, seq_offset, b, pt[i], qt[i], g, min(n_o, n_g, w.gamma - 1) + 1,
+                                   min(n_g + 1, w.gamma))
     return rep
 
 
@@ -161,9 +166,12 @@ def _compare_seq(rep: Report, w, b: int, i: int, res, g: GpuResult):
                                           int(g.out_tokens[b, n_o]), float(res.gap[i])))
 
 
-def _compare_probs(rep: Report, w, seed: int, seq_offset: int, b: int, pt, qt, g: GpuResult):
+def _compare_probs(rep: Report, w, seed: int, seq_offset: int, b: int, pt, qt, g: GpuResult, both: int,
+                   judged_g: int):
+    """Positions [0, both) were judged on both sides; the GPU judged
+    [0, judged_g) and must report NaN after that."""
     gamma = w.tokens.shape[1]
-    for j in range(gamma):
+    for j in range(both):
         for o_val, g_val in ((pt[j], g.token_probs[b, j, 0]), (qt[j], g.token_probs[b, j, 1])):
             if o_val >= PROB_FLOOR:
                 rel = abs(float(g_val) - o_val) / o_val
@@ -176,3 +184,8 @@ def _compare_probs(rep: Report, w, seed: int, seq_offset: int, b: int, pt, qt, g
         u_o = O.uniform_accept(O.word(seed, seq_offset + b, j, 0, O.ACCEPT))
         if float(g.accept_ur[b, j, 0]) != u_o:
             rep.u_failures += 1
+    for j in range(judged_g, gamma):
+        if not (np.all(np.isnan(g.token_probs[b, j])) and np.all(np.isnan(g.accept_ur[b, j]))):
+            rep.prob_failures += 1
+            if len(rep.mismatch_examples) < 10:
+                rep.mismatch_examples.append(("unjudged-not-nan", b, j))

@@ -58,8 +58,9 @@ def test_workspace_bytes(L):
 
 def test_launch_names(L):
     import rejection_sampling_verify_17_amd as S
-    assert S.launch_names(64, 5, 128256, 1, 0) == ["k_stats", "k_sample", "k_pick"]
-    assert S.launch_names(256, 8, 152064, 1, 50) == ["k_topk_rows", "k_topk_finish"]
+    # one launch per position 0..gamma, then the pick (the top-k path picks in place)
+    assert S.launch_names(64, 5, 128256, 1, 0) == ["k_step"] * 6 + ["k_pick"]
+    assert S.launch_names(256, 8, 152064, 1, 50) == ["k_topk_step"] * 9
 
 
 def _call(L, **over):
