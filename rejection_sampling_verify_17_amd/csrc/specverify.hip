@@ -18,6 +18,7 @@ using namespace sv;
 constexpr int kMaxGamma = 64;           // one wave ballots all positions
 constexpr int kMaxV = 1 << 28;          // byte offsets of a row fit 32 bits
 constexpr int kListMax = 1024;          // top-k lists kept up to this K
+constexpr double kSmallRows = 256e6;    // bytes of all rows below which one launch reads them all
 #ifndef SV_TARGET_TILES
 #define SV_TARGET_TILES 4096
 #endif
@@ -28,7 +29,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
   bool topk;
-  int nch, nvec, cv, ngb, cv2, klist;
+  int window;  // positions whose statistics one launch computes (dense path)
+  int nch, nvec, cv, nchw, ngb, cv2, klist;
   size_t off_part, off_bestpart, off_nseq, off_state, off_rowinfo, off_lists;
   size_t total;
 };
@@ -46,19 +48,27 @@ Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype
   p.topk = top_k > 0 && top_k < V;
   p.klist = (p.topk && top_k <= kListMax) ? top_k : 0;
   if (!p.topk) {
-    // blocks per sequence: about kTargetTiles blocks per launch, each thread
-    // keeping at least two vectors of a row
+    // Reading rows past the first rejection costs bytes; every extra launch
+    // costs a fixed ~10 us.  When all rows together are small, one launch
+    // reads them all; otherwise one position per launch.
+    const double all_rows = 2.0 * B * gamma * (double)V * (dtype == SV_BF16 ? 2 : 4);
+    p.window = all_rows <= kSmallRows ? gamma : 1;
+    // about kTargetTiles blocks per launch, each thread keeping at least two
+    // vectors (statistics) or two group blocks (sampling)
     const int max_ch = std::max(1, p.nvec / (2 * kThreads));
-    p.nch = std::max(1, std::min((kTargetTiles + B - 1) / B, max_ch));
+    const int rows = B * p.window;
+    p.nch = std::max(1, std::min((kTargetTiles + rows - 1) / rows, max_ch));
     p.cv = (p.nvec + p.nch - 1) / p.nch;
-    p.cv2 = (p.ngb + p.nch - 1) / p.nch;
+    const int max_chw = std::max(1, p.ngb / (2 * kThreads));
+    p.nchw = std::max(1, std::min((kTargetTiles + B - 1) / B, max_chw));
+    p.cv2 = (p.ngb + p.nchw - 1) / p.nchw;
   }
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
   // Nothing here is read before this call writes it: the workspace needs no
   // initialisation and may serve calls of any shape in turn.
   p.off_part = take(p.topk ? 0 : (size_t)B * gamma * p.nch * sizeof(float4));
-  p.off_bestpart = take(p.topk ? 0 : (size_t)B * p.nch * sizeof(unsigned long long));
+  p.off_bestpart = take(p.topk ? 0 : (size_t)B * p.nchw * sizeof(unsigned long long));
   p.off_nseq = take((size_t)B * sizeof(int32_t));
   p.off_state = take((size_t)2 * B * sizeof(int32_t));
   const size_t slots = (size_t)B * (2 * gamma);
@@ -85,10 +95,18 @@ struct Launches {
     };
     bool ok = true;
     if (!p.topk) {
-      for (int j = 0; j <= a.gamma; ++j) {
+      int launch = 0, p0 = 0;
+      for (int w0 = 0;; ) {
+        const int w1 = std::min(a.gamma, w0 + p.window);
+        const int dw = w1 > w0 ? w1 - w0 : 1;
         before();
-        hipLaunchKernelGGL(k_step<DT>, dim3(a.B * p.nch), dim3(kThreads), 0, stream, a, j);
+        const int per_seq = std::max(dw * p.nch, p.nchw);
+        hipLaunchKernelGGL(k_step<DT>, dim3(a.B * per_seq), dim3(kThreads), 0, stream, a, launch, p0, w0, w1);
         ok = ok && after();
+        ++launch;
+        if (w0 == a.gamma) break;
+        p0 = w0;
+        w0 = w1;
       }
       before();
       const int waves = kThreads / kWave;
@@ -145,6 +163,7 @@ sv_status verify_impl(const void *target, const void *draft, const int32_t *toke
   a.nseq = (int32_t *)(ws + p.off_nseq);
   a.state = (int32_t *)(ws + p.off_state);
   a.nch = p.nch;
+  a.nchw = p.nchw;
   a.nvec = p.nvec;
   a.cv = p.cv;
   a.ngb = p.ngb;
@@ -199,11 +218,12 @@ sv_status sv_verify_timed(const void *target_logits, const void *draft_logits, c
 
 const char *sv_launch_name(int32_t B, int32_t gamma, int32_t V, int32_t dtype, int32_t top_k, int32_t i) {
   if (!shape_ok(B, gamma, V, dtype)) return nullptr;
-  const bool topk = top_k > 0 && top_k < V;
+  const Plan p = make_plan(B, gamma, V, top_k, dtype);
   if (i < 0) return nullptr;
-  if (i <= gamma) return topk ? "k_topk_step" : "k_step";
-  if (!topk && i == gamma + 1) return "k_pick";
-  return nullptr;
+  if (p.topk) return i <= gamma ? "k_topk_step" : nullptr;
+  const int steps = (gamma + p.window - 1) / p.window + 1;  // windows, then the judge-only launch
+  if (i < steps) return "k_step";
+  return i == steps ? "k_pick" : nullptr;
 }
 
 const char *sv_status_string(sv_status s) {

@@ -1,28 +1,31 @@
 // Verification kernels, dense path (no top-k filter).
 //
 // The rule judges drafts left to right and discards everything after the
-// first rejection, so rows after it are never read.  One launch per position:
+// first rejection, so rows after it need not be read.  Launches walk the
+// positions in windows [w0, w1) (one position each for large batches, all of
+// them at once when the whole input is small and launches would dominate):
 //
-//   k_step(j = 0)   every sequence: partial base-2 softmax statistics (R, S) of
-//                   draft row 0 and target row 0, one vocabulary chunk per block.
-//   k_step(j >= 1)  every block of a sequence still alive at j-1 first judges
-//                   position j-1 itself (wave 0 merges that row pair's
-//                   partials, evaluates q(t)/p(t) in registers and draws u),
-//                   then, on its chunk:
-//                     accepted, j < gamma:  statistics of row pair j;
-//                     accepted, j = gamma:  Gumbel-max winner over target row
-//                                           gamma (the bonus token);
-//                     rejected:             Gumbel-max winner over the residual
-//                                           max(0, q - p) of row pair j-1.
+//   k_step(first window)  every sequence: partial base-2 softmax statistics
+//                   (R, S) of draft and target rows w0..w1-1, one vocabulary
+//                   chunk per block.
+//   k_step(next windows)  every block of a sequence still alive first judges
+//                   the previous window itself (wave 0: lane l merges row pair
+//                   l's partials, evaluates q(t)/p(t) in registers and draws
+//                   u; a ballot finds the first rejection), then, on its chunk:
+//                     all accepted, window left:  statistics of its row;
+//                     all accepted, none left:    Gumbel-max winner over
+//                                                 target row gamma (bonus);
+//                     rejected at n:              Gumbel-max winner over the
+//                                                 residual max(0, q - p) of row n.
 //                   Memory-bound statistics of live sequences and VALU-bound
 //                   sampling of finished ones share each launch.
 //   k_pick          one wave per sequence: the best chunk winner is the token.
 //
-// A per-sequence state (double-buffered by launch parity, so blocks of one
-// launch read what the previous launch wrote) says whether the sequence is
-// alive at j-1.  Blocks never signal each other inside a launch: results cross
-// launch boundaries only (on this GPU an agent-scope fence is a write-back and
-// invalidation of the whole L2, far too dear to pay per block).
+// A per-sequence state (double-buffered by launch index parity, so blocks of
+// one launch read what the previous launch wrote) says whether the sequence
+// is alive at the window start.  Blocks never signal each other inside a launch:
+// results cross launch boundaries only (on this GPU an agent-scope fence is a
+// write-back and invalidation of the whole L2, far too dear to pay per block).
 //
 // The rule is that of page "스펙큘러티브 디코딩 — 작은 모델이 먼저 쓰고 큰 모델이
 // 검사한다" (blog.mna-game.duckdns.org post 46), §1, and page "추측 디코딩: 큰 모델을
@@ -35,8 +38,9 @@ namespace sv {
 
 constexpr int kThreads = 256;
 
-// Per-sequence state between launches: j >= 0 means "alive: rows 0..j-1
-// accepted and row pair j's statistics written"; anything else means done.
+// Per-sequence state between launches: w >= 0 means "alive: every position
+// before the last window accepted and the last window's statistics written,
+// up to row w"; anything else means done.
 constexpr int kDone = -1;
 constexpr int kInvalid = -2;
 
@@ -54,11 +58,12 @@ struct Args {
   float *accept_ur;        // [B][gamma][2] or null
   // workspace
   float4 *part;            // [B][gamma][nch] {Rp, Sp, Rq, Sq}
-  unsigned long long *bestpart;  // [B][nch] chunk winners (0 = none)
+  unsigned long long *bestpart;  // [B][nchw] chunk winners (0 = none)
   int32_t *nseq;           // [B] n, or -1 for an invalid sequence
   int32_t *state;          // [2][B] launch-parity double buffer
-  int32_t nch;             // blocks (vocabulary chunks) per sequence
+  int32_t nch;             // statistics: vocabulary chunks per row
   int32_t nvec, cv;        // statistics: 16-byte vectors per row (any alignment), per chunk
+  int32_t nchw;            // sampling: vocabulary chunks of the sampled row
   int32_t ngb, cv2;        // sampling: group blocks per row, per chunk
   // top-k path
   uint4 *rowinfo;          // [B][2*gamma] {thr lo, thr hi, R bits, S bits}
@@ -261,24 +266,32 @@ __device__ unsigned long long chunk_winner(const Args &a, int b, int pos, bool r
 }
 
 // ---------------------------------------------------------------------------
-// One launch per position j = 0..gamma (see the top of this file).
+// One launch per window of positions (see the top of this file).  A launch
+// judges the previous window [p0, w0) and computes statistics of the rows of
+// its own window [w0, w1) (w0 = w1 = gamma: the last launch, judge only).
+// Blocks per sequence: max(dw x nch, nchw), dw = max(1, w1 - w0).  For
+// statistics block (r, ch) handles chunk ch of row w0 + r; for sampling block
+// ch handles chunk ch of the sampled row; blocks beyond that count exit.
 // ---------------------------------------------------------------------------
 template <int DT>
-__global__ __launch_bounds__(kThreads) void k_step(Args a, int j) {
-  const int b = blockIdx.x / a.nch;
-  const int ch = blockIdx.x - b * a.nch;
+__global__ __launch_bounds__(kThreads) void k_step(Args a, int launch, int p0, int w0, int w1) {
+  const int dw = w1 > w0 ? w1 - w0 : 1;
+  const int per_seq = max(dw * a.nch, a.nchw);
+  const int b = blockIdx.x / per_seq;
+  const int rem = blockIdx.x - b * per_seq;
   const int gamma = a.gamma;
-  const bool lead = ch == 0;  // writes the sequence's outputs and state
-  int32_t *state_in = a.state + (size_t)((j + 1) & 1) * a.B;
-  int32_t *state_out = a.state + (size_t)(j & 1) * a.B;
+  const bool lead = rem == 0;  // writes the sequence's outputs and state
+  int32_t *state_in = a.state + (size_t)((launch + 1) & 1) * a.B;
+  int32_t *state_out = a.state + (size_t)(launch & 1) * a.B;
 
-  __shared__ int sh_mode;   // 0 stats of row j, 1 residual of row j-1, 2 bonus, -1 nothing
+  __shared__ int sh_mode;   // 0 statistics, 1 residual, 2 bonus, -1 nothing
+  __shared__ int sh_row;    // row to sample (residual)
   __shared__ float4 sh_st;
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
-    int mode = 0;
+    int mode = 0, row = 0;
     float4 st = make_float4(0.f, 1.f, 0.f, 1.f);
-    if (j == 0) {
+    if (w0 == 0) {
       if (!tokens_valid(a, b)) {
         mode = -1;
         if (lead) {
@@ -288,46 +301,59 @@ __global__ __launch_bounds__(kThreads) void k_step(Args a, int j) {
         }
       } else if (lead) {
         for (int k = lane; k < gamma; k += kWave) write_diag(a, b, k, NAN, NAN, NAN, NAN);
-        if (lane == 0) state_out[b] = 0;
+        if (lane == 0) state_out[b] = w1;
       }
     } else {
       const int s = state_in[b];
-      if (s != j - 1) {
-        mode = -1;  // finished (or invalid) before position j-1
+      if (s != w0) {
+        mode = -1;  // finished (or invalid) before this window
         if (lead && lane == 0) state_out[b] = s;
       } else {
-        // judge position j-1: merge its row pair's partial statistics (lanes
-        // stride over chunks), then one lane evaluates the ratio
+        // judge positions p0..w0-1: lane l merges the partial statistics of
+        // row pair p0 + l, evaluates its ratio and draws its u; a ballot of
+        // the accept bits finds the first rejection
+        const int nj = w0 - p0;
+        const bool act = lane < nj;
+        const int jpos = p0 + (act ? lane : 0);
         float Rp = -INFINITY, Sp = 0.0f, Rq = -INFINITY, Sq = 0.0f;
-        const float4 *pp = a.part + ((size_t)b * gamma + (j - 1)) * a.nch;
-        for (int k = lane; k < a.nch; k += kWave) {
-          const float4 v = pp[k];
-          merge_stats(Rp, Sp, v.x, v.y);
-          merge_stats(Rq, Sq, v.z, v.w);
+        bool accept = false;
+        if (act) {
+          const float4 *pp = a.part + ((size_t)b * gamma + jpos) * a.nch;
+          for (int k = 0; k < a.nch; ++k) {
+            const float4 v = pp[k];
+            merge_stats(Rp, Sp, v.x, v.y);
+            merge_stats(Rq, Sq, v.z, v.w);
+          }
+          const int t = a.tokens[(size_t)b * gamma + jpos];
+          const float zp = Row<DT>(draft_row<DT>(a, b, jpos), a.V).load_one(t);
+          const float zq = Row<DT>(target_row<DT>(a, b, jpos), a.V).load_one(t);
+          const Judged jr =
+              judge_one(a, seq_of(a, b), jpos, zp, zq, zp == -INFINITY, zq == -INFINITY, Rp, Sp, Rq, Sq);
+          accept = jr.accept;
+          if (lead) write_diag(a, b, jpos, jr.pt, jr.qt, jr.u, jr.ratio);
         }
-        wave_merge_stats(Rp, Sp);
-        wave_merge_stats(Rq, Sq);
-        st = make_float4(Rp, Sp, Rq, Sq);
-        const int t = a.tokens[(size_t)b * gamma + (j - 1)];
-        const float zp = Row<DT>(draft_row<DT>(a, b, j - 1), a.V).load_one(t);
-        const float zq = Row<DT>(target_row<DT>(a, b, j - 1), a.V).load_one(t);
-        const Judged r = judge_one(a, seq_of(a, b), j - 1, zp, zq, zp == -INFINITY, zq == -INFINITY, Rp, Sp, Rq, Sq);
-        if (lead && lane == 0) write_diag(a, b, j - 1, r.pt, r.qt, r.u, r.ratio);
-        if (!r.accept) {
+        const unsigned long long mask = __ballot(act && accept);
+        const int k = (mask == ~0ull) ? kWave : __builtin_ctzll(~mask);  // first clear bit
+        if (lead && act && lane > k) write_diag(a, b, jpos, NAN, NAN, NAN, NAN);  // judged after the rejection
+        if (k < nj) {
           mode = 1;
-          if (lead) write_judged(a, b, lane, j - 1);
+          row = p0 + k;
+          st = make_float4(__shfl(Rp, k, kWave), __shfl(Sp, k, kWave), __shfl(Rq, k, kWave), __shfl(Sq, k, kWave));
+          if (lead) write_judged(a, b, lane, row);
           if (lead && lane == 0) state_out[b] = kDone;
-        } else if (j == gamma) {
+        } else if (w0 == gamma) {
           mode = 2;
+          row = gamma;
           if (lead) write_judged(a, b, lane, gamma);
           if (lead && lane == 0) state_out[b] = kDone;
         } else if (lead && lane == 0) {
-          state_out[b] = j;
+          state_out[b] = w1;
         }
       }
     }
     if (lane == 0) {
       sh_mode = mode;
+      sh_row = row;
       sh_st = st;
     }
   }
@@ -335,14 +361,18 @@ __global__ __launch_bounds__(kThreads) void k_step(Args a, int j) {
   const int mode = sh_mode;
   if (mode < 0) return;
   if (mode == 0) {
+    if (rem >= dw * a.nch) return;
+    const int r = rem / a.nch;
+    const int ch = rem - r * a.nch;
+    const int j = w0 + r;
     const int v0 = ch * a.cv;
-    const float4 p = chunk_stats<DT>(a, b, j, v0, min(a.nvec, v0 + a.cv));
-    if (threadIdx.x == 0) a.part[((size_t)b * gamma + j) * a.nch + ch] = p;
+    const float4 pst = chunk_stats<DT>(a, b, j, v0, min(a.nvec, v0 + a.cv));
+    if (threadIdx.x == 0) a.part[((size_t)b * gamma + j) * a.nch + ch] = pst;
   } else {
-    const int g0 = ch * a.cv2;
-    const unsigned long long w =
-        chunk_winner<DT>(a, b, mode == 1 ? j - 1 : gamma, mode == 1, sh_st, g0, min(a.ngb, g0 + a.cv2));
-    if (threadIdx.x == 0) a.bestpart[(size_t)b * a.nch + ch] = w;
+    if (rem >= a.nchw) return;
+    const int g0 = rem * a.cv2;
+    const unsigned long long w = chunk_winner<DT>(a, b, sh_row, mode == 1, sh_st, g0, min(a.ngb, g0 + a.cv2));
+    if (threadIdx.x == 0) a.bestpart[(size_t)b * a.nchw + rem] = w;
   }
 }
 
@@ -359,8 +389,8 @@ __global__ __launch_bounds__(kThreads) void k_pick(Args a) {
   const int n = a.nseq[b];
   if (n < 0 || n > a.gamma) return;
   unsigned long long best = 0ull;
-  for (int i = lane; i < a.nch; i += kWave) {
-    const unsigned long long k = a.bestpart[(size_t)b * a.nch + i];
+  for (int i = lane; i < a.nchw; i += kWave) {
+    const unsigned long long k = a.bestpart[(size_t)b * a.nchw + i];
     best = k > best ? k : best;
   }
   best = wave_max_u64(best);

@@ -132,17 +132,18 @@ struct LdsMax32 {  // per-thread maxima as 32-bit keys in the high word
 };
 
 // Entry source for a row of V logits: for_each(f) calls f(z, v) once for every
-// entry of the row (any order), kU 16-byte loads in flight per thread;
-// for_own(f) visits only the entries this thread visits in for_each.
+// entry of the row (any order), kU 16-byte loads in flight per thread.
 template <int DT> struct StreamRow {
   static constexpr int NE = Elem<DT>::kVec;
   static constexpr int kU = 8;
   const Row<DT> &row;
-  int V;
-  __device__ __forceinline__ StreamRow(const Row<DT> &r, int V_) : row(r), V(V_) {}
+  int e0, e1;  // entries [e0, e1) of the row
+  __device__ __forceinline__ StreamRow(const Row<DT> &r, int V) : row(r), e0(0), e1(V) {}
+  __device__ __forceinline__ StreamRow(const Row<DT> &r, int lo, int hi) : row(r), e0(lo), e1(hi) {}
   template <class F> __device__ __forceinline__ void for_each(F f) const {
-    const int nvec = row.nvec(V);
-    for (int base = threadIdx.x; base < nvec; base += kTopkThreads * kU) {
+    const int iv0 = (e0 + row.s) / NE;            // vector holding entry e0
+    const int iv1 = (e1 - 1 + row.s) / NE + 1;    // one past the vector holding e1 - 1
+    for (int base = iv0 + (int)threadIdx.x; base < iv1; base += kTopkThreads * kU) {
       u32x4 d[kU];
 #pragma unroll
       for (int u = 0; u < kU; ++u) d[u] = row.raw(base + u * kTopkThreads);
@@ -150,16 +151,15 @@ template <int DT> struct StreamRow {
       for (int u = 0; u < kU; ++u) {
         float z[NE];
         decode<DT>(d[u], z);
-        const int e0 = (base + u * kTopkThreads) * NE - row.s;
+        const int ev = (base + u * kTopkThreads) * NE - row.s;
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
-          const int v = e0 + e;
-          if (v >= 0 && v < V) f(z[e], v);
+          const int v = ev + e;
+          if (v >= e0 && v < e1 && base + u * kTopkThreads < iv1) f(z[e], v);
         }
       }
     }
   }
-  template <class F> __device__ __forceinline__ void for_own(F f) const { for_each(f); }
 };
 
 // Keys of every entry of a source.
@@ -180,23 +180,27 @@ struct TopkRow {
   unsigned int ncand;
 };
 
+// Exact threshold of a top-K select over the entries `src` enumerates: the
+// K-th largest key (K <= number of entries).  Leaves the candidates in LDS
+// (sh.cand[0..ncand) when in_lds; otherwise they are the source's entries).
+struct Selected {
+  unsigned long long thr;
+  bool in_lds;
+  unsigned int ncand;
+};
+
 template <class Src>
-__device__ __forceinline__ TopkRow topk_row(TopkShared &sh, const Src &src, int K, float c, int2 *list) {
+__device__ __forceinline__ Selected select_threshold(TopkShared &sh, const Src &src, int K) {
   const int tid = threadIdx.x;
 
-  // Phase A (one pass over the row): this thread's four largest keys, kept
-  // sorted t0 >= t1 >= t2 >= t3 (0 = none; every real key is > 0).
-  unsigned long long t0 = 0ull, t1 = 0ull, t2 = 0ull, t3 = 0ull;
-  src.for_each([&](float z, int v) {
-    const unsigned long long key = entry_key(z, (uint32_t)v);
-    if (key > t3) {
-      t3 = key;
-      if (t3 > t2) { const unsigned long long x = t2; t2 = t3; t3 = x; }
-      if (t2 > t1) { const unsigned long long x = t1; t1 = t2; t2 = x; }
-      if (t1 > t0) { const unsigned long long x = t0; t0 = t1; t1 = x; }
-    }
+  // Phase A: per-thread maximum logit (a float max per entry).
+  float zmax = -INFINITY;
+  bool any = false;
+  src.for_each([&](float z, int) {
+    zmax = fmaxf(zmax, z);
+    any = true;
   });
-  sh.tmax[tid] = (unsigned int)(t0 >> 32);  // the thread's largest orderable logit
+  sh.tmax[tid] = any ? orderable(zmax) : 0u;  // 0: no entry (every real key is > 0)
   if (tid == 0) { sh.ncand = 0u; sh.nkept = 0u; }
   __syncthreads();
 
@@ -204,25 +208,18 @@ __device__ __forceinline__ TopkRow topk_row(TopkShared &sh, const Src &src, int 
   // entry >= L each, so the K-th largest logit of the row is >= L.
   unsigned int L = 0u;
   if (K <= kTopkThreads) L = (unsigned int)(radix_select(sh, LdsMax32{sh.tmax}, (unsigned)K, 64, 32) >> 32);
-  const unsigned long long Lkey = (unsigned long long)L << 32;  // smallest key with logit >= L
+  const bool take_all = L == 0u;
+  const float Lf = take_all ? -INFINITY : from_orderable(L);
 
-  // Phase C: gather every entry with key >= Lkey into LDS.  A thread's stored
-  // keys are its four largest; only if all four pass can it own more, and then
-  // it scans its own entries again for the rest (keys below t3).
-  auto append = [&](unsigned long long key) {
-    const unsigned int slot = atomicAdd(&sh.ncand, 1u);
-    if (slot < (unsigned int)kCap) sh.cand[slot] = key;
-  };
-  if (t0 >= Lkey && t0 != 0ull) append(t0);
-  if (t1 >= Lkey && t1 != 0ull) append(t1);
-  if (t2 >= Lkey && t2 != 0ull) append(t2);
-  if (t3 >= Lkey && t3 != 0ull) {
-    append(t3);
-    src.for_own([&](float z, int v) {
-      const unsigned long long key = entry_key(z, (uint32_t)v);
-      if (key >= Lkey && key < t3) append(key);
-    });
-  }
+  // Phase C (a second pass, served from cache): gather every entry with
+  // logit >= L into LDS as its 64-bit key (-0 also passes a +0 bound, which
+  // only adds a candidate).
+  src.for_each([&](float z, int v) {
+    if (take_all || z >= Lf) {
+      const unsigned int slot = atomicAdd(&sh.ncand, 1u);
+      if (slot < (unsigned int)kCap) sh.cand[slot] = entry_key(z, (uint32_t)v);
+    }
+  });
   __syncthreads();
   const unsigned int ncand = sh.ncand;
   const bool in_lds = ncand <= (unsigned int)kCap;
@@ -231,40 +228,44 @@ __device__ __forceinline__ TopkRow topk_row(TopkShared &sh, const Src &src, int 
   unsigned long long thr;
   if (in_lds) thr = radix_select(sh, LdsKeys{sh.cand, ncand}, (unsigned)K, 64, 0);
   else thr = radix_select(sh, SrcKeys<Src>{src}, (unsigned)K, 64, 0);
-
-  // Phase E: statistics over kept entries (and the list).  The select may stop
-  // with the low bits of `thr` cleared; that separates the K kept entries from
-  // the other candidates but not from every entry of the row, so the stored
-  // threshold is made exact: the smallest kept key.
-  float zmax = -INFINITY;
+  // The select may stop with the low bits of `thr` cleared; that separates
+  // the K kept entries from the other candidates but not from every entry of
+  // the row, so the threshold is made exact: the smallest kept key.
   unsigned long long kmin = ~0ull;
-  auto visit_max = [&](unsigned long long key) {
-    if (key >= thr) {
-      zmax = fmaxf(zmax, from_orderable((uint32_t)(key >> 32)));
-      kmin = key < kmin ? key : kmin;
-    }
+  auto visit = [&](unsigned long long key) {
+    if (key >= thr) kmin = key < kmin ? key : kmin;
   };
-  if (in_lds) LdsKeys{sh.cand, ncand}.for_each(visit_max);
-  else SrcKeys<Src>{src}.for_each(visit_max);
-  zmax = wave_max_f(zmax);
+  if (in_lds) LdsKeys{sh.cand, ncand}.for_each(visit);
+  else SrcKeys<Src>{src}.for_each(visit);
   kmin = ~wave_max_u64(~kmin);
-  if ((tid % kWave) == 0) {
-    sh.red_f[tid / kWave] = zmax;
-    sh.red_u[tid / kWave] = kmin;
-  }
+  if ((threadIdx.x % kWave) == 0) sh.red_u[threadIdx.x / kWave] = kmin;
+  __syncthreads();
+  kmin = sh.red_u[0];
+  for (int i = 1; i < kTopkThreads / kWave; ++i) kmin = sh.red_u[i] < kmin ? sh.red_u[i] : kmin;
+  __syncthreads();
+  return Selected{kmin, in_lds, ncand};
+}
+
+// Base-2 softmax statistics over the kept entries (keys >= thr) of a key set;
+// writes the kept entries to `list` when given.
+template <class Keys>
+__device__ __forceinline__ TopkRow kept_stats(TopkShared &sh, const Keys &keys, unsigned long long thr, float c,
+                                              int2 *list, int K) {
+  const int tid = threadIdx.x;
+  if (tid == 0) sh.nkept = 0u;
+  float zmax = -INFINITY;
+  keys.for_each([&](unsigned long long key) {
+    if (key >= thr) zmax = fmaxf(zmax, from_orderable((uint32_t)(key >> 32)));
+  });
+  zmax = wave_max_f(zmax);
+  if ((tid % kWave) == 0) sh.red_f[tid / kWave] = zmax;
   __syncthreads();
   zmax = sh.red_f[0];
-  kmin = sh.red_u[0];
-  for (int i = 1; i < kTopkThreads / kWave; ++i) {
-    zmax = fmaxf(zmax, sh.red_f[i]);
-    kmin = sh.red_u[i] < kmin ? sh.red_u[i] : kmin;
-  }
+  for (int i = 1; i < kTopkThreads / kWave; ++i) zmax = fmaxf(zmax, sh.red_f[i]);
   __syncthreads();
-  thr = kmin;
   const float R = (zmax == -INFINITY) ? -INFINITY : ceilf(zmax * c);
-
   float S = 0.0f;
-  auto visit_sum = [&](unsigned long long key) {
+  keys.for_each([&](unsigned long long key) {
     if (key >= thr) {
       const float z = from_orderable((uint32_t)(key >> 32));
       if (z != -INFINITY) S += __builtin_amdgcn_exp2f(fmaf(z, c, -R));
@@ -274,17 +275,28 @@ __device__ __forceinline__ TopkRow topk_row(TopkShared &sh, const Src &src, int 
           list[slot] = make_int2((int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull)), (int)__float_as_uint(z));
       }
     }
-  };
-  if (in_lds) LdsKeys{sh.cand, ncand}.for_each(visit_sum);
-  else SrcKeys<Src>{src}.for_each(visit_sum);
+  });
   S = wave_sum_f(S);
   if ((tid % kWave) == 0) sh.red_f[tid / kWave] = S;
   __syncthreads();
   S = 0.0f;
   for (int i = 0; i < kTopkThreads / kWave; ++i) S += sh.red_f[i];
   __syncthreads();
-  return TopkRow{thr, R, S, in_lds, ncand};
+  return TopkRow{thr, R, S, false, 0u};
 }
+
+// Top-K of a row: exact threshold, statistics over the kept entries, and the
+// kept list when given.
+template <class Src>
+__device__ __forceinline__ TopkRow topk_row(TopkShared &sh, const Src &src, int K, float c, int2 *list) {
+  const Selected sel = select_threshold(sh, src, K);
+  TopkRow r = sel.in_lds ? kept_stats(sh, LdsKeys{sh.cand, sel.ncand}, sel.thr, c, list, K)
+                         : kept_stats(sh, SrcKeys<Src>{src}, sel.thr, c, list, K);
+  r.in_lds = sel.in_lds;
+  r.ncand = sel.ncand;
+  return r;
+}
+
 
 __device__ __forceinline__ uint4 pack_rowinfo(const TopkRow &r) {
   return make_uint4((uint32_t)(r.thr & 0xFFFFFFFFull), (uint32_t)(r.thr >> 32), __float_as_uint(r.R),

@@ -58,8 +58,11 @@ def test_workspace_bytes(L):
 
 def test_launch_names(L):
     import rejection_sampling_verify_17_amd as S
-    # one launch per position 0..gamma, then the pick (the top-k path picks in place)
-    assert S.launch_names(64, 5, 128256, 1, 0) == ["k_step"] * 6 + ["k_pick"]
+    # small inputs: one launch for every row, one to judge, then the pick
+    assert S.launch_names(64, 5, 128256, 1, 0) == ["k_step"] * 2 + ["k_pick"]
+    # large inputs: one launch per position 0..gamma, then the pick
+    assert S.launch_names(1024, 4, 50257, 0, 0) == ["k_step"] * 5 + ["k_pick"]
+    # the top-k path picks in place
     assert S.launch_names(256, 8, 152064, 1, 50) == ["k_topk_step"] * 9
 
 

@@ -50,6 +50,21 @@ def test_parity_small(name, B, seeds):
 FULL = ["c2", "c3", "c4a", "c4b", "c4c"]
 
 
+@pytest.mark.parametrize("sigma", [0.5, 2.0])
+def test_parity_one_position_per_launch(sigma):
+    """Inputs large enough (537 MB of rows) that the library judges one
+    position per launch, with gamma = 8 so sequences finish at every launch."""
+    w = I.make("c4b", B=64, gamma=8, V=131072, draft_sigma=sigma, data_seed=1077, draft_seed=2077)
+    _say(f"case window-1 B={w.B} gamma={w.gamma} V={w.V} sigma={sigma}")
+    import rejection_sampling_verify_17_amd as S
+    assert S.launch_names(w.B, w.gamma, w.V, S.SV_F32, 0) == ["k_step"] * 9 + ["k_pick"]
+    tensors = PT.to_device(w)
+    for seed in (3100, 3101):
+        g = PT.run_gpu(w, seed, tensors=tensors)
+        _check(PT.compare(w, seed, g), f"window-1 sigma {sigma} seed {seed}")
+        _say(f"n histogram {np.bincount(g.n_accepted, minlength=w.gamma + 1).tolist()}")
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_parity_full_size(name):
     """Full workload, benchmark launch geometry, every sequence against the oracle."""
@@ -167,6 +182,19 @@ def _edge_workloads():
     w = I.from_arrays(t, d, np.zeros((2, 2), np.int32), top_k=40)
     w.tokens[:] = I.sample_rows(d.reshape(-1, 20000), 1.0, 40, rng).reshape(2, 2)
     out.append(("topk-overflow", w))
+    # constant rows with top-k: every entry ties, chunks overflow the LDS
+    # candidate buffer, the smallest indices are kept
+    t = np.full((3, 3, 20000), 0.25, np.float32)
+    d = t[:, :2].copy()
+    d[:, :, 5000:5100] = 1.0
+    w = I.from_arrays(t, d, np.zeros((3, 2), np.int32), top_k=10)
+    w.tokens[:] = I.sample_rows(d.reshape(-1, 20000), 1.0, 10, rng).reshape(3, 2)
+    out.append(("topk-constant-rows", w))
+    # p == q with top-k: every draft kept, bonus row selected in chunks
+    t = rng.normal(0, 2, (16, 4, 40000)).astype(np.float32)
+    w = I.from_arrays(t, t[:, :3].copy(), np.zeros((16, 3), np.int32), top_k=20)
+    w.tokens[:] = I.sample_rows(t[:, :3].reshape(-1, 40000), 1.0, 20, rng).reshape(16, 3)
+    out.append(("topk-p-equals-q", w))
     # p == q: everything kept, bonus from row gamma
     t = rng.normal(0, 2, (32, 4, 1000)).astype(np.float32)
     w = I.from_arrays(t, t[:, :3].copy(), np.zeros((32, 3), np.int32))
@@ -184,7 +212,7 @@ def test_edge_cases(name, w):
     for seed in (11, 12):
         g = PT.run_gpu(w, seed)
         _check(PT.compare(w, seed, g), f"edge {name} seed {seed}")
-    if name == "p-equals-q":
+    if name in ("p-equals-q", "topk-p-equals-q"):
         assert np.all(g.n_accepted == w.gamma)
 
 
