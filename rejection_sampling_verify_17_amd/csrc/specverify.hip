@@ -3,6 +3,7 @@
 // include/specverify.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -19,19 +20,35 @@ constexpr int kMaxGamma = 64;           // one wave ballots all positions
 constexpr int kMaxV = 1 << 28;          // byte offsets of a row fit 32 bits
 constexpr int kListMax = 1024;          // top-k lists kept up to this K
 constexpr double kSmallRows = 256e6;    // bytes of all rows below which one launch reads them all
-#ifndef SV_TARGET_TILES
-#define SV_TARGET_TILES 4096
-#endif
-constexpr int kTargetTiles = SV_TARGET_TILES;  // blocks per launch to aim for
+constexpr int kTargetItems = 2048;      // statistics items per launch to aim for
+constexpr int kSlotsPerCU = 8;          // resident k_rows blocks per compute unit
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Compute units of the current device (queried once per device).
+int compute_units() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+  if (dev >= 0) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev >= 0) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 struct Plan {
   bool topk;
   int window;  // positions whose statistics one launch computes (dense path)
-  int nch, nvec, cv, nchw, ngb, cv2, klist;
-  size_t off_part, off_bestpart, off_nseq, off_state, off_rowinfo, off_lists;
+  int nch, nvec, cv, ngb, cs_max, jseq, njb, klist;
+  size_t off_part, off_ztok, off_bestpart, off_scs, off_slist, off_sst, off_tlist, off_scnt, off_tcnt;
+  size_t off_nseq, off_state, off_rowinfo, off_lists;
   size_t total;
 };
 
@@ -53,22 +70,35 @@ Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype
     // reads them all; otherwise one position per launch.
     const double all_rows = 2.0 * B * gamma * (double)V * (dtype == SV_BF16 ? 2 : 4);
     p.window = all_rows <= kSmallRows ? gamma : 1;
-    // about kTargetTiles blocks per launch, each thread keeping at least two
+    // about kTargetItems statistics items per launch, each thread keeping at least two
     // vectors (statistics) or two group blocks (sampling)
     const int max_ch = std::max(1, p.nvec / (2 * kThreads));
     const int rows = B * p.window;
-    p.nch = std::max(1, std::min((kTargetTiles + rows - 1) / rows, max_ch));
+    p.nch = std::max(1, std::min((kTargetItems + rows - 1) / rows, max_ch));
     p.cv = (p.nvec + p.nch - 1) / p.nch;
-    const int max_chw = std::max(1, p.ngb / (2 * kThreads));
-    p.nchw = std::max(1, std::min((kTargetTiles + B - 1) / B, max_chw));
-    p.cv2 = (p.ngb + p.nchw - 1) / p.nchw;
+    // a sampled row is split so that every thread keeps at least one group block
+    p.cs_max = std::max(1, std::min(kMaxSampleChunks, p.ngb / kThreads));
+    // judge blocks of jseq sequences (a multiple of the waves per block), at
+    // most kMaxJudgeBlocks of them
+    const int per = (B + kJudgeWaves * kMaxJudgeBlocks - 1) / (kJudgeWaves * kMaxJudgeBlocks);
+    p.jseq = kJudgeWaves * per;
+    p.njb = (B + p.jseq - 1) / p.jseq;
   }
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
   // Nothing here is read before this call writes it: the workspace needs no
   // initialisation and may serve calls of any shape in turn.
-  p.off_part = take(p.topk ? 0 : (size_t)B * gamma * p.nch * sizeof(float4));
-  p.off_bestpart = take(p.topk ? 0 : (size_t)B * p.nchw * sizeof(unsigned long long));
+  const size_t dense = p.topk ? 0 : 1;
+  const size_t lslots = dense * (size_t)p.njb * p.jseq;
+  p.off_part = take(dense * B * gamma * p.nch * sizeof(float4));
+  p.off_ztok = take(dense * B * gamma * sizeof(float2));
+  p.off_bestpart = take(dense * B * p.cs_max * sizeof(unsigned long long));
+  p.off_scs = take(dense * B * sizeof(int32_t));
+  p.off_slist = take(lslots * sizeof(int2));
+  p.off_sst = take(lslots * sizeof(float4));
+  p.off_tlist = take(lslots * sizeof(int32_t));
+  p.off_scnt = take(dense * p.njb * sizeof(int32_t));
+  p.off_tcnt = take(dense * p.njb * sizeof(int32_t));
   p.off_nseq = take((size_t)B * sizeof(int32_t));
   p.off_state = take((size_t)2 * B * sizeof(int32_t));
   const size_t slots = (size_t)B * (2 * gamma);
@@ -80,8 +110,8 @@ Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype
 
 template <int DT>
 struct Launches {
-  // gamma + 2 launches (dense) or gamma + 1 (top-k): one per position, then
-  // the pick.
+  // Dense: k_rows for the first window, a (k_judge, k_rows) pair per window,
+  // then k_pick.  Top-k: one launch per position and one for the bonus row.
   static sv_status run(const Args &a, const Plan &p, hipStream_t stream, void *const *events, int n_events,
                        int *n_launches) {
     int li = 0;
@@ -95,18 +125,23 @@ struct Launches {
     };
     bool ok = true;
     if (!p.topk) {
-      int launch = 0, p0 = 0;
-      for (int w0 = 0;; ) {
-        const int w1 = std::min(a.gamma, w0 + p.window);
-        const int dw = w1 > w0 ? w1 - w0 : 1;
+      const int slots = kSlotsPerCU * compute_units();
+      auto grid = [&](long long items) { return (unsigned)std::max(1LL, std::min<long long>(slots, items)); };
+      int w1 = std::min(a.gamma, p.window);
+      before();
+      hipLaunchKernelGGL(k_rows<DT>, dim3(grid((long long)a.B * w1 * p.nch)), dim3(kThreads), 0, stream, a, 1, 0,
+                         w1);
+      ok = ok && after();
+      for (int p0 = 0, w0 = w1;; p0 = w0, w0 = w1) {
+        w1 = std::min(a.gamma, w0 + p.window);
         before();
-        const int per_seq = std::max(dw * p.nch, p.nchw);
-        hipLaunchKernelGGL(k_step<DT>, dim3(a.B * per_seq), dim3(kThreads), 0, stream, a, launch, p0, w0, w1);
+        hipLaunchKernelGGL(k_judge<DT>, dim3(p.njb), dim3(kJudgeWaves * kWave), 0, stream, a, p0, w0);
         ok = ok && after();
-        ++launch;
+        before();
+        const long long items = (long long)a.B * std::max((w1 - w0) * p.nch, p.cs_max);
+        hipLaunchKernelGGL(k_rows<DT>, dim3(grid(items)), dim3(kThreads), 0, stream, a, 0, w0, w1);
+        ok = ok && after();
         if (w0 == a.gamma) break;
-        p0 = w0;
-        w0 = w1;
       }
       before();
       const int waves = kThreads / kWave;
@@ -159,15 +194,23 @@ sv_status verify_impl(const void *target, const void *draft, const int32_t *toke
   a.token_probs = token_probs;
   a.accept_ur = accept_ur;
   a.part = (float4 *)(ws + p.off_part);
+  a.ztok = (float2 *)(ws + p.off_ztok);
   a.bestpart = (unsigned long long *)(ws + p.off_bestpart);
-  a.nseq = (int32_t *)(ws + p.off_nseq);
-  a.state = (int32_t *)(ws + p.off_state);
+  a.scs = (int32_t *)(ws + p.off_scs);
+  a.slist = (int2 *)(ws + p.off_slist);
+  a.sst = (float4 *)(ws + p.off_sst);
+  a.tlist = (int32_t *)(ws + p.off_tlist);
+  a.scnt = (int32_t *)(ws + p.off_scnt);
+  a.tcnt = (int32_t *)(ws + p.off_tcnt);
+  a.jseq = p.jseq;
+  a.njb = p.njb;
   a.nch = p.nch;
-  a.nchw = p.nchw;
   a.nvec = p.nvec;
   a.cv = p.cv;
   a.ngb = p.ngb;
-  a.cv2 = p.cv2;
+  a.cs_max = p.cs_max;
+  a.nseq = (int32_t *)(ws + p.off_nseq);
+  a.state = (int32_t *)(ws + p.off_state);
   a.rowinfo = p.topk ? (uint4 *)(ws + p.off_rowinfo) : nullptr;
   a.lists = p.klist ? (int2 *)(ws + p.off_lists) : nullptr;
   a.klist = p.klist;
@@ -221,9 +264,12 @@ const char *sv_launch_name(int32_t B, int32_t gamma, int32_t V, int32_t dtype, i
   const Plan p = make_plan(B, gamma, V, top_k, dtype);
   if (i < 0) return nullptr;
   if (p.topk) return i <= gamma ? "k_topk_step" : nullptr;
-  const int steps = (gamma + p.window - 1) / p.window + 1;  // windows, then the judge-only launch
-  if (i < steps) return "k_step";
-  return i == steps ? "k_pick" : nullptr;
+  // k_rows, then (k_judge, k_rows) per window and once more for the last
+  // judgement, then k_pick
+  const int pairs = (gamma + p.window - 1) / p.window;
+  if (i == 0) return "k_rows";
+  if (i <= 2 * pairs) return (i & 1) ? "k_judge" : "k_rows";
+  return i == 2 * pairs + 1 ? "k_pick" : nullptr;
 }
 
 const char *sv_status_string(sv_status s) {

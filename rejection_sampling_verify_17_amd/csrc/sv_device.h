@@ -34,8 +34,12 @@ __device__ __forceinline__ Philox4 philox(uint32_t c0, uint32_t c1, uint32_t c2,
 #pragma unroll
   for (int round = 0; round < 10; ++round) {
     const uint32_t mA = 0xD2511F53u, mB = 0xCD9E8D57u;
-    const uint32_t hiA = __umulhi(mA, c0), loA = mA * c0;
-    const uint32_t hiB = __umulhi(mB, c2), loB = mB * c2;
+    // one v_mad_u64_u32 gives both halves of each product
+    uint64_t pA, pB, ccA, ccB;
+    asm("v_mad_u64_u32 %0, %1, %2, %3, 0" : "=v"(pA), "=s"(ccA) : "s"(mA), "v"(c0));
+    asm("v_mad_u64_u32 %0, %1, %2, %3, 0" : "=v"(pB), "=s"(ccB) : "s"(mB), "v"(c2));
+    const uint32_t hiA = (uint32_t)(pA >> 32), loA = (uint32_t)pA;
+    const uint32_t hiB = (uint32_t)(pB >> 32), loB = (uint32_t)pB;
     const uint32_t n0 = hiB ^ c1 ^ k0;
     const uint32_t n2 = hiA ^ c3 ^ k1;
     c0 = n0;
@@ -163,11 +167,13 @@ template <int DT> struct Row {
   // Vector iv: z[e] is entry NE*iv + e - s.
   __device__ __forceinline__ void load_vec(int iv, float (&z)[NE]) const { decode<DT>(raw(iv), z); }
 
-  // Entries [NE*g, NE*g + NE) in order (a "group block": NE/4 Philox groups),
-  // assembled from vectors g and g+1 with a funnel shift by s entries.
+  // Entries [NE*g, NE*g + NE) in order (a "group block": NE/4 Philox groups).
+  // When the row starts on a 4-byte boundary (always for fp32, for bf16 when
+  // s is even) one 16-byte load at a 4-byte-aligned offset reads them;
+  // otherwise they are assembled from vectors g and g+1 with a funnel shift.
   __device__ __forceinline__ void load_block(int g, float (&z)[NE]) const {
-    if (s == 0) {
-      decode<DT>(raw(g), z);
+    if (((s * ESZ) & 3) == 0) {
+      decode<DT>(__builtin_amdgcn_raw_buffer_load_b128(rsrc, g * 16 + s * ESZ, 0, 0), z);
       return;
     }
     const u32x4 A = raw(g), B = raw(g + 1);

@@ -1,31 +1,34 @@
 // Verification kernels, dense path (no top-k filter).
 //
 // The rule judges drafts left to right and discards everything after the
-// first rejection, so rows after it need not be read.  Launches walk the
-// positions in windows [w0, w1) (one position each for large batches, all of
-// them at once when the whole input is small and launches would dominate):
+// first rejection, so rows after it need not be read.  Positions are walked
+// in windows [w0, w1): one position each for large batches, all of them at
+// once when the whole input is small and extra launches would dominate.
 //
-//   k_step(first window)  every sequence: partial base-2 softmax statistics
-//                   (R, S) of draft and target rows w0..w1-1, one vocabulary
-//                   chunk per block.
-//   k_step(next windows)  every block of a sequence still alive first judges
-//                   the previous window itself (wave 0: lane l merges row pair
-//                   l's partials, evaluates q(t)/p(t) in registers and draws
-//                   u; a ballot finds the first rejection), then, on its chunk:
-//                     all accepted, window left:  statistics of its row;
-//                     all accepted, none left:    Gumbel-max winner over
-//                                                 target row gamma (bonus);
-//                     rejected at n:              Gumbel-max winner over the
-//                                                 residual max(0, q - p) of row n.
-//                   Memory-bound statistics of live sequences and VALU-bound
-//                   sampling of finished ones share each launch.
+//   k_rows (first)  statistics of rows 0..w1-1 of every sequence: partial
+//                   base-2 softmax statistics (R, S) of each draft and target
+//                   row, one vocabulary chunk per work item, and the two
+//                   logits at the drafted token.
+//   k_judge         one wave per sequence still alive judges the window just
+//                   measured (lane l merges row pair l's partials, evaluates
+//                   q(t)/p(t) in registers and draws u; a ballot finds the
+//                   first rejection), writes the sequence's outputs and puts
+//                   it on one of two compact lists: statistics of the next
+//                   window (all accepted, rows left), or sampling (the
+//                   residual max(0, q - p) of the rejected row, or the bonus
+//                   row gamma when everything was accepted).
+//   k_rows          a grid sized to the chip walks both lists: sampling items
+//                   (Gumbel-max winner over one chunk of a row, VALU-bound)
+//                   first, then statistics items (memory-bound), so the two
+//                   kinds share every compute unit.  The chunk count of a
+//                   sampled row follows the number of rows to sample.
 //   k_pick          one wave per sequence: the best chunk winner is the token.
 //
-// A per-sequence state (double-buffered by launch index parity, so blocks of
-// one launch read what the previous launch wrote) says whether the sequence
-// is alive at the window start.  Blocks never signal each other inside a launch:
-// results cross launch boundaries only (on this GPU an agent-scope fence is a
-// write-back and invalidation of the whole L2, far too dear to pay per block).
+// Blocks never signal each other inside a launch: results cross launch
+// boundaries only (on this GPU an agent-scope fence is a write-back and
+// invalidation of the whole L2, far too dear to pay per block).  The lists are
+// written per judge block (no atomics); k_rows finds an item's entry through a
+// prefix sum of the per-block lengths held in LDS.
 //
 // The rule is that of page "스펙큘러티브 디코딩 — 작은 모델이 먼저 쓰고 큰 모델이
 // 검사한다" (blog.mna-game.duckdns.org post 46), §1, and page "추측 디코딩: 큰 모델을
@@ -37,10 +40,14 @@
 namespace sv {
 
 constexpr int kThreads = 256;
+constexpr int kJudgeWaves = 16;          // sequences judged side by side per judge block
+constexpr int kMaxJudgeBlocks = 1024;    // judge blocks at most (their list lengths sit in LDS)
+constexpr int kBonusRow = 0x10000;       // sampling-list flag: sample the bonus row
+constexpr int kMaxSampleChunks = kWave;  // chunks a sampled row is split into at most (one lane each in k_pick)
 
 // Per-sequence state between launches: w >= 0 means "alive: every position
-// before the last window accepted and the last window's statistics written,
-// up to row w"; anything else means done.
+// before w accepted and the statistics of the window from w written";
+// anything else means done.
 constexpr int kDone = -1;
 constexpr int kInvalid = -2;
 
@@ -56,15 +63,23 @@ struct Args {
   int32_t *n_accepted;     // [B]
   float *token_probs;      // [B][gamma][2] or null
   float *accept_ur;        // [B][gamma][2] or null
-  // workspace
+  // workspace, dense path
   float4 *part;            // [B][gamma][nch] {Rp, Sp, Rq, Sq}
-  unsigned long long *bestpart;  // [B][nchw] chunk winners (0 = none)
-  int32_t *nseq;           // [B] n, or -1 for an invalid sequence
-  int32_t *state;          // [2][B] launch-parity double buffer
+  float2 *ztok;            // [B][gamma] draft and target logit at the drafted token
+  unsigned long long *bestpart;  // [B][cs_max] chunk winners (0 = none)
+  int32_t *scs;            // [B] chunks the sampled row was split into
+  int2 *slist;             // [njb][jseq] sampling list {b, row | kBonusRow}
+  float4 *sst;             // [njb][jseq] statistics of the sampled row pair
+  int32_t *tlist;          // [njb][jseq] statistics list: sequences alive for the next window
+  int32_t *scnt, *tcnt;    // [njb] list lengths per judge block
+  int32_t jseq, njb;       // sequences per judge block, judge blocks
   int32_t nch;             // statistics: vocabulary chunks per row
   int32_t nvec, cv;        // statistics: 16-byte vectors per row (any alignment), per chunk
-  int32_t nchw;            // sampling: vocabulary chunks of the sampled row
-  int32_t ngb, cv2;        // sampling: group blocks per row, per chunk
+  int32_t ngb;             // sampling: group blocks (16 bytes of entries) per row
+  int32_t cs_max;          // sampling: chunks per row at most
+  // both paths
+  int32_t *nseq;           // [B] n, or -1 for an invalid sequence
+  int32_t *state;          // [2][B] (the top-k path alternates halves by launch parity)
   // top-k path
   uint4 *rowinfo;          // [B][2*gamma] {thr lo, thr hi, R bits, S bits}
   int2 *lists;             // [B][2*gamma][K] (index, logit bits) or null
@@ -124,9 +139,8 @@ __device__ __forceinline__ void write_diag(const Args &a, int b, int j, float pt
   }
 }
 
-// Are all drafted tokens of sequence b in [0, V)?  (wave 0)
-__device__ __forceinline__ bool tokens_valid(const Args &a, int b) {
-  const int lane = threadIdx.x;
+// Are all drafted tokens of sequence b in [0, V)?  (one wave)
+__device__ __forceinline__ bool tokens_valid(const Args &a, int b, int lane) {
   bool ok = true;
   for (int j = lane; j < a.gamma; j += kWave) {
     const int t = a.tokens[(size_t)b * a.gamma + j];
@@ -158,18 +172,61 @@ __device__ __forceinline__ Judged judge_one(const Args &a, uint32_t seq, int j, 
 }
 
 // ---------------------------------------------------------------------------
-// Block pieces
+// Work items
 // ---------------------------------------------------------------------------
 
-// Partial statistics of draft row j and target row j over vectors [v0, v1).
+// Rescale (R, S) so that R >= m c (m: the largest logit about to be added).
+__device__ __forceinline__ void raise_ref(float &R, float &S, float m, float c) {
+  const float mc = m * c;
+  if (mc > R) {
+    const float Rn = ceilf(mc);
+    S = (R == -INFINITY) ? 0.0f : scale_pow2(S, R - Rn);
+    R = Rn;
+  }
+}
+
+// Fold vectors [u0, u0 + FU) of one row into (R, S): one maximum and one
+// rescale test, then one fma, exp2 and add per entry.
+template <int FU, int U, int NE>
+__device__ __forceinline__ void fold_vecs(float &R, float &S, const float (&z)[U][NE], int u0, float c) {
+  float m = z[u0][0];
+#pragma unroll
+  for (int u = u0; u < u0 + FU; ++u)
+#pragma unroll
+    for (int e = 0; e < NE; ++e) m = fmaxf(m, z[u][e]);
+  raise_ref(R, S, m, c);
+  if (R != -INFINITY) {
+#pragma unroll
+    for (int u = u0; u < u0 + FU; ++u)
+#pragma unroll
+      for (int e = 0; e < NE; ++e) S += __builtin_amdgcn_exp2f(fmaf(z[u][e], c, -R));
+  }
+}
+
+// Partial statistics of draft row j and target row j over vectors [v0, v1);
+// the chunk whose vectors hold the drafted token also records its two logits
+// (loaded up front by thread 0, so the load overlaps the stream).  Each
+// iteration loads U vectors of each row and folds them 8 entries at a time;
+// entries outside the row or the chunk (only in edge iterations) are masked
+// to -inf first.
 template <int DT>
 __device__ float4 chunk_stats(const Args &a, int b, int j, int v0, int v1) {
   constexpr int NE = Elem<DT>::kVec;
-  constexpr int U = 4;  // vectors in flight per row per thread
+  constexpr int U = 2;                // vectors in flight per row per thread
+  constexpr int FU = NE == 4 ? 2 : 1;  // vectors per fold (8 entries)
   const Row<DT> P(draft_row<DT>(a, b, j), a.V);
   const Row<DT> Q(target_row<DT>(a, b, j), a.V);
   const int V = a.V;
   const float c = a.c;
+  const int t = a.tokens[(size_t)b * a.gamma + j];
+  const bool tv = t >= 0 && t < V;
+  const bool capp = tv && threadIdx.x == 0 && (t + P.s) / NE >= v0 && (t + P.s) / NE < v1;
+  const bool capq = tv && threadIdx.x == 0 && (t + Q.s) / NE >= v0 && (t + Q.s) / NE < v1;
+  const float zpt = capp ? P.load_one(t) : 0.0f;
+  const float zqt = capq ? Q.load_one(t) : 0.0f;
+  // vectors [ilo, ihi) hold no entry outside the row in either row
+  const int ilo = (max(P.s, Q.s) + NE - 1) / NE;
+  const int ihi = min((V + P.s) / NE, (V + Q.s) / NE);
   float Rp = -INFINITY, Sp = 0.0f, Rq = -INFINITY, Sq = 0.0f;
   for (int base = v0 + (int)threadIdx.x; base < v1; base += kThreads * U) {
     float zp[U][NE], zq[U][NE];
@@ -179,200 +236,344 @@ __device__ float4 chunk_stats(const Args &a, int b, int j, int v0, int v1) {
       P.load_vec(iv, zp[u]);  // past the row: zeros or neighbours, masked below
       Q.load_vec(iv, zq[u]);
     }
+    const int top = base + (U - 1) * kThreads;
+    const bool edge = base < ilo || top >= ihi || top >= v1;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int iv = base + u * kThreads;
-      const int ep = iv * NE - P.s, eq = iv * NE - Q.s;  // entry of element 0
-      if (iv >= v1 || ep < 0 || eq < 0 || ep + NE > V || eq + NE > V) {
+    for (int u0 = 0; u0 < U; u0 += FU) {
+      if (edge) {
 #pragma unroll
-        for (int e = 0; e < NE; ++e) {
-          if (iv >= v1 || ep + e < 0 || ep + e >= V) zp[u][e] = -INFINITY;
-          if (iv >= v1 || eq + e < 0 || eq + e >= V) zq[u][e] = -INFINITY;
+        for (int u = u0; u < u0 + FU; ++u) {
+          const int iv = base + u * kThreads;
+          const int e0p = iv * NE - P.s, e0q = iv * NE - Q.s;  // entry of element 0
+#pragma unroll
+          for (int e = 0; e < NE; ++e) {
+            if (iv >= v1 || e0p + e < 0 || e0p + e >= V) zp[u][e] = -INFINITY;
+            if (iv >= v1 || e0q + e < 0 || e0q + e >= V) zq[u][e] = -INFINITY;
+          }
         }
       }
-      accumulate<NE>(Rp, Sp, zp[u], c);
-      accumulate<NE>(Rq, Sq, zq[u], c);
+      fold_vecs<FU>(Rp, Sp, zp, u0, c);
+      fold_vecs<FU>(Rq, Sq, zq, u0, c);
     }
   }
+  float2 *zt = a.ztok + (size_t)b * a.gamma + j;
+  if (capp) zt->x = zpt;
+  if (capq) zt->y = zqt;
   block_merge_stats2<kThreads>(Rp, Sp, Rq, Sq);
   return make_float4(Rp, Sp, Rq, Sq);
 }
 
-// Gumbel-max winner of group blocks [g0, g1) of row `pos`: residual weights
-// q - p (statistics st of that row pair) when `residual`, else the bonus row
-// (weights q).  Residual key r / E2 (the exponential race, monotone in
-// ln r - ln E); bonus key z c - log2 E2 (monotone in ln q - ln E).
-template <int DT>
-__device__ unsigned long long chunk_winner(const Args &a, int b, int pos, bool residual, float4 st, int g0,
-                                           int g1) {
+// Gumbel-max winner over group blocks [g0, g1) of row `pos`: the residual
+// weights max(0, q - p) (statistics st of that row pair) when RESID, else the
+// bonus row (weights q).  Residual key r / E2 (the exponential race, monotone
+// in ln r - ln E), compared inside a thread as r * E2' > r' * E2 so no
+// reciprocal is needed; bonus key z c - log2 E2 (monotone in ln q - ln E).
+// Each thread walks its entries in increasing index, so a strict comparison
+// keeps the smaller index among equal keys; the block reduction does the same
+// on the packed key.  exp2(-inf) = 0 gives masked logits zero weight.
+template <int DT, bool RESID>
+__device__ unsigned long long chunk_winner(const Args &a, int b, int pos, float4 st, int g0, int g1) {
   constexpr int NE = Elem<DT>::kVec;
+  constexpr int U = NE == 4 ? 2 : 1;  // group blocks in flight per thread (8 entries)
   const uint32_t seq = seq_of(a, b);
   const float c = a.c;
-  const int V = a.V;
-  const Row<DT> Q(target_row<DT>(a, b, pos), V);
-  const Row<DT> P(draft_row<DT>(a, b, residual ? pos : 0), V);
+  const Row<DT> Q(target_row<DT>(a, b, pos), a.V);
+  const Row<DT> P(draft_row<DT>(a, b, RESID ? pos : 0), a.V);
   const float invSp = 1.0f / st.y, invSq = 1.0f / st.w;
-  constexpr int U = 2;  // group blocks in flight per thread
-  unsigned long long best = 0ull;
+  const uint32_t lim = (uint32_t)min(a.V, g1 * NE);  // entries at or past lim are masked
+  float bestk = -INFINITY;        // bonus: best key
+  float bestr = 0.0f, bestE = 1.0f;  // residual: best r / E2 as a fraction
+  uint32_t besti = 0xFFFFFFFFu;  // none
   for (int base = g0 + (int)threadIdx.x; base < g1; base += kThreads * U) {
     float zq[U][NE], zp[U][NE];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       Q.load_block(base + u * kThreads, zq[u]);  // past the chunk: masked below
-      if (residual) P.load_block(base + u * kThreads, zp[u]);
+      if (RESID) P.load_block(base + u * kThreads, zp[u]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int gb = base + u * kThreads;
-      if (gb >= g1) continue;
 #pragma unroll
       for (int g = 0; g < NE / 4; ++g) {
-        float w[4];
-        bool any = false;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int idx = gb * NE + g * 4 + e;
-          const float zqe = zq[u][g * 4 + e];
-          if (residual) {
-            const float qv = (zqe == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(fmaf(zqe, c, -st.z)) * invSq;
-            const float zpe = zp[u][g * 4 + e];
-            const float pv = (zpe == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(fmaf(zpe, c, -st.x)) * invSp;
-            w[e] = (idx < V) ? qv - pv : 0.0f;
-            any |= w[e] > 0.0f;
-          } else {
-            w[e] = (idx < V && zqe != -INFINITY) ? zqe : -INFINITY;
-            any |= w[e] != -INFINITY;
-          }
-        }
-        if (!any) continue;
         const uint32_t group = (uint32_t)(gb * (NE / 4) + g);
         const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)pos, group, PURPOSE_SAMPLE);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t idx = group * 4u + (uint32_t)e;
-          unsigned long long k = 0ull;
-          if (residual) {
-            if (w[e] > 0.0f) k = pack_key(w[e] * __builtin_amdgcn_rcpf(exp2_variate(blk.w[e])), idx);
+          const float E2 = exp2_variate(blk.w[e]);
+          bool take;
+          if (RESID) {
+            const float qv = __builtin_amdgcn_exp2f(fmaf(zq[u][g * 4 + e], c, -st.z)) * invSq;
+            const float pv = __builtin_amdgcn_exp2f(fmaf(zp[u][g * 4 + e], c, -st.x)) * invSp;
+            const float r = qv - pv;
+            take = idx < lim && r * bestE > bestr * E2;  // r / E2 > bestr / bestE (and r > 0)
+            bestr = take ? r : bestr;
+            bestE = take ? E2 : bestE;
           } else {
-            if (w[e] != -INFINITY)
-              k = pack_key(fmaf(w[e], c, -__builtin_amdgcn_logf(exp2_variate(blk.w[e]))), idx);
+            const float key = fmaf(zq[u][g * 4 + e], c, -__builtin_amdgcn_logf(E2));
+            take = idx < lim && key > bestk;
+            bestk = take ? key : bestk;
           }
-          best = k > best ? k : best;
+          besti = take ? idx : besti;
         }
       }
     }
   }
+  if (RESID) bestk = bestr / bestE;
+  const unsigned long long best = besti == 0xFFFFFFFFu ? 0ull : pack_key(bestk, besti);
   return block_max_u64<kThreads>(best);
 }
 
 // ---------------------------------------------------------------------------
-// One launch per window of positions (see the top of this file).  A launch
-// judges the previous window [p0, w0) and computes statistics of the rows of
-// its own window [w0, w1) (w0 = w1 = gamma: the last launch, judge only).
-// Blocks per sequence: max(dw x nch, nchw), dw = max(1, w1 - w0).  For
-// statistics block (r, ch) handles chunk ch of row w0 + r; for sampling block
-// ch handles chunk ch of the sampled row; blocks beyond that count exit.
+// Judge: one wave per sequence.  Positions [p0, w0) were measured by the last
+// k_rows; the window [w0, w1) follows (w0 = gamma: none left).
+// mode: -1 nothing to do, 0 statistics of the next window, 1 residual of
+// `row`, 2 bonus row.  Every load is issued up front (one memory round trip):
+// the state, the lane's drafted token, the logits at the token and the
+// partial statistics, spread over the lanes.
 // ---------------------------------------------------------------------------
-template <int DT>
-__global__ __launch_bounds__(kThreads) void k_step(Args a, int launch, int p0, int w0, int w1) {
-  const int dw = w1 > w0 ? w1 - w0 : 1;
-  const int per_seq = max(dw * a.nch, a.nchw);
-  const int b = blockIdx.x / per_seq;
-  const int rem = blockIdx.x - b * per_seq;
-  const int gamma = a.gamma;
-  const bool lead = rem == 0;  // writes the sequence's outputs and state
-  int32_t *state_in = a.state + (size_t)((launch + 1) & 1) * a.B;
-  int32_t *state_out = a.state + (size_t)(launch & 1) * a.B;
+__device__ __forceinline__ int pow2_at_least(int x) {
+  int g = 1;
+  while (g < x) g <<= 1;
+  return g;
+}
 
-  __shared__ int sh_mode;   // 0 statistics, 1 residual, 2 bonus, -1 nothing
-  __shared__ int sh_row;    // row to sample (residual)
-  __shared__ float4 sh_st;
-  if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
-    int mode = 0, row = 0;
-    float4 st = make_float4(0.f, 1.f, 0.f, 1.f);
-    if (w0 == 0) {
-      if (!tokens_valid(a, b)) {
-        mode = -1;
-        if (lead) {
-          write_invalid(a, b, lane);
-          for (int k = lane; k < gamma; k += kWave) write_diag(a, b, k, NAN, NAN, NAN, NAN);
-          if (lane == 0) state_out[b] = kInvalid;
-        }
-      } else if (lead) {
-        for (int k = lane; k < gamma; k += kWave) write_diag(a, b, k, NAN, NAN, NAN, NAN);
-        if (lane == 0) state_out[b] = w1;
-      }
-    } else {
-      const int s = state_in[b];
-      if (s != w0) {
-        mode = -1;  // finished (or invalid) before this window
-        if (lead && lane == 0) state_out[b] = s;
-      } else {
-        // judge positions p0..w0-1: lane l merges the partial statistics of
-        // row pair p0 + l, evaluates its ratio and draws its u; a ballot of
-        // the accept bits finds the first rejection
-        const int nj = w0 - p0;
-        const bool act = lane < nj;
-        const int jpos = p0 + (act ? lane : 0);
-        float Rp = -INFINITY, Sp = 0.0f, Rq = -INFINITY, Sq = 0.0f;
-        bool accept = false;
-        if (act) {
-          const float4 *pp = a.part + ((size_t)b * gamma + jpos) * a.nch;
-          for (int k = 0; k < a.nch; ++k) {
-            const float4 v = pp[k];
-            merge_stats(Rp, Sp, v.x, v.y);
-            merge_stats(Rq, Sq, v.z, v.w);
-          }
-          const int t = a.tokens[(size_t)b * gamma + jpos];
-          const float zp = Row<DT>(draft_row<DT>(a, b, jpos), a.V).load_one(t);
-          const float zq = Row<DT>(target_row<DT>(a, b, jpos), a.V).load_one(t);
-          const Judged jr =
-              judge_one(a, seq_of(a, b), jpos, zp, zq, zp == -INFINITY, zq == -INFINITY, Rp, Sp, Rq, Sq);
-          accept = jr.accept;
-          if (lead) write_diag(a, b, jpos, jr.pt, jr.qt, jr.u, jr.ratio);
-        }
-        const unsigned long long mask = __ballot(act && accept);
-        const int k = (mask == ~0ull) ? kWave : __builtin_ctzll(~mask);  // first clear bit
-        if (lead && act && lane > k) write_diag(a, b, jpos, NAN, NAN, NAN, NAN);  // judged after the rejection
-        if (k < nj) {
-          mode = 1;
-          row = p0 + k;
-          st = make_float4(__shfl(Rp, k, kWave), __shfl(Sp, k, kWave), __shfl(Rq, k, kWave), __shfl(Sq, k, kWave));
-          if (lead) write_judged(a, b, lane, row);
-          if (lead && lane == 0) state_out[b] = kDone;
-        } else if (w0 == gamma) {
-          mode = 2;
-          row = gamma;
-          if (lead) write_judged(a, b, lane, gamma);
-          if (lead && lane == 0) state_out[b] = kDone;
-        } else if (lead && lane == 0) {
-          state_out[b] = w1;
-        }
+template <int DT>
+__device__ void judge_seq(const Args &a, int b, int lane, int p0, int w0, int &mode, int &row, float4 &st) {
+  const int gamma = a.gamma, nch = a.nch;
+  const int nj = w0 - p0;
+  mode = -1;
+  row = 0;
+  st = make_float4(0.f, 1.f, 0.f, 1.f);
+  const int state = p0 == 0 ? 0 : a.state[b];
+  const int tok = lane < gamma ? a.tokens[(size_t)b * gamma + lane] : 0;
+  const bool act = lane < nj;
+  const int jpos = p0 + (act ? lane : 0);
+  const float2 z = a.ztok[(size_t)b * gamma + jpos];
+  // merged statistics of position p0 + lane: gs lanes per position and pass
+  const int gs = nch >= kWave ? kWave : pow2_at_least(nch);
+  const int ppp = kWave / gs;
+  float Rp = -INFINITY, Sp = 0.0f, Rq = -INFINITY, Sq = 0.0f;
+  for (int q0 = 0; q0 < nj; q0 += ppp) {
+    const int myq = q0 + lane / gs;
+    float rp = -INFINITY, sp = 0.0f, rq = -INFINITY, sq = 0.0f;
+    if (myq < nj) {
+      const float4 *pp = a.part + ((size_t)b * gamma + p0 + myq) * nch;
+      for (int ch = lane % gs; ch < nch; ch += gs) {
+        const float4 v = pp[ch];
+        merge_stats(rp, sp, v.x, v.y);
+        merge_stats(rq, sq, v.z, v.w);
       }
     }
-    if (lane == 0) {
-      sh_mode = mode;
-      sh_row = row;
-      sh_st = st;
+    for (int off = gs / 2; off > 0; off >>= 1) {
+      const float rp2 = __shfl_xor(rp, off, kWave), sp2 = __shfl_xor(sp, off, kWave);
+      const float rq2 = __shfl_xor(rq, off, kWave), sq2 = __shfl_xor(sq, off, kWave);
+      merge_stats(rp, sp, rp2, sp2);
+      merge_stats(rq, sq, rq2, sq2);
+    }
+    const bool mine = lane >= q0 && lane < q0 + ppp;
+    const int src = mine ? (lane - q0) * gs : 0;
+    const float xrp = __shfl(rp, src, kWave), xsp = __shfl(sp, src, kWave);
+    const float xrq = __shfl(rq, src, kWave), xsq = __shfl(sq, src, kWave);
+    if (mine) {
+      Rp = xrp;
+      Sp = xsp;
+      Rq = xrq;
+      Sq = xsq;
     }
   }
-  __syncthreads();
-  const int mode = sh_mode;
-  if (mode < 0) return;
-  if (mode == 0) {
-    if (rem >= dw * a.nch) return;
-    const int r = rem / a.nch;
-    const int ch = rem - r * a.nch;
-    const int j = w0 + r;
-    const int v0 = ch * a.cv;
-    const float4 pst = chunk_stats<DT>(a, b, j, v0, min(a.nvec, v0 + a.cv));
-    if (threadIdx.x == 0) a.part[((size_t)b * gamma + j) * a.nch + ch] = pst;
+  if (p0 == 0) {
+    const bool ok = __ballot(lane < gamma && (tok < 0 || tok >= a.V)) == 0ull;
+    for (int k = lane; k < gamma; k += kWave) write_diag(a, b, k, NAN, NAN, NAN, NAN);
+    if (!ok) {
+      write_invalid(a, b, lane);
+      if (lane == 0) a.state[b] = kInvalid;
+      return;
+    }
+  } else if (state != p0) {
+    return;  // finished (or invalid) before this window
+  }
+  // lane l judges position p0 + l; a ballot of the accept bits finds the
+  // first rejection
+  Judged jr{};
+  if (act) jr = judge_one(a, seq_of(a, b), jpos, z.x, z.y, z.x == -INFINITY, z.y == -INFINITY, Rp, Sp, Rq, Sq);
+  const unsigned long long mask = __ballot(act && jr.accept);
+  const int k = (mask == ~0ull) ? kWave : __builtin_ctzll(~mask);  // first clear bit
+  if (act && lane <= k) write_diag(a, b, jpos, jr.pt, jr.qt, jr.u, jr.ratio);
+  int n;
+  if (k < nj) {
+    n = p0 + k;
+    mode = 1;
+    st = make_float4(__shfl(Rp, k, kWave), __shfl(Sp, k, kWave), __shfl(Rq, k, kWave), __shfl(Sq, k, kWave));
+  } else if (w0 == gamma) {
+    n = gamma;
+    mode = 2;
   } else {
-    if (rem >= a.nchw) return;
-    const int g0 = rem * a.cv2;
-    const unsigned long long w = chunk_winner<DT>(a, b, sh_row, mode == 1, sh_st, g0, min(a.ngb, g0 + a.cv2));
-    if (threadIdx.x == 0) a.bestpart[(size_t)b * a.nchw + rem] = w;
+    if (lane == 0) a.state[b] = w0;
+    mode = 0;
+    return;
+  }
+  row = n;
+  // outputs: the accepted prefix, -1 after the sampled slot n (written by k_pick)
+  int32_t *out = a.out_tokens + (size_t)b * (gamma + 1);
+  for (int i = lane; i <= gamma; i += kWave) {
+    if (i < n) out[i] = tok;  // i < n <= gamma, so i == lane
+    else if (i > n) out[i] = -1;
+  }
+  if (lane == 0) {
+    a.n_accepted[b] = n;
+    a.nseq[b] = n;
+    a.state[b] = kDone;
+  }
+}
+
+// Judge block jb holds sequences [jb * jseq, (jb + 1) * jseq) and writes its
+// list entries to the same slots, compacted, with their counts.
+template <int DT>
+__global__ __launch_bounds__(kJudgeWaves *kWave) void k_judge(Args a, int p0, int w0) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int jb = blockIdx.x;
+  const size_t slot0 = (size_t)jb * a.jseq;
+  __shared__ int sh_mode[kJudgeWaves], sh_row[kJudgeWaves], sh_b[kJudgeWaves];
+  __shared__ float4 sh_st[kJudgeWaves];
+  int ns = 0, nt = 0;  // list lengths so far (wave 0)
+  for (int k0 = 0; k0 < a.jseq; k0 += kJudgeWaves) {
+    const long long bl = (long long)slot0 + k0 + wave;
+    int mode = -1, row = 0;
+    float4 st = make_float4(0.f, 1.f, 0.f, 1.f);
+    if (k0 + wave < a.jseq && bl < a.B) judge_seq<DT>(a, (int)bl, lane, p0, w0, mode, row, st);
+    if (lane == 0) {
+      sh_mode[wave] = mode;
+      sh_row[wave] = row;
+      sh_b[wave] = (int)bl;
+      sh_st[wave] = st;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int m = lane < kJudgeWaves ? sh_mode[lane] : -1;
+      const unsigned long long ms = __ballot(m >= 1), mt = __ballot(m == 0);
+      const unsigned long long below = (1ull << lane) - 1ull;
+      if (m >= 1) {
+        const size_t i = slot0 + ns + __popcll(ms & below);
+        a.slist[i] = make_int2(sh_b[lane], sh_row[lane] | (m == 2 ? kBonusRow : 0));
+        a.sst[i] = sh_st[lane];
+      }
+      if (m == 0) a.tlist[slot0 + nt + __popcll(mt & below)] = sh_b[lane];
+      ns += __popcll(ms);
+      nt += __popcll(mt);
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    a.scnt[jb] = ns;
+    a.tcnt[jb] = nt;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row work
+// ---------------------------------------------------------------------------
+
+// Exclusive prefix sums pre[0..n] of cnt[0..n) (n <= 4 * kThreads), in LDS.
+__device__ __forceinline__ void scan_counts(const int32_t *cnt, int n, int *pre) {
+  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+  __shared__ int wsum[kThreads / kWave];
+  int v[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid * 4 + i;
+    v[i] = idx < n ? cnt[idx] : 0;
+    sum += v[i];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += y;
+  }
+  if (lane == kWave - 1) wsum[w] = incl;
+  __syncthreads();
+  int run = incl - sum;
+  for (int i = 0; i < w; ++i) run += wsum[i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid * 4 + i;
+    if (idx < n) pre[idx] = run;
+    run += v[i];
+  }
+  if (tid == kThreads - 1) pre[n] = run;
+  __syncthreads();
+}
+
+// Values every thread of the block holds alike, moved to scalar registers
+// (row addresses and buffer descriptors built from them stay scalar).
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ float uni(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+// Slot of list entry l: the judge block jb with pre[jb] <= l < pre[jb + 1].
+__device__ __forceinline__ size_t list_slot(const Args &a, const int *pre, int l) {
+  int lo = 0, hi = a.njb;  // pre[lo] <= l < pre[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid] <= l) lo = mid;
+    else hi = mid;
+  }
+  return (size_t)uni(lo) * a.jseq + (size_t)uni(l - pre[lo]);
+}
+
+// first: statistics of rows [w0, w1) of every sequence (no lists yet).
+// Otherwise the lists of the judge launch before: sampling items, then
+// statistics items of rows [w0, w1) (none when w0 = w1).
+template <int DT>
+__global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int first, int w0, int w1) {
+  __shared__ int pre_s[kMaxJudgeBlocks + 1], pre_t[kMaxJudgeBlocks + 1];
+  int n_samp = 0, n_stat = a.B;
+  if (!first) {
+    scan_counts(a.scnt, a.njb, pre_s);
+    scan_counts(a.tcnt, a.njb, pre_t);
+    n_samp = uni(pre_s[a.njb]);
+    n_stat = uni(pre_t[a.njb]);
+  }
+  const int per_stat = (w1 - w0) * a.nch;
+  // about two sampling items per block, each thread keeping at least one
+  // group block
+  const int cs = n_samp > 0 ? max(1, min(a.cs_max, (int)((2 * gridDim.x + n_samp - 1) / n_samp))) : 1;
+  const long long s_items = (long long)n_samp * cs;
+  const long long total = s_items + (long long)n_stat * per_stat;
+  for (long long k = blockIdx.x; k < total; k += gridDim.x) {
+    if (k < s_items) {
+      const int l = (int)(k / cs);
+      const int ch = (int)(k - (long long)l * cs);
+      const size_t slot = list_slot(a, pre_s, l);
+      const int2 e = a.slist[slot];
+      const int b = uni(e.x), ey = uni(e.y), row = ey & 0xFFFF;
+      const int gper = (a.ngb + cs - 1) / cs;
+      const int g0 = ch * gper, g1 = min(a.ngb, g0 + gper);
+      unsigned long long w;
+      if (ey & kBonusRow) {
+        w = chunk_winner<DT, false>(a, b, row, make_float4(0.f, 1.f, 0.f, 1.f), g0, g1);
+      } else {
+        const float4 st = a.sst[slot];
+        w = chunk_winner<DT, true>(a, b, row, make_float4(uni(st.x), uni(st.y), uni(st.z), uni(st.w)), g0, g1);
+      }
+      if (threadIdx.x == 0) {
+        a.bestpart[(size_t)b * a.cs_max + ch] = w;
+        if (ch == 0) a.scs[b] = cs;
+      }
+    } else {
+      const long long k2 = k - s_items;
+      const int l = (int)(k2 / per_stat);
+      const int rc = (int)(k2 - (long long)l * per_stat);
+      const int r = rc / a.nch, ch = rc - r * a.nch;
+      const int b = first ? l : uni(a.tlist[list_slot(a, pre_t, l)]);
+      const int j = w0 + r;
+      const int v0 = ch * a.cv;
+      const float4 pst = chunk_stats<DT>(a, b, j, v0, min(a.nvec, v0 + a.cv));
+      if (threadIdx.x == 0) a.part[((size_t)b * a.gamma + j) * a.nch + ch] = pst;
+    }
   }
 }
 
@@ -387,12 +588,10 @@ __global__ __launch_bounds__(kThreads) void k_pick(Args a) {
   const int b = blockIdx.x * (kThreads / kWave) + (int)threadIdx.x / kWave;
   if (b >= a.B) return;
   const int n = a.nseq[b];
+  const int cs = min(a.scs[b], a.cs_max);
+  const unsigned long long k = lane < a.cs_max ? a.bestpart[(size_t)b * a.cs_max + lane] : 0ull;
   if (n < 0 || n > a.gamma) return;
-  unsigned long long best = 0ull;
-  for (int i = lane; i < a.nchw; i += kWave) {
-    const unsigned long long k = a.bestpart[(size_t)b * a.nchw + i];
-    best = k > best ? k : best;
-  }
+  unsigned long long best = lane < cs ? k : 0ull;
   best = wave_max_u64(best);
   if (best == 0ull) {
     const Row<DT> Q(target_row<DT>(a, b, n), a.V);

@@ -429,7 +429,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_step(Args a, int j) {
     const int lane = threadIdx.x;
     int mode = 0;  // 0 select row j, 1 residual at j-1, 2 bonus, -1 nothing
     if (j == 0) {
-      if (!tokens_valid(a, b)) {
+      if (!tokens_valid(a, b, lane)) {
         mode = -1;
         if (lead) {
           write_invalid(a, b, lane);
