@@ -273,7 +273,7 @@ def _find(d, suffix):
 
 
 def _short(name: str) -> str:
-    for k in ("k_topk_step", "k_rows", "k_judge", "k_pick"):
+    for k in ("k_topk_step", "k_rows", "k_judge"):
         if k in name:
             return k
     return name[:60]

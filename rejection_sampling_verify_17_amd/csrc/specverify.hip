@@ -46,8 +46,8 @@ int compute_units() {
 struct Plan {
   bool topk;
   int window;  // positions whose statistics one launch computes (dense path)
-  int nch, nvec, cv, ngb, cs_max, jseq, njb, klist;
-  size_t off_part, off_ztok, off_bestpart, off_scs, off_slist, off_sst, off_tlist, off_scnt, off_tcnt;
+  int nch, nvec, cv, ngb, cs_max, klist;
+  size_t off_part, off_ztok, off_slist, off_sst, off_tlist, off_lcnt, off_icnt, off_pcnt, off_pbest;
   size_t off_nseq, off_state, off_rowinfo, off_lists;
   size_t total;
 };
@@ -78,29 +78,23 @@ Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype
     p.cv = (p.nvec + p.nch - 1) / p.nch;
     // a sampled row is split so that every thread keeps at least one group block
     p.cs_max = std::max(1, std::min(kMaxSampleChunks, p.ngb / kThreads));
-    // judge blocks of jseq sequences (a multiple of the waves per block), at
-    // most kMaxJudgeBlocks of them
-    const int per = (B + kJudgeWaves * kMaxJudgeBlocks - 1) / (kJudgeWaves * kMaxJudgeBlocks);
-    p.jseq = kJudgeWaves * per;
-    p.njb = (B + p.jseq - 1) / p.jseq;
   }
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
   // Nothing here is read before this call writes it: the workspace needs no
   // initialisation and may serve calls of any shape in turn.
   const size_t dense = p.topk ? 0 : 1;
-  const size_t lslots = dense * (size_t)p.njb * p.jseq;
   p.off_part = take(dense * B * gamma * p.nch * sizeof(float4));
   p.off_ztok = take(dense * B * gamma * sizeof(float2));
-  p.off_bestpart = take(dense * B * p.cs_max * sizeof(unsigned long long));
-  p.off_scs = take(dense * B * sizeof(int32_t));
-  p.off_slist = take(lslots * sizeof(int2));
-  p.off_sst = take(lslots * sizeof(float4));
-  p.off_tlist = take(lslots * sizeof(int32_t));
-  p.off_scnt = take(dense * p.njb * sizeof(int32_t));
-  p.off_tcnt = take(dense * p.njb * sizeof(int32_t));
+  p.off_slist = take(dense * 3 * B * sizeof(int2));
+  p.off_sst = take(dense * 3 * B * sizeof(float4));
+  p.off_tlist = take(dense * 3 * B * sizeof(int32_t));
+  p.off_lcnt = take(dense * 3 * 2 * sizeof(int32_t));
+  p.off_icnt = take(dense * B * sizeof(int32_t));
+  p.off_pcnt = take(dense * B * sizeof(int32_t));
+  p.off_pbest = take(dense * B * sizeof(unsigned long long));
   p.off_nseq = take((size_t)B * sizeof(int32_t));
-  p.off_state = take((size_t)2 * B * sizeof(int32_t));
+  p.off_state = take(p.topk ? (size_t)2 * B * sizeof(int32_t) : 0);
   const size_t slots = (size_t)B * (2 * gamma);
   p.off_rowinfo = take(p.topk ? slots * sizeof(uint4) : 0);
   p.off_lists = take(p.klist ? slots * (size_t)p.klist * sizeof(int2) : 0);
@@ -110,8 +104,9 @@ Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype
 
 template <int DT>
 struct Launches {
-  // Dense: k_rows for the first window, a (k_judge, k_rows) pair per window,
-  // then k_pick.  Top-k: one launch per position and one for the bonus row.
+  // Dense: k_rows for the first window, k_judge, then k_rows per further
+  // window and once more to sample.  Top-k: one launch per position and one
+  // for the bonus row.
   static sv_status run(const Args &a, const Plan &p, hipStream_t stream, void *const *events, int n_events,
                        int *n_launches) {
     int li = 0;
@@ -127,26 +122,26 @@ struct Launches {
     if (!p.topk) {
       const int slots = kSlotsPerCU * compute_units();
       auto grid = [&](long long items) { return (unsigned)std::max(1LL, std::min<long long>(slots, items)); };
-      int w1 = std::min(a.gamma, p.window);
+      int w0 = std::min(a.gamma, p.window);
       before();
-      hipLaunchKernelGGL(k_rows<DT>, dim3(grid((long long)a.B * w1 * p.nch)), dim3(kThreads), 0, stream, a, 1, 0,
-                         w1);
+      hipLaunchKernelGGL((k_rows<DT, true>), dim3(grid((long long)a.B * w0 * p.nch)), dim3(kThreads), 0, stream, a, 0, 0,
+                         w0, 0);
       ok = ok && after();
-      for (int p0 = 0, w0 = w1;; p0 = w0, w0 = w1) {
-        w1 = std::min(a.gamma, w0 + p.window);
-        before();
-        hipLaunchKernelGGL(k_judge<DT>, dim3(p.njb), dim3(kJudgeWaves * kWave), 0, stream, a, p0, w0);
-        ok = ok && after();
+      before();
+      hipLaunchKernelGGL(k_judge<DT>, dim3((a.B + kJudgeWaves - 1) / kJudgeWaves), dim3(kJudgeWaves * kWave), 0,
+                         stream, a, w0);
+      ok = ok && after();
+      int target = 0;  // statistics items per sequence over launches 1..i
+      for (int launch = 1;; ++launch) {
+        const int w1 = std::min(a.gamma, w0 + p.window);
+        target += (w1 - w0) * p.nch;
         before();
         const long long items = (long long)a.B * std::max((w1 - w0) * p.nch, p.cs_max);
-        hipLaunchKernelGGL(k_rows<DT>, dim3(grid(items)), dim3(kThreads), 0, stream, a, 0, w0, w1);
+        hipLaunchKernelGGL((k_rows<DT, false>), dim3(grid(items)), dim3(kThreads), 0, stream, a, launch, w0, w1, target);
         ok = ok && after();
         if (w0 == a.gamma) break;
+        w0 = w1;
       }
-      before();
-      const int waves = kThreads / kWave;
-      hipLaunchKernelGGL(k_pick<DT>, dim3((a.B + waves - 1) / waves), dim3(kThreads), 0, stream, a);
-      ok = ok && after();
     } else {
       for (int j = 0; j <= a.gamma; ++j) {
         before();
@@ -195,22 +190,20 @@ sv_status verify_impl(const void *target, const void *draft, const int32_t *toke
   a.accept_ur = accept_ur;
   a.part = (float4 *)(ws + p.off_part);
   a.ztok = (float2 *)(ws + p.off_ztok);
-  a.bestpart = (unsigned long long *)(ws + p.off_bestpart);
-  a.scs = (int32_t *)(ws + p.off_scs);
   a.slist = (int2 *)(ws + p.off_slist);
   a.sst = (float4 *)(ws + p.off_sst);
   a.tlist = (int32_t *)(ws + p.off_tlist);
-  a.scnt = (int32_t *)(ws + p.off_scnt);
-  a.tcnt = (int32_t *)(ws + p.off_tcnt);
-  a.jseq = p.jseq;
-  a.njb = p.njb;
+  a.lcnt = (int32_t *)(ws + p.off_lcnt);
+  a.icnt = (int32_t *)(ws + p.off_icnt);
+  a.pcnt = (int32_t *)(ws + p.off_pcnt);
+  a.pbest = (unsigned long long *)(ws + p.off_pbest);
   a.nch = p.nch;
   a.nvec = p.nvec;
   a.cv = p.cv;
   a.ngb = p.ngb;
   a.cs_max = p.cs_max;
   a.nseq = (int32_t *)(ws + p.off_nseq);
-  a.state = (int32_t *)(ws + p.off_state);
+  a.state = p.topk ? (int32_t *)(ws + p.off_state) : nullptr;
   a.rowinfo = p.topk ? (uint4 *)(ws + p.off_rowinfo) : nullptr;
   a.lists = p.klist ? (int2 *)(ws + p.off_lists) : nullptr;
   a.klist = p.klist;
@@ -264,12 +257,12 @@ const char *sv_launch_name(int32_t B, int32_t gamma, int32_t V, int32_t dtype, i
   const Plan p = make_plan(B, gamma, V, top_k, dtype);
   if (i < 0) return nullptr;
   if (p.topk) return i <= gamma ? "k_topk_step" : nullptr;
-  // k_rows, then (k_judge, k_rows) per window and once more for the last
-  // judgement, then k_pick
-  const int pairs = (gamma + p.window - 1) / p.window;
+  // k_rows (first window), k_judge, then one k_rows per further window and
+  // one to sample after the last
+  const int rows_after = (gamma + p.window - 1) / p.window;
   if (i == 0) return "k_rows";
-  if (i <= 2 * pairs) return (i & 1) ? "k_judge" : "k_rows";
-  return i == 2 * pairs + 1 ? "k_pick" : nullptr;
+  if (i == 1) return "k_judge";
+  return i < 2 + rows_after ? "k_rows" : nullptr;
 }
 
 const char *sv_status_string(sv_status s) {

@@ -5,30 +5,34 @@
 // in windows [w0, w1): one position each for large batches, all of them at
 // once when the whole input is small and extra launches would dominate.
 //
-//   k_rows (first)  statistics of rows 0..w1-1 of every sequence: partial
-//                   base-2 softmax statistics (R, S) of each draft and target
-//                   row, one vocabulary chunk per work item, and the two
-//                   logits at the drafted token.
-//   k_judge         one wave per sequence still alive judges the window just
-//                   measured (lane l merges row pair l's partials, evaluates
-//                   q(t)/p(t) in registers and draws u; a ballot finds the
-//                   first rejection), writes the sequence's outputs and puts
-//                   it on one of two compact lists: statistics of the next
-//                   window (all accepted, rows left), or sampling (the
-//                   residual max(0, q - p) of the rejected row, or the bonus
-//                   row gamma when everything was accepted).
-//   k_rows          a grid sized to the chip walks both lists: sampling items
-//                   (Gumbel-max winner over one chunk of a row, VALU-bound)
-//                   first, then statistics items (memory-bound), so the two
-//                   kinds share every compute unit.  The chunk count of a
-//                   sampled row follows the number of rows to sample.
-//   k_pick          one wave per sequence: the best chunk winner is the token.
+//   k_rows (launch 0)  statistics of rows 0..w1-1 of every sequence: partial
+//                      base-2 softmax statistics (R, S) of each draft and
+//                      target row, one vocabulary chunk per work item, and the
+//                      two logits at the drafted token.
+//   k_judge            one wave per sequence judges that first window (lane l
+//                      merges row pair l's partials, evaluates q(t)/p(t) in
+//                      registers and draws u; a ballot finds the first
+//                      rejection), writes the outputs and puts the sequence
+//                      on a list for the next launch: statistics of the next
+//                      window, or sampling (the residual max(0, q - p) of the
+//                      rejected row, or the bonus row gamma).
+//   k_rows (launch i)  a grid sized to the chip walks the two lists, sampling
+//                      items (Gumbel-max winner over one chunk of a row,
+//                      VALU-bound) first, then statistics items of window i
+//                      (memory-bound), so both kinds share every compute unit.
+//                      The block that finishes a sequence's last statistics
+//                      item judges the window at once and appends the sequence
+//                      to the lists of launch i+1; the block that finishes a
+//                      sampled row's last chunk writes the token.
 //
-// Blocks never signal each other inside a launch: results cross launch
-// boundaries only (on this GPU an agent-scope fence is a write-back and
-// invalidation of the whole L2, far too dear to pay per block).  The lists are
-// written per judge block (no atomics); k_rows finds an item's entry through a
-// prefix sum of the per-block lengths held in LDS.
+// Blocks of one launch talk only through per-sequence counters: an item's
+// results are written with stores that bypass the (per-die, mutually
+// non-coherent) L2 caches, the writer waits until they are performed, then
+// increments the counter atomically; the block whose increment completes the
+// count reads them back with loads that bypass the L2 as well.  No block ever
+// waits for another, and no fence (on this GPU a write-back and invalidation of
+// the whole L2) is needed.  Lists are appended with atomic slot counters and
+// read by the next launch; three sets rotate (read, append, clear).
 //
 // The rule is that of page "스펙큘러티브 디코딩 — 작은 모델이 먼저 쓰고 큰 모델이
 // 검사한다" (blog.mna-game.duckdns.org post 46), §1, and page "추측 디코딩: 큰 모델을
@@ -40,14 +44,12 @@
 namespace sv {
 
 constexpr int kThreads = 256;
-constexpr int kJudgeWaves = 16;          // sequences judged side by side per judge block
-constexpr int kMaxJudgeBlocks = 1024;    // judge blocks at most (their list lengths sit in LDS)
+constexpr int kJudgeWaves = 16;          // sequences judged side by side per k_judge block
 constexpr int kBonusRow = 0x10000;       // sampling-list flag: sample the bonus row
-constexpr int kMaxSampleChunks = kWave;  // chunks a sampled row is split into at most (one lane each in k_pick)
+constexpr int kMaxSampleChunks = 8;      // chunks a sampled row is split into at most (each finishes with atomics on the row's counters)
 
-// Per-sequence state between launches: w >= 0 means "alive: every position
-// before w accepted and the statistics of the window from w written";
-// anything else means done.
+// Per-sequence state of the top-k path between launches: w >= 0 means
+// "alive up to position w"; anything else means done.
 constexpr int kDone = -1;
 constexpr int kInvalid = -2;
 
@@ -66,21 +68,21 @@ struct Args {
   // workspace, dense path
   float4 *part;            // [B][gamma][nch] {Rp, Sp, Rq, Sq}
   float2 *ztok;            // [B][gamma] draft and target logit at the drafted token
-  unsigned long long *bestpart;  // [B][cs_max] chunk winners (0 = none)
-  int32_t *scs;            // [B] chunks the sampled row was split into
-  int2 *slist;             // [njb][jseq] sampling list {b, row | kBonusRow}
-  float4 *sst;             // [njb][jseq] statistics of the sampled row pair
-  int32_t *tlist;          // [njb][jseq] statistics list: sequences alive for the next window
-  int32_t *scnt, *tcnt;    // [njb] list lengths per judge block
-  int32_t jseq, njb;       // sequences per judge block, judge blocks
+  int2 *slist;             // [3][B] sampling lists {b, row | kBonusRow}
+  float4 *sst;             // [3][B] statistics of the sampled row pair
+  int32_t *tlist;          // [3][B] statistics lists: sequences alive for the next window
+  int32_t *lcnt;           // [3][2] list lengths {sampling, statistics}
+  int32_t *icnt;           // [B] statistics items finished (over the windows judged in k_rows)
+  int32_t *pcnt;           // [B] sampling chunks finished
+  unsigned long long *pbest;  // [B] best packed key of the sampled row so far (0 = none)
   int32_t nch;             // statistics: vocabulary chunks per row
   int32_t nvec, cv;        // statistics: 16-byte vectors per row (any alignment), per chunk
   int32_t ngb;             // sampling: group blocks (16 bytes of entries) per row
   int32_t cs_max;          // sampling: chunks per row at most
   // both paths
   int32_t *nseq;           // [B] n, or -1 for an invalid sequence
-  int32_t *state;          // [2][B] (the top-k path alternates halves by launch parity)
   // top-k path
+  int32_t *state;          // [2][B] alternating halves by launch parity
   uint4 *rowinfo;          // [B][2*gamma] {thr lo, thr hi, R bits, S bits}
   int2 *lists;             // [B][2*gamma][K] (index, logit bits) or null
   int32_t klist;           // K when lists are kept, else 0
@@ -172,6 +174,39 @@ __device__ __forceinline__ Judged judge_one(const Args &a, uint32_t seq, int j, 
 }
 
 // ---------------------------------------------------------------------------
+// Communication between blocks of one launch
+// ---------------------------------------------------------------------------
+
+// Agent-scope relaxed atomic loads and stores: they bypass the L2 of the die
+// the block runs on, so a block on another die sees the value.
+__device__ __forceinline__ void store_coherent(float *p, float v) {
+  __hip_atomic_store((uint32_t *)p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float *p) {
+  return __uint_as_float(__hip_atomic_load((uint32_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ void store_coherent(float4 *p, float4 v) {
+  float *f = (float *)p;
+  store_coherent(f, v.x);
+  store_coherent(f + 1, v.y);
+  store_coherent(f + 2, v.z);
+  store_coherent(f + 3, v.w);
+}
+__device__ __forceinline__ float4 load_coherent(const float4 *p) {
+  const float *f = (const float *)p;
+  return make_float4(load_coherent(f), load_coherent(f + 1), load_coherent(f + 2), load_coherent(f + 3));
+}
+
+// Called by one thread after its coherent stores: waits until they are
+// performed, then counts one more finished item.  True for the caller whose
+// item completes `target`; that caller may then read every other item's
+// stores with coherent loads.
+__device__ __forceinline__ bool count_finished(int32_t *ctr, int target) {
+  __builtin_amdgcn_s_waitcnt(0);
+  return __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == target - 1;
+}
+
+// ---------------------------------------------------------------------------
 // Work items
 // ---------------------------------------------------------------------------
 
@@ -256,9 +291,9 @@ __device__ float4 chunk_stats(const Args &a, int b, int j, int v0, int v1) {
       fold_vecs<FU>(Rq, Sq, zq, u0, c);
     }
   }
-  float2 *zt = a.ztok + (size_t)b * a.gamma + j;
-  if (capp) zt->x = zpt;
-  if (capq) zt->y = zqt;
+  float *zt = (float *)(a.ztok + (size_t)b * a.gamma + j);
+  if (capp) store_coherent(zt, zpt);
+  if (capq) store_coherent(zt + 1, zqt);
   block_merge_stats2<kThreads>(Rp, Sp, Rq, Sq);
   return make_float4(Rp, Sp, Rq, Sq);
 }
@@ -326,12 +361,12 @@ __device__ unsigned long long chunk_winner(const Args &a, int b, int pos, float4
 }
 
 // ---------------------------------------------------------------------------
-// Judge: one wave per sequence.  Positions [p0, w0) were measured by the last
-// k_rows; the window [w0, w1) follows (w0 = gamma: none left).
+// Judging a window: one wave per sequence.  Positions [p0, w0) have their
+// statistics; the next window starts at w0 (w0 = gamma: none left).
 // mode: -1 nothing to do, 0 statistics of the next window, 1 residual of
 // `row`, 2 bonus row.  Every load is issued up front (one memory round trip):
-// the state, the lane's drafted token, the logits at the token and the
-// partial statistics, spread over the lanes.
+// the lane's drafted token, the logits at the token and the partial
+// statistics, spread over the lanes.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int pow2_at_least(int x) {
   int g = 1;
@@ -340,17 +375,18 @@ __device__ __forceinline__ int pow2_at_least(int x) {
 }
 
 template <int DT>
-__device__ void judge_seq(const Args &a, int b, int lane, int p0, int w0, int &mode, int &row, float4 &st) {
+__device__ void judge_window(const Args &a, int b, int lane, int p0, int w0, bool first, int &mode, int &row,
+                             float4 &st) {
   const int gamma = a.gamma, nch = a.nch;
   const int nj = w0 - p0;
   mode = -1;
   row = 0;
   st = make_float4(0.f, 1.f, 0.f, 1.f);
-  const int state = p0 == 0 ? 0 : a.state[b];
   const int tok = lane < gamma ? a.tokens[(size_t)b * gamma + lane] : 0;
   const bool act = lane < nj;
   const int jpos = p0 + (act ? lane : 0);
-  const float2 z = a.ztok[(size_t)b * gamma + jpos];
+  const float *zt = (const float *)(a.ztok + (size_t)b * gamma + jpos);
+  const float zp = load_coherent(zt), zq = load_coherent(zt + 1);
   // merged statistics of position p0 + lane: gs lanes per position and pass
   const int gs = nch >= kWave ? kWave : pow2_at_least(nch);
   const int ppp = kWave / gs;
@@ -361,7 +397,7 @@ __device__ void judge_seq(const Args &a, int b, int lane, int p0, int w0, int &m
     if (myq < nj) {
       const float4 *pp = a.part + ((size_t)b * gamma + p0 + myq) * nch;
       for (int ch = lane % gs; ch < nch; ch += gs) {
-        const float4 v = pp[ch];
+        const float4 v = load_coherent(pp + ch);
         merge_stats(rp, sp, v.x, v.y);
         merge_stats(rq, sq, v.z, v.w);
       }
@@ -383,21 +419,18 @@ __device__ void judge_seq(const Args &a, int b, int lane, int p0, int w0, int &m
       Sq = xsq;
     }
   }
-  if (p0 == 0) {
+  if (first) {
     const bool ok = __ballot(lane < gamma && (tok < 0 || tok >= a.V)) == 0ull;
     for (int k = lane; k < gamma; k += kWave) write_diag(a, b, k, NAN, NAN, NAN, NAN);
     if (!ok) {
       write_invalid(a, b, lane);
-      if (lane == 0) a.state[b] = kInvalid;
       return;
     }
-  } else if (state != p0) {
-    return;  // finished (or invalid) before this window
   }
   // lane l judges position p0 + l; a ballot of the accept bits finds the
   // first rejection
   Judged jr{};
-  if (act) jr = judge_one(a, seq_of(a, b), jpos, z.x, z.y, z.x == -INFINITY, z.y == -INFINITY, Rp, Sp, Rq, Sq);
+  if (act) jr = judge_one(a, seq_of(a, b), jpos, zp, zq, zp == -INFINITY, zq == -INFINITY, Rp, Sp, Rq, Sq);
   const unsigned long long mask = __ballot(act && jr.accept);
   const int k = (mask == ~0ull) ? kWave : __builtin_ctzll(~mask);  // first clear bit
   if (act && lane <= k) write_diag(a, b, jpos, jr.pt, jr.qt, jr.u, jr.ratio);
@@ -410,12 +443,12 @@ __device__ void judge_seq(const Args &a, int b, int lane, int p0, int w0, int &m
     n = gamma;
     mode = 2;
   } else {
-    if (lane == 0) a.state[b] = w0;
     mode = 0;
     return;
   }
   row = n;
-  // outputs: the accepted prefix, -1 after the sampled slot n (written by k_pick)
+  // outputs: the accepted prefix, -1 after the sampled slot n (written by
+  // the block that finishes the sampled row)
   int32_t *out = a.out_tokens + (size_t)b * (gamma + 1);
   for (int i = lane; i <= gamma; i += kWave) {
     if (i < n) out[i] = tok;  // i < n <= gamma, so i == lane
@@ -424,87 +457,83 @@ __device__ void judge_seq(const Args &a, int b, int lane, int p0, int w0, int &m
   if (lane == 0) {
     a.n_accepted[b] = n;
     a.nseq[b] = n;
-    a.state[b] = kDone;
   }
 }
 
-// Judge block jb holds sequences [jb * jseq, (jb + 1) * jseq) and writes its
-// list entries to the same slots, compacted, with their counts.
-template <int DT>
-__global__ __launch_bounds__(kJudgeWaves *kWave) void k_judge(Args a, int p0, int w0) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int jb = blockIdx.x;
-  const size_t slot0 = (size_t)jb * a.jseq;
-  __shared__ int sh_mode[kJudgeWaves], sh_row[kJudgeWaves], sh_b[kJudgeWaves];
-  __shared__ float4 sh_st[kJudgeWaves];
-  int ns = 0, nt = 0;  // list lengths so far (wave 0)
-  for (int k0 = 0; k0 < a.jseq; k0 += kJudgeWaves) {
-    const long long bl = (long long)slot0 + k0 + wave;
-    int mode = -1, row = 0;
-    float4 st = make_float4(0.f, 1.f, 0.f, 1.f);
-    if (k0 + wave < a.jseq && bl < a.B) judge_seq<DT>(a, (int)bl, lane, p0, w0, mode, row, st);
-    if (lane == 0) {
-      sh_mode[wave] = mode;
-      sh_row[wave] = row;
-      sh_b[wave] = (int)bl;
-      sh_st[wave] = st;
+// List set of launch i (three rotate: read by launch i, appended by launch
+// i - 1, cleared by launch i - 2).
+__device__ __forceinline__ int list_set(int launch) { return launch % 3; }
+
+// Append sequence b to the lists of list set li (one thread).
+__device__ __forceinline__ void append(const Args &a, int li, int mode, int b, int row, float4 st) {
+  int32_t *cnt = a.lcnt + 2 * li;
+  // every sequence is appended at most once per set, so slot < B; the test
+  // only keeps a broken invariant from writing out of bounds
+  if (mode >= 1) {
+    const int slot = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (slot < a.B) {
+      a.slist[(size_t)li * a.B + slot] = make_int2(b, row | (mode == 2 ? kBonusRow : 0));
+      a.sst[(size_t)li * a.B + slot] = st;
     }
-    __syncthreads();
-    if (wave == 0) {
-      const int m = lane < kJudgeWaves ? sh_mode[lane] : -1;
-      const unsigned long long ms = __ballot(m >= 1), mt = __ballot(m == 0);
-      const unsigned long long below = (1ull << lane) - 1ull;
-      if (m >= 1) {
-        const size_t i = slot0 + ns + __popcll(ms & below);
-        a.slist[i] = make_int2(sh_b[lane], sh_row[lane] | (m == 2 ? kBonusRow : 0));
-        a.sst[i] = sh_st[lane];
-      }
-      if (m == 0) a.tlist[slot0 + nt + __popcll(mt & below)] = sh_b[lane];
-      ns += __popcll(ms);
-      nt += __popcll(mt);
-    }
-    __syncthreads();
+  } else if (mode == 0) {
+    const int slot = __hip_atomic_fetch_add(cnt + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (slot < a.B) a.tlist[(size_t)li * a.B + slot] = b;
   }
-  if (threadIdx.x == 0) {
-    a.scnt[jb] = ns;
-    a.tcnt[jb] = nt;
+}
+
+// First judgement (window [0, w0) of every sequence, measured by launch 0):
+// one wave per sequence.  Also clears the per-sequence counters of the
+// launches to come and the list set launch 1 appends to.  A block reserves
+// its list slots with one atomic per list.
+template <int DT>
+__global__ __launch_bounds__(kJudgeWaves *kWave) void k_judge(Args a, int w0) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int b = blockIdx.x * kJudgeWaves + wave;
+  __shared__ int sh_mode[kJudgeWaves], sh_row[kJudgeWaves];
+  __shared__ float4 sh_st[kJudgeWaves];
+  if (blockIdx.x == 0 && threadIdx.x < 2) a.lcnt[2 * list_set(2) + threadIdx.x] = 0;
+  int mode = -1, row = 0;
+  float4 st = make_float4(0.f, 1.f, 0.f, 1.f);
+  if (b < a.B) {
+    if (lane == 0) {
+      a.icnt[b] = 0;
+      a.pcnt[b] = 0;
+      a.pbest[b] = 0ull;
+    }
+    judge_window<DT>(a, b, lane, 0, w0, true, mode, row, st);
+  }
+  if (lane == 0) {
+    sh_mode[wave] = mode;
+    sh_row[wave] = row;
+    sh_st[wave] = st;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int m = lane < kJudgeWaves ? sh_mode[lane] : -1;
+    const unsigned long long ms = __ballot(m >= 1), mt = __ballot(m == 0);
+    const unsigned long long below = (1ull << lane) - 1ull;
+    const int li = list_set(1);
+    int32_t *cnt = a.lcnt + 2 * li;
+    int bs = 0, bt = 0;
+    if (lane == 0) {
+      if (ms) bs = __hip_atomic_fetch_add(cnt, __popcll(ms), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (mt) bt = __hip_atomic_fetch_add(cnt + 1, __popcll(mt), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    bs = __shfl(bs, 0, kWave);
+    bt = __shfl(bt, 0, kWave);
+    const int bl = blockIdx.x * kJudgeWaves + lane;
+    if (m >= 1) {
+      const int slot = bs + __popcll(ms & below);
+      a.slist[(size_t)li * a.B + slot] = make_int2(bl, sh_row[lane] | (m == 2 ? kBonusRow : 0));
+      a.sst[(size_t)li * a.B + slot] = sh_st[lane];
+    }
+    if (m == 0) a.tlist[(size_t)li * a.B + bt + __popcll(mt & below)] = bl;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Row work
 // ---------------------------------------------------------------------------
-
-// Exclusive prefix sums pre[0..n] of cnt[0..n) (n <= 4 * kThreads), in LDS.
-__device__ __forceinline__ void scan_counts(const int32_t *cnt, int n, int *pre) {
-  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
-  __shared__ int wsum[kThreads / kWave];
-  int v[4], sum = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = tid * 4 + i;
-    v[i] = idx < n ? cnt[idx] : 0;
-    sum += v[i];
-  }
-  int incl = sum;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int y = __shfl_up(incl, d, kWave);
-    if (lane >= d) incl += y;
-  }
-  if (lane == kWave - 1) wsum[w] = incl;
-  __syncthreads();
-  int run = incl - sum;
-  for (int i = 0; i < w; ++i) run += wsum[i];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = tid * 4 + i;
-    if (idx < n) pre[idx] = run;
-    run += v[i];
-  }
-  if (tid == kThreads - 1) pre[n] = run;
-  __syncthreads();
-}
 
 // Values every thread of the block holds alike, moved to scalar registers
 // (row addresses and buffer descriptors built from them stay scalar).
@@ -513,100 +542,126 @@ __device__ __forceinline__ float uni(float x) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
 }
 
-// Slot of list entry l: the judge block jb with pre[jb] <= l < pre[jb + 1].
-__device__ __forceinline__ size_t list_slot(const Args &a, const int *pre, int l) {
-  int lo = 0, hi = a.njb;  // pre[lo] <= l < pre[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (pre[mid] <= l) lo = mid;
-    else hi = mid;
-  }
-  return (size_t)uni(lo) * a.jseq + (size_t)uni(l - pre[lo]);
-}
-
-// first: statistics of rows [w0, w1) of every sequence (no lists yet).
-// Otherwise the lists of the judge launch before: sampling items, then
-// statistics items of rows [w0, w1) (none when w0 = w1).
-template <int DT>
-__global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int first, int w0, int w1) {
-  __shared__ int pre_s[kMaxJudgeBlocks + 1], pre_t[kMaxJudgeBlocks + 1];
+// Launch 0: statistics of rows [w0, w1) of every sequence (judged by
+// k_judge).  Launch i >= 1: the lists of set i: sampling items, then
+// statistics items of rows [w0, w1) (none when w0 = w1).  A block takes its
+// items in rounds of up to kQueue; each item's result goes out at once
+// (partial statistics by coherent store, chunk winner kept in LDS), and at the
+// end of a round the block finishes all its items together: winners folded
+// into the row's best key, per-sequence counters advanced, and for every
+// sequence whose window or sampled row it completed, the judgement (window)
+// or the token (row).  `target` is the number of statistics items of a
+// sequence over launches 1..i.
+template <int DT, bool FIRST>
+__global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int launch, int w0, int w1, int target) {
+  constexpr int kQueue = 64;
+  __shared__ int sh_nq;
+  __shared__ int q_b[kQueue], q_row[kQueue];  // row >= 0: sampled row; -1: statistics item
+  __shared__ int q_fin[kQueue];               // 1: finished the sequence's window or row
+  __shared__ unsigned long long q_w[kQueue];  // chunk winner, then the row's best key
+  const int li = list_set(launch);
   int n_samp = 0, n_stat = a.B;
-  if (!first) {
-    scan_counts(a.scnt, a.njb, pre_s);
-    scan_counts(a.tcnt, a.njb, pre_t);
-    n_samp = uni(pre_s[a.njb]);
-    n_stat = uni(pre_t[a.njb]);
+  if (!FIRST) {
+    n_samp = min(max(uni(a.lcnt[2 * li]), 0), a.B);
+    n_stat = min(max(uni(a.lcnt[2 * li + 1]), 0), a.B);
   }
+  if (blockIdx.x == 0 && threadIdx.x < 2) a.lcnt[2 * list_set(launch + (FIRST ? 1 : 2)) + threadIdx.x] = 0;
   const int per_stat = (w1 - w0) * a.nch;
   // about two sampling items per block, each thread keeping at least one
   // group block
   const int cs = n_samp > 0 ? max(1, min(a.cs_max, (int)((2 * gridDim.x + n_samp - 1) / n_samp))) : 1;
   const long long s_items = (long long)n_samp * cs;
   const long long total = s_items + (long long)n_stat * per_stat;
-  for (long long k = blockIdx.x; k < total; k += gridDim.x) {
-    if (k < s_items) {
-      const int l = (int)(k / cs);
-      const int ch = (int)(k - (long long)l * cs);
-      const size_t slot = list_slot(a, pre_s, l);
-      const int2 e = a.slist[slot];
-      const int b = uni(e.x), ey = uni(e.y), row = ey & 0xFFFF;
-      const int gper = (a.ngb + cs - 1) / cs;
-      const int g0 = ch * gper, g1 = min(a.ngb, g0 + gper);
-      unsigned long long w;
-      if (ey & kBonusRow) {
-        w = chunk_winner<DT, false>(a, b, row, make_float4(0.f, 1.f, 0.f, 1.f), g0, g1);
+  const long long round = (long long)kQueue * gridDim.x;
+  if (threadIdx.x == 0) sh_nq = 0;
+  for (long long k0 = blockIdx.x; k0 < total; k0 += round) {
+    const long long kend = min(total, k0 + round);
+    for (long long k = k0; k < kend; k += gridDim.x) {
+      if (!FIRST && k < s_items) {
+        const int l = (int)(k / cs);
+        const int ch = (int)(k - (long long)l * cs);
+        const int2 e = a.slist[(size_t)li * a.B + l];
+        const int b = uni(e.x), ey = uni(e.y), row = ey & 0xFFFF;
+        if ((unsigned)b >= (unsigned)a.B || row > a.gamma) continue;  // never taken: entries come from append()
+        const int gper = (a.ngb + cs - 1) / cs;
+        const int g0 = ch * gper, g1 = min(a.ngb, g0 + gper);
+        unsigned long long w;
+        if (ey & kBonusRow) {
+          w = chunk_winner<DT, false>(a, b, row, make_float4(0.f, 1.f, 0.f, 1.f), g0, g1);
+        } else {
+          const float4 st = a.sst[(size_t)li * a.B + l];
+          w = chunk_winner<DT, true>(a, b, row, make_float4(uni(st.x), uni(st.y), uni(st.z), uni(st.w)), g0, g1);
+        }
+        if (threadIdx.x == 0) {
+          const int q = sh_nq++;
+          q_b[q] = b;
+          q_row[q] = row;
+          q_w[q] = w;
+        }
       } else {
-        const float4 st = a.sst[slot];
-        w = chunk_winner<DT, true>(a, b, row, make_float4(uni(st.x), uni(st.y), uni(st.z), uni(st.w)), g0, g1);
+        const long long k2 = k - s_items;
+        const int l = (int)(k2 / per_stat);
+        const int rc = (int)(k2 - (long long)l * per_stat);
+        const int r = rc / a.nch, ch = rc - r * a.nch;
+        const int b = FIRST ? l : uni(a.tlist[(size_t)li * a.B + l]);
+        if ((unsigned)b >= (unsigned)a.B) continue;  // never taken: entries come from append()
+        const int j = w0 + r;
+        const int v0 = ch * a.cv;
+        const float4 pst = chunk_stats<DT>(a, b, j, v0, min(a.nvec, v0 + a.cv));
+        if (threadIdx.x == 0) {
+          store_coherent(a.part + ((size_t)b * a.gamma + j) * a.nch + ch, pst);
+          if (!FIRST) {
+            const int q = sh_nq++;
+            q_b[q] = b;
+            q_row[q] = -1;
+          }
+        }
       }
-      if (threadIdx.x == 0) {
-        a.bestpart[(size_t)b * a.cs_max + ch] = w;
-        if (ch == 0) a.scs[b] = cs;
+    }
+    if (FIRST) continue;
+    // finish the round's items, one thread each
+    __syncthreads();
+    const int nq = sh_nq;
+    const int t = threadIdx.x;
+    if (t < nq && q_row[t] >= 0)
+      __hip_atomic_fetch_max(a.pbest + q_b[t], q_w[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);  // every wave: its coherent stores and maxima are performed
+    __syncthreads();
+    if (t < nq) {
+      const int b = q_b[t];
+      const bool samp = q_row[t] >= 0;
+      const int old = __hip_atomic_fetch_add(samp ? a.pcnt + b : a.icnt + b, 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      const bool fin = old == (samp ? cs : target) - 1;
+      q_fin[t] = fin;
+      if (fin && samp) {
+        const unsigned long long best =
+            __hip_atomic_fetch_max(a.pbest + b, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        q_w[t] = best;
+        if (best != 0ull) a.out_tokens[(size_t)b * (a.gamma + 1) + q_row[t]] = (int32_t)packed_index(best);
       }
-    } else {
-      const long long k2 = k - s_items;
-      const int l = (int)(k2 / per_stat);
-      const int rc = (int)(k2 - (long long)l * per_stat);
-      const int r = rc / a.nch, ch = rc - r * a.nch;
-      const int b = first ? l : uni(a.tlist[list_slot(a, pre_t, l)]);
-      const int j = w0 + r;
-      const int v0 = ch * a.cv;
-      const float4 pst = chunk_stats<DT>(a, b, j, v0, min(a.nvec, v0 + a.cv));
-      if (threadIdx.x == 0) a.part[((size_t)b * a.gamma + j) * a.nch + ch] = pst;
     }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Pick: one wave per sequence.  The largest chunk winner is the token; if the
-// residual was empty (reachable only through rounding), q_n is sampled instead
-// by the same wave.
-// ---------------------------------------------------------------------------
-template <int DT>
-__global__ __launch_bounds__(kThreads) void k_pick(Args a) {
-  const int lane = threadIdx.x % kWave;
-  const int b = blockIdx.x * (kThreads / kWave) + (int)threadIdx.x / kWave;
-  if (b >= a.B) return;
-  const int n = a.nseq[b];
-  const int cs = min(a.scs[b], a.cs_max);
-  const unsigned long long k = lane < a.cs_max ? a.bestpart[(size_t)b * a.cs_max + lane] : 0ull;
-  if (n < 0 || n > a.gamma) return;
-  unsigned long long best = lane < cs ? k : 0ull;
-  best = wave_max_u64(best);
-  if (best == 0ull) {
-    const Row<DT> Q(target_row<DT>(a, b, n), a.V);
-    const uint32_t seq = seq_of(a, b);
-    for (int v = lane; v < a.V; v += kWave) {
-      const float z = Q.load_one(v);
-      if (z == -INFINITY) continue;
-      const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)n, (uint32_t)v >> 2, PURPOSE_SAMPLE);
-      const float E = exp2_variate(word_of(blk, (uint32_t)v & 3u));
-      const unsigned long long k = pack_key(fmaf(z, a.c, -__builtin_amdgcn_logf(E)), (uint32_t)v);
-      best = k > best ? k : best;
+    __syncthreads();
+    // judgements of completed windows, one wave each
+    for (int q = threadIdx.x / kWave; q < nq; q += kThreads / kWave) {
+      if (!q_fin[q] || q_row[q] >= 0) continue;
+      const int b = q_b[q];
+      int mode, row;
+      float4 st;
+      judge_window<DT>(a, b, threadIdx.x % kWave, w0, w1, false, mode, row, st);
+      if (threadIdx.x % kWave == 0) append(a, list_set(launch + 1), mode, b, row, st);
     }
-    best = wave_max_u64(best);
+    // an empty residual (reachable only through rounding): sample q_row
+    for (int q = 0; q < nq; ++q) {
+      if (!q_fin[q] || q_row[q] < 0 || q_w[q] != 0ull) continue;
+      const int b = uni(q_b[q]), row = uni(q_row[q]);
+      const unsigned long long best = chunk_winner<DT, false>(a, b, row, make_float4(0.f, 1.f, 0.f, 1.f), 0, a.ngb);
+      if (threadIdx.x == 0) a.out_tokens[(size_t)b * (a.gamma + 1) + row] = (int32_t)packed_index(best);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) sh_nq = 0;
+    __syncthreads();
   }
-  if (lane == 0) a.out_tokens[(size_t)b * (a.gamma + 1) + n] = (int32_t)packed_index(best);
 }
 
 }  // namespace sv
