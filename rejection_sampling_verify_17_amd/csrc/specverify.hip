@@ -94,7 +94,7 @@ Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype
   p.off_pcnt = take(dense * B * sizeof(int32_t));
   p.off_pbest = take(dense * B * sizeof(unsigned long long));
   p.off_nseq = take((size_t)B * sizeof(int32_t));
-  p.off_state = take(p.topk ? (size_t)2 * B * sizeof(int32_t) : 0);
+  p.off_state = take(p.topk ? 2 * (size_t)B * sizeof(int32_t) : 0);
   const size_t slots = (size_t)B * (2 * gamma);
   p.off_rowinfo = take(p.topk ? slots * sizeof(uint4) : 0);
   p.off_lists = take(p.klist ? slots * (size_t)p.klist * sizeof(int2) : 0);
@@ -105,8 +105,8 @@ Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype
 template <int DT>
 struct Launches {
   // Dense: k_rows for the first window, k_judge, then k_rows per further
-  // window and once more to sample.  Top-k: one launch per position and one
-  // for the bonus row.
+  // window and once more to sample.  Top-k: position 0, the other positions,
+  // then the judgement and draw.
   static sv_status run(const Args &a, const Plan &p, hipStream_t stream, void *const *events, int n_events,
                        int *n_launches) {
     int li = 0;
@@ -143,10 +143,22 @@ struct Launches {
         w0 = w1;
       }
     } else {
-      for (int j = 0; j <= a.gamma; ++j) {
+      // windows [0, 1), [1, 2), [2, 4), [4, 8), ...: with low acceptance few
+      // sequences reach the wide windows, and a launch over few rows costs
+      // about the same as one over many (one block per row)
+      const int G = a.gamma;
+      int launch = 0, p0 = 0, w0 = 0, size = 1;
+      while (true) {
+        const int w1 = std::min(G, w0 + size);
+        const int per_seq = w1 > w0 ? 2 * (w1 - w0) : 1;
         before();
-        hipLaunchKernelGGL(k_topk_step<DT>, dim3(a.B * 2), dim3(kTopkThreads), 0, stream, a, j);
+        hipLaunchKernelGGL(k_topk_step<DT>, dim3(a.B * per_seq), dim3(kTopkThreads), 0, stream, a, launch++, p0, w0,
+                           w1);
         ok = ok && after();
+        if (w0 == G) break;
+        p0 = w0;
+        w0 = w1;
+        if (p0 > 0) size *= 2;
       }
     }
     if (n_launches) *n_launches = li;
@@ -256,7 +268,15 @@ const char *sv_launch_name(int32_t B, int32_t gamma, int32_t V, int32_t dtype, i
   if (!shape_ok(B, gamma, V, dtype)) return nullptr;
   const Plan p = make_plan(B, gamma, V, top_k, dtype);
   if (i < 0) return nullptr;
-  if (p.topk) return i <= gamma ? "k_topk_step" : nullptr;
+  if (p.topk) {
+    int launches = 1;  // windows [0,1), [1,2), [2,4), ... then the judgement
+    for (int w0 = 0, size = 1; w0 < gamma; ++launches) {
+      const int w1 = std::min(gamma, w0 + size);
+      if (w0 > 0) size *= 2;
+      w0 = w1;
+    }
+    return i < launches ? "k_topk_step" : nullptr;
+  }
   // k_rows (first window), k_judge, then one k_rows per further window and
   // one to sample after the last
   const int rows_after = (gamma + p.window - 1) / p.window;

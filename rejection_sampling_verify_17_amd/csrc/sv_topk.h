@@ -35,7 +35,7 @@
 
 namespace sv {
 
-constexpr int kTopkThreads = 512;
+constexpr int kTopkThreads = 1024;
 constexpr int kCap = 2048;  // candidate entries held in LDS
 
 struct TopkShared {
@@ -64,13 +64,14 @@ __device__ __forceinline__ unsigned long long entry_key(float z, uint32_t v) {
 // so among the keys `src` enumerates (when unique) "key >= result" still selects
 // exactly the K largest.  Keys outside that set may also pass the cleared
 // threshold, so callers that test other keys need the exact K-th largest.
-template <class Src>
-__device__ __forceinline__ unsigned long long radix_select(TopkShared &sh, const Src &src, unsigned int K, int hi, int lo) {
+// NT threads; Sh provides hist[256], sel_prefix, sel_k, sel_done in LDS.
+template <int NT, class Sh, class Src>
+__device__ __forceinline__ unsigned long long radix_select(Sh &sh, const Src &src, unsigned int K, int hi, int lo) {
   const int tid = threadIdx.x;
   unsigned long long prefix = 0ull, mask = 0ull;
   unsigned int k = K;
   for (int shift = hi - 8; shift >= lo; shift -= 8) {
-    for (int i = tid; i < 256; i += kTopkThreads) sh.hist[i] = 0u;
+    for (int i = tid; i < 256; i += NT) sh.hist[i] = 0u;
     __syncthreads();
     src.for_each([&](unsigned long long key) {
       if ((key & mask) == prefix) atomicAdd(&sh.hist[(unsigned int)(key >> shift) & 255u], 1u);
@@ -115,19 +116,18 @@ __device__ __forceinline__ unsigned long long radix_select(TopkShared &sh, const
   return prefix;
 }
 
-struct LdsKeys {
+template <int NT> struct LdsKeys {
   const unsigned long long *keys;
   unsigned int n;
   template <class F> __device__ __forceinline__ void for_each(F f) const {
-    for (unsigned int i = threadIdx.x; i < n; i += kTopkThreads) f(keys[i]);
+    for (unsigned int i = threadIdx.x; i < n; i += NT) f(keys[i]);
   }
 };
 
-struct LdsMax32 {  // per-thread maxima as 32-bit keys in the high word
+template <int NT> struct LdsMax32 {  // per-thread maxima as 32-bit keys in the high word
   const unsigned int *m;
   template <class F> __device__ __forceinline__ void for_each(F f) const {
-    for (unsigned int i = threadIdx.x; i < (unsigned int)kTopkThreads; i += kTopkThreads)
-      f((unsigned long long)m[i] << 32);
+    for (unsigned int i = threadIdx.x; i < (unsigned int)NT; i += NT) f((unsigned long long)m[i] << 32);
   }
 };
 
@@ -135,7 +135,7 @@ struct LdsMax32 {  // per-thread maxima as 32-bit keys in the high word
 // entry of the row (any order), kU 16-byte loads in flight per thread.
 template <int DT> struct StreamRow {
   static constexpr int NE = Elem<DT>::kVec;
-  static constexpr int kU = 8;
+  static constexpr int kU = 4;
   const Row<DT> &row;
   int e0, e1;  // entries [e0, e1) of the row
   __device__ __forceinline__ StreamRow(const Row<DT> &r, int V) : row(r), e0(0), e1(V) {}
@@ -207,7 +207,7 @@ __device__ __forceinline__ Selected select_threshold(TopkShared &sh, const Src &
   // Phase B: lower bound L = K-th largest per-thread maximum: K threads own an
   // entry >= L each, so the K-th largest logit of the row is >= L.
   unsigned int L = 0u;
-  if (K <= kTopkThreads) L = (unsigned int)(radix_select(sh, LdsMax32{sh.tmax}, (unsigned)K, 64, 32) >> 32);
+  if (K <= kTopkThreads) L = (unsigned int)(radix_select<kTopkThreads>(sh, LdsMax32<kTopkThreads>{sh.tmax}, (unsigned)K, 64, 32) >> 32);
   const bool take_all = L == 0u;
   const float Lf = take_all ? -INFINITY : from_orderable(L);
 
@@ -226,8 +226,8 @@ __device__ __forceinline__ Selected select_threshold(TopkShared &sh, const Src &
 
   // Phase D: threshold among the candidates.
   unsigned long long thr;
-  if (in_lds) thr = radix_select(sh, LdsKeys{sh.cand, ncand}, (unsigned)K, 64, 0);
-  else thr = radix_select(sh, SrcKeys<Src>{src}, (unsigned)K, 64, 0);
+  if (in_lds) thr = radix_select<kTopkThreads>(sh, LdsKeys<kTopkThreads>{sh.cand, ncand}, (unsigned)K, 64, 0);
+  else thr = radix_select<kTopkThreads>(sh, SrcKeys<Src>{src}, (unsigned)K, 64, 0);
   // The select may stop with the low bits of `thr` cleared; that separates
   // the K kept entries from the other candidates but not from every entry of
   // the row, so the threshold is made exact: the smallest kept key.
@@ -235,7 +235,7 @@ __device__ __forceinline__ Selected select_threshold(TopkShared &sh, const Src &
   auto visit = [&](unsigned long long key) {
     if (key >= thr) kmin = key < kmin ? key : kmin;
   };
-  if (in_lds) LdsKeys{sh.cand, ncand}.for_each(visit);
+  if (in_lds) LdsKeys<kTopkThreads>{sh.cand, ncand}.for_each(visit);
   else SrcKeys<Src>{src}.for_each(visit);
   kmin = ~wave_max_u64(~kmin);
   if ((threadIdx.x % kWave) == 0) sh.red_u[threadIdx.x / kWave] = kmin;
@@ -290,7 +290,7 @@ __device__ __forceinline__ TopkRow kept_stats(TopkShared &sh, const Keys &keys, 
 template <class Src>
 __device__ __forceinline__ TopkRow topk_row(TopkShared &sh, const Src &src, int K, float c, int2 *list) {
   const Selected sel = select_threshold(sh, src, K);
-  TopkRow r = sel.in_lds ? kept_stats(sh, LdsKeys{sh.cand, sel.ncand}, sel.thr, c, list, K)
+  TopkRow r = sel.in_lds ? kept_stats(sh, LdsKeys<kTopkThreads>{sh.cand, sel.ncand}, sel.thr, c, list, K)
                          : kept_stats(sh, SrcKeys<Src>{src}, sel.thr, c, list, K);
   r.in_lds = sel.in_lds;
   r.ncand = sel.ncand;
@@ -415,20 +415,30 @@ __device__ __forceinline__ Judged judge_topk(const Args &a, int b, int j) {
   return judge_one(a, seq_of(a, b), j, zp, zq, pzero, qzero, pr.R, pr.S, qr.R, qr.S);
 }
 
+// One launch per window [w0, w1) of positions (w0 = w1 = gamma: judge and
+// sample only).  Blocks per sequence: 2 (w1 - w0), at least 1; block
+// (rp, r) selects row w0 + rp of the draft (r = 0) or the target (r = 1), and
+// block 0 leads (writes the outputs, draws the token).  Every block first
+// judges the previous window [p0, w0) of its sequence (wave 0, lane l:
+// position p0 + l; a ballot finds the first rejection).
 template <int DT>
-__global__ __launch_bounds__(kTopkThreads) void k_topk_step(Args a, int j) {
+__global__ __launch_bounds__(kTopkThreads) void k_topk_step(Args a, int launch, int p0, int w0, int w1) {
   __shared__ TopkShared sh;
-  const int b = blockIdx.x >> 1;
-  const int r = blockIdx.x & 1;  // 0: draft row (and the sequence's lead), 1: target row
-  const bool lead = r == 0;
+  const int dw = w1 - w0;
+  const int per_seq = dw > 0 ? 2 * dw : 1;
+  const int b = blockIdx.x / per_seq;
+  const int rem = blockIdx.x - b * per_seq;
+  const int rp = rem >> 1, r = rem & 1;  // r: 0 draft row (block 0 leads), 1 target row
+  const bool lead = rem == 0;
   const int gamma = a.gamma;
-  int32_t *state_in = a.state + (size_t)((j + 1) & 1) * a.B;
-  int32_t *state_out = a.state + (size_t)(j & 1) * a.B;
+  int32_t *state_in = a.state + (size_t)((launch + 1) & 1) * a.B;
+  int32_t *state_out = a.state + (size_t)(launch & 1) * a.B;
 
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
-    int mode = 0;  // 0 select row j, 1 residual at j-1, 2 bonus, -1 nothing
-    if (j == 0) {
+    int mode = 0;  // 0 select a row of the window, 1 residual at row n, 2 bonus, -1 nothing
+    int n = 0;
+    if (w0 == 0) {
       if (!tokens_valid(a, b, lane)) {
         mode = -1;
         if (lead) {
@@ -442,30 +452,42 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_step(Args a, int j) {
       }
     } else {
       const int s = state_in[b];
-      if (s != j - 1) {
+      if (s != p0) {
         mode = -1;
         if (lead && lane == 0) state_out[b] = s;
       } else {
-        const Judged jr = judge_topk<DT>(a, b, j - 1);
-        if (lead && lane == 0) write_diag(a, b, j - 1, jr.pt, jr.qt, jr.u, jr.ratio);
-        if (!jr.accept) {
+        const int nj = w0 - p0;
+        const bool act = lane < nj;
+        Judged jr{};
+        if (act) jr = judge_topk<DT>(a, b, p0 + lane);
+        const unsigned long long mask = __ballot(act && jr.accept);
+        const int k = (mask == ~0ull) ? kWave : __builtin_ctzll(~mask);  // first clear bit
+        if (lead && act && lane <= k) write_diag(a, b, p0 + lane, jr.pt, jr.qt, jr.u, jr.ratio);
+        if (k < nj) {
+          n = p0 + k;
           mode = lead ? 1 : -1;
-          if (lead) write_judged(a, b, lane, j - 1);
+          if (lead) write_judged(a, b, lane, n);
           if (lead && lane == 0) state_out[b] = kDone;
-        } else if (j == gamma) {
+        } else if (w0 == gamma) {
           mode = lead ? 2 : -1;
           if (lead) write_judged(a, b, lane, gamma);
           if (lead && lane == 0) state_out[b] = kDone;
         } else if (lead && lane == 0) {
-          state_out[b] = j;
+          state_out[b] = w0;
         }
       }
     }
-    if (lane == 0) sh.bcast_n = mode;
+    if (lane == 0) {
+      sh.bcast_n = mode;
+      sh.sel_k = (unsigned)n;
+    }
   }
   __syncthreads();
   const int mode = sh.bcast_n;
+  const int n = (int)sh.sel_k;
+  __syncthreads();
   if (mode < 0) return;
+  const int j = w0 + rp;  // the row to select in mode 0
   int32_t *out = a.out_tokens + (size_t)b * (gamma + 1);
   if (mode == 0) {
     const int slot = r == 0 ? j : gamma + j;
@@ -475,7 +497,6 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_step(Args a, int j) {
     const TopkRow tr = select_row<DT>(sh, row, a.V, a.top_k, a.c, list);
     if (threadIdx.x == 0) a.rowinfo[slot_of(a, b, slot)] = pack_rowinfo(tr);
   } else if (mode == 1) {
-    const int n = j - 1;
     const TopkRow pr = unpack_rowinfo(a.rowinfo[slot_of(a, b, n)]);
     const TopkRow qr = unpack_rowinfo(a.rowinfo[slot_of(a, b, gamma + n)]);
     const int2 *qlist = a.lists ? a.lists + slot_of(a, b, gamma + n) * (size_t)a.klist : nullptr;

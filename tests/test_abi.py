@@ -63,8 +63,11 @@ def test_launch_names(L):
     # large inputs: statistics of position 0 and its judgement, then one launch
     # per further position (each judges its position in place) and one to sample
     assert S.launch_names(1024, 4, 50257, 0, 0) == ["k_rows", "k_judge"] + ["k_rows"] * 4
-    # the top-k path picks in place
-    assert S.launch_names(256, 8, 152064, 1, 50) == ["k_topk_step"] * 9
+    # the top-k path: windows [0,1), [1,2), [2,4), [4,8) of the sequences still
+    # alive, then the judgement of the last window and the draw
+    assert S.launch_names(256, 8, 152064, 1, 50) == ["k_topk_step"] * 5
+    assert S.launch_names(16, 1, 152064, 1, 50) == ["k_topk_step"] * 2
+    assert S.launch_names(4, 3, 152064, 1, 300) == ["k_topk_step"] * 4
 
 
 def _call(L, **over):
