@@ -20,7 +20,6 @@ constexpr int kMaxGamma = 64;           // one wave ballots all positions
 constexpr int kMaxV = 1 << 28;          // byte offsets of a row fit 32 bits
 constexpr int kListMax = 1024;          // top-k lists kept up to this K
 constexpr double kSmallRows = 256e6;    // bytes of all rows below which one launch reads them all
-constexpr int kTargetItems = 2048;      // statistics items per launch to aim for
 constexpr int kSlotsPerCU = 8;          // resident k_rows blocks per compute unit
 constexpr size_t kAlign = 256;
 
@@ -46,7 +45,7 @@ int compute_units() {
 struct Plan {
   bool topk;
   int window;  // positions whose statistics one launch computes (dense path)
-  int nch, nvec, cv, ngb, cs_max, klist;
+  int nch, nch_max, nvec, ngb, cs_max, klist;
   size_t off_part, off_ztok, off_slist, off_sst, off_tlist, off_lcnt, off_icnt, off_pcnt, off_pbest;
   size_t off_nseq, off_state, off_rowinfo, off_lists;
   size_t total;
@@ -74,8 +73,8 @@ Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype
     // vectors (statistics) or two group blocks (sampling)
     const int max_ch = std::max(1, p.nvec / (2 * kThreads));
     const int rows = B * p.window;
+    p.nch_max = max_ch;
     p.nch = std::max(1, std::min((kTargetItems + rows - 1) / rows, max_ch));
-    p.cv = (p.nvec + p.nch - 1) / p.nch;
     // a sampled row is split so that every thread keeps at least one group block
     p.cs_max = std::max(1, std::min(kMaxSampleChunks, p.ngb / kThreads));
   }
@@ -84,7 +83,7 @@ Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype
   // Nothing here is read before this call writes it: the workspace needs no
   // initialisation and may serve calls of any shape in turn.
   const size_t dense = p.topk ? 0 : 1;
-  p.off_part = take(dense * B * gamma * p.nch * sizeof(float4));
+  p.off_part = take(dense * B * gamma * p.nch_max * sizeof(float4));
   p.off_ztok = take(dense * B * gamma * sizeof(float2));
   p.off_slist = take(dense * 3 * B * sizeof(int2));
   p.off_sst = take(dense * 3 * B * sizeof(float4));
@@ -125,19 +124,17 @@ struct Launches {
       int w0 = std::min(a.gamma, p.window);
       before();
       hipLaunchKernelGGL((k_rows<DT, true>), dim3(grid((long long)a.B * w0 * p.nch)), dim3(kThreads), 0, stream, a, 0, 0,
-                         w0, 0);
+                         w0);
       ok = ok && after();
       before();
       hipLaunchKernelGGL(k_judge<DT>, dim3((a.B + kJudgeWaves - 1) / kJudgeWaves), dim3(kJudgeWaves * kWave), 0,
                          stream, a, w0);
       ok = ok && after();
-      int target = 0;  // statistics items per sequence over launches 1..i
       for (int launch = 1;; ++launch) {
         const int w1 = std::min(a.gamma, w0 + p.window);
-        target += (w1 - w0) * p.nch;
         before();
-        const long long items = (long long)a.B * std::max((w1 - w0) * p.nch, p.cs_max);
-        hipLaunchKernelGGL((k_rows<DT, false>), dim3(grid(items)), dim3(kThreads), 0, stream, a, launch, w0, w1, target);
+        const long long items = (long long)a.B * std::max((w1 - w0) * p.nch_max, p.cs_max);
+        hipLaunchKernelGGL((k_rows<DT, false>), dim3(grid(items)), dim3(kThreads), 0, stream, a, launch, w0, w1);
         ok = ok && after();
         if (w0 == a.gamma) break;
         w0 = w1;
@@ -210,8 +207,8 @@ sv_status verify_impl(const void *target, const void *draft, const int32_t *toke
   a.pcnt = (int32_t *)(ws + p.off_pcnt);
   a.pbest = (unsigned long long *)(ws + p.off_pbest);
   a.nch = p.nch;
+  a.nch_max = p.nch_max;
   a.nvec = p.nvec;
-  a.cv = p.cv;
   a.ngb = p.ngb;
   a.cs_max = p.cs_max;
   a.nseq = (int32_t *)(ws + p.off_nseq);

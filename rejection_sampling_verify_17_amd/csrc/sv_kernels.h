@@ -46,6 +46,7 @@ namespace sv {
 constexpr int kThreads = 256;
 constexpr int kJudgeWaves = 16;          // sequences judged side by side per k_judge block
 constexpr int kBonusRow = 0x10000;       // sampling-list flag: sample the bonus row
+constexpr int kTargetItems = 2048;       // statistics items per launch to aim for
 constexpr int kMaxSampleChunks = 8;      // chunks a sampled row is split into at most (each finishes with atomics on the row's counters)
 
 // Per-sequence state of the top-k path between launches: w >= 0 means
@@ -66,17 +67,18 @@ struct Args {
   float *token_probs;      // [B][gamma][2] or null
   float *accept_ur;        // [B][gamma][2] or null
   // workspace, dense path
-  float4 *part;            // [B][gamma][nch] {Rp, Sp, Rq, Sq}
+  float4 *part;            // [B][gamma][nch_max] {Rp, Sp, Rq, Sq}
   float2 *ztok;            // [B][gamma] draft and target logit at the drafted token
   int2 *slist;             // [3][B] sampling lists {b, row | kBonusRow}
   float4 *sst;             // [3][B] statistics of the sampled row pair
   int32_t *tlist;          // [3][B] statistics lists: sequences alive for the next window
   int32_t *lcnt;           // [3][2] list lengths {sampling, statistics}
-  int32_t *icnt;           // [B] statistics items finished (over the windows judged in k_rows)
+  int32_t *icnt;           // [B] statistics items of the current window finished
   int32_t *pcnt;           // [B] sampling chunks finished
   unsigned long long *pbest;  // [B] best packed key of the sampled row so far (0 = none)
-  int32_t nch;             // statistics: vocabulary chunks per row
-  int32_t nvec, cv;        // statistics: 16-byte vectors per row (any alignment), per chunk
+  int32_t nch;             // statistics: vocabulary chunks per row in launch 0
+  int32_t nch_max;         // statistics: chunks per row at most (stride of part)
+  int32_t nvec;            // statistics: 16-byte vectors per row (any alignment)
   int32_t ngb;             // sampling: group blocks (16 bytes of entries) per row
   int32_t cs_max;          // sampling: chunks per row at most
   // both paths
@@ -375,9 +377,9 @@ __device__ __forceinline__ int pow2_at_least(int x) {
 }
 
 template <int DT>
-__device__ void judge_window(const Args &a, int b, int lane, int p0, int w0, bool first, int &mode, int &row,
-                             float4 &st) {
-  const int gamma = a.gamma, nch = a.nch;
+__device__ void judge_window(const Args &a, int b, int lane, int p0, int w0, int nch, bool first, int &mode,
+                             int &row, float4 &st) {
+  const int gamma = a.gamma;
   const int nj = w0 - p0;
   mode = -1;
   row = 0;
@@ -395,7 +397,7 @@ __device__ void judge_window(const Args &a, int b, int lane, int p0, int w0, boo
     const int myq = q0 + lane / gs;
     float rp = -INFINITY, sp = 0.0f, rq = -INFINITY, sq = 0.0f;
     if (myq < nj) {
-      const float4 *pp = a.part + ((size_t)b * gamma + p0 + myq) * nch;
+      const float4 *pp = a.part + ((size_t)b * gamma + p0 + myq) * a.nch_max;
       for (int ch = lane % gs; ch < nch; ch += gs) {
         const float4 v = load_coherent(pp + ch);
         merge_stats(rp, sp, v.x, v.y);
@@ -500,7 +502,7 @@ __global__ __launch_bounds__(kJudgeWaves *kWave) void k_judge(Args a, int w0) {
       a.pcnt[b] = 0;
       a.pbest[b] = 0ull;
     }
-    judge_window<DT>(a, b, lane, 0, w0, true, mode, row, st);
+    judge_window<DT>(a, b, lane, 0, w0, a.nch, true, mode, row, st);
   }
   if (lane == 0) {
     sh_mode[wave] = mode;
@@ -550,10 +552,9 @@ __device__ __forceinline__ float uni(float x) {
 // end of a round the block finishes all its items together: winners folded
 // into the row's best key, per-sequence counters advanced, and for every
 // sequence whose window or sampled row it completed, the judgement (window)
-// or the token (row).  `target` is the number of statistics items of a
-// sequence over launches 1..i.
+// or the token (row).
 template <int DT, bool FIRST>
-__global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int launch, int w0, int w1, int target) {
+__global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int launch, int w0, int w1) {
   constexpr int kQueue = 64;
   __shared__ int sh_nq;
   __shared__ int q_b[kQueue], q_row[kQueue];  // row >= 0: sampled row; -1: statistics item
@@ -566,11 +567,19 @@ __global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int launch, int w0
     n_stat = min(max(uni(a.lcnt[2 * li + 1]), 0), a.B);
   }
   if (blockIdx.x == 0 && threadIdx.x < 2) a.lcnt[2 * list_set(launch + (FIRST ? 1 : 2)) + threadIdx.x] = 0;
-  const int per_stat = (w1 - w0) * a.nch;
   // about two sampling items per block, each thread keeping at least one
   // group block
   const int cs = n_samp > 0 ? max(1, min(a.cs_max, (int)((2 * gridDim.x + n_samp - 1) / n_samp))) : 1;
   const long long s_items = (long long)n_samp * cs;
+  // chunks per row: fixed in launch 0 (k_judge reads them); later, more when
+  // few rows and few sampling items are left, so about kTargetItems items
+  // keep the chip busy
+  const int dw = w1 - w0;
+  const int want = (int)max(0ll, (long long)kTargetItems - s_items);
+  const int rows = max(1, n_stat * dw);
+  const int nch = FIRST ? a.nch : max(a.nch, min(a.nch_max, (want + rows - 1) / rows));
+  const int cv = (a.nvec + nch - 1) / nch;
+  const int per_stat = dw * nch;
   const long long total = s_items + (long long)n_stat * per_stat;
   const long long round = (long long)kQueue * gridDim.x;
   if (threadIdx.x == 0) sh_nq = 0;
@@ -602,14 +611,14 @@ __global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int launch, int w0
         const long long k2 = k - s_items;
         const int l = (int)(k2 / per_stat);
         const int rc = (int)(k2 - (long long)l * per_stat);
-        const int r = rc / a.nch, ch = rc - r * a.nch;
+        const int r = rc / nch, ch = rc - r * nch;
         const int b = FIRST ? l : uni(a.tlist[(size_t)li * a.B + l]);
         if ((unsigned)b >= (unsigned)a.B) continue;  // never taken: entries come from append()
         const int j = w0 + r;
-        const int v0 = ch * a.cv;
-        const float4 pst = chunk_stats<DT>(a, b, j, v0, min(a.nvec, v0 + a.cv));
+        const int v0 = ch * cv;
+        const float4 pst = chunk_stats<DT>(a, b, j, v0, min(a.nvec, v0 + cv));
         if (threadIdx.x == 0) {
-          store_coherent(a.part + ((size_t)b * a.gamma + j) * a.nch + ch, pst);
+          store_coherent(a.part + ((size_t)b * a.gamma + j) * a.nch_max + ch, pst);
           if (!FIRST) {
             const int q = sh_nq++;
             q_b[q] = b;
@@ -632,7 +641,7 @@ __global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int launch, int w0
       const bool samp = q_row[t] >= 0;
       const int old = __hip_atomic_fetch_add(samp ? a.pcnt + b : a.icnt + b, 1, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
-      const bool fin = old == (samp ? cs : target) - 1;
+      const bool fin = old == (samp ? cs : per_stat) - 1;
       q_fin[t] = fin;
       if (fin && samp) {
         const unsigned long long best =
@@ -648,8 +657,12 @@ __global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int launch, int w0
       const int b = q_b[q];
       int mode, row;
       float4 st;
-      judge_window<DT>(a, b, threadIdx.x % kWave, w0, w1, false, mode, row, st);
-      if (threadIdx.x % kWave == 0) append(a, list_set(launch + 1), mode, b, row, st);
+      judge_window<DT>(a, b, threadIdx.x % kWave, w0, w1, nch, false, mode, row, st);
+      if (threadIdx.x % kWave == 0) {
+        // every item of this window is counted: the counter starts over for the next
+        if (mode == 0) __hip_atomic_store(a.icnt + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        append(a, list_set(launch + 1), mode, b, row, st);
+      }
     }
     // an empty residual (reachable only through rounding): sample q_row
     for (int q = 0; q < nq; ++q) {
