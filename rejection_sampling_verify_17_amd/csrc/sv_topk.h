@@ -6,19 +6,24 @@
 // ordered like "larger logit, then smaller index"; the kept set is the K
 // largest keys, i.e. all keys >= the K-th largest ("threshold").
 //
-// The drafts are judged left to right and nothing after the first rejection is
-// read.  k_topk_step(j) runs two blocks per sequence (draft row, target row):
-//   j = 0        each block selects its row 0: threshold by an LDS radix
-//                select, base-2 softmax statistics (R, S) over the kept
-//                entries and, for small K, the kept list.
-//   j >= 1       both blocks of a sequence alive at j-1 judge position j-1
-//                (wave 0: membership of t in both kept sets, ratio in
-//                registers, Philox u); accepted and j < gamma: each selects
-//                its row j; rejected: the draft-row block draws the
-//                replacement from the residual over the target row's kept
-//                list; accepted at j = gamma: the draft-row block selects
-//                target row gamma and draws the bonus token over its kept
-//                entries.  The deciding block writes the token itself.
+// The drafts are judged left to right; positions are walked in windows
+// [0, 1), [1, 2), [2, 4), [4, 8), ... and k_topk_step(window) runs one block
+// per row of the window (draft and target rows of every position):
+//   first window   each block selects its row: threshold by an LDS radix
+//                  select, base-2 softmax statistics (R, S) over the kept
+//                  entries and, for small K, the kept list.
+//   later windows  every block of a sequence alive at the previous window
+//                  first judges it (wave 0, lane l: position p0 + l,
+//                  membership of t in both kept sets, ratio in registers,
+//                  Philox u; a ballot finds the first rejection); all kept:
+//                  each selects its row of the new window; rejected at n: the
+//                  lead block draws the replacement from the residual over
+//                  the target row's kept list of position n; all kept and no
+//                  window left: the lead block selects target row gamma and
+//                  draws the bonus token over its kept entries.  The deciding
+//                  block writes the token itself.
+// With low acceptance few sequences reach the wide windows, and a launch over
+// few rows costs about as much as one over many.
 //
 // Selection: a lower bound L on the K-th largest logit comes from the
 // per-thread maxima (K threads each own an entry >= their maximum's K-th
