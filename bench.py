@@ -18,6 +18,7 @@ from __future__ import annotations
 import argparse
 import ctypes
 import hashlib
+import re
 import json
 import os
 import sys
@@ -68,10 +69,16 @@ class Hip:
 
 
 def source_digest() -> str:
+    """Digest of the kernel sources with comments and blank space removed, so
+    that counter summaries stay valid across edits of the documentation only."""
     h = hashlib.sha256()
     for f in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        text = " ".join(text.split())
+        h.update(f.encode() + b"\0" + text.encode())
     return h.hexdigest()[:16]
 
 
@@ -79,7 +86,7 @@ def source_digest() -> str:
 # Algorithmic bytes
 # ---------------------------------------------------------------------------
 def algorithmic_bytes(w, n_accepted: np.ndarray) -> dict:
-    """Bytes the method must move ("Roofline"), from the step's own
+    """Bytes the method must move, from the step's own
     outcome n_b.  The drafts are judged left to right and nothing after the
     first rejection is needed, so the statistics read row pairs 0..n_b
     (min(n_b + 1, gamma) pairs, 2 V b bytes each); the resample then reads
