@@ -49,6 +49,7 @@ struct TopkShared {
   unsigned int tmax[kTopkThreads];
   unsigned int ncand;
   unsigned int nkept;
+  unsigned int nhot;
   unsigned long long sel_prefix;
   unsigned int sel_k;
   int sel_done;
@@ -140,14 +141,32 @@ template <int NT> struct LdsMax32 {  // per-thread maxima as 32-bit keys in the 
 // entry of the row (any order), kU 16-byte loads in flight per thread.
 template <int DT> struct StreamRow {
   static constexpr int NE = Elem<DT>::kVec;
-  static constexpr int kU = 4;
+  static constexpr int kU = 2;
   const Row<DT> &row;
   int e0, e1;  // entries [e0, e1) of the row
   __device__ __forceinline__ StreamRow(const Row<DT> &r, int V) : row(r), e0(0), e1(V) {}
   __device__ __forceinline__ StreamRow(const Row<DT> &r, int lo, int hi) : row(r), e0(lo), e1(hi) {}
+  __device__ __forceinline__ int iv0() const { return (e0 + row.s) / NE; }          // vector holding entry e0
+  __device__ __forceinline__ int iv1() const { return (e1 - 1 + row.s) / NE + 1; }  // one past the vector holding e1 - 1
+  // Vectors thread t visits in for_each: iv0 + t + kTopkThreads i, i < this.
+  __device__ __forceinline__ int vectors_per_thread() const {
+    return (iv1() - iv0() + kTopkThreads - 1) / kTopkThreads;
+  }
+  // f(z, v) for the entries of the i-th vector thread t visits in for_each.
+  template <class F> __device__ __forceinline__ void for_vector_of(int t, int i, F f) const {
+    const int iv = iv0() + t + kTopkThreads * i;
+    if (iv >= iv1()) return;
+    float z[NE];
+    decode<DT>(row.raw(iv), z);
+    const int ev = iv * NE - row.s;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      const int v = ev + e;
+      if (v >= e0 && v < e1) f(z[e], v);
+    }
+  }
   template <class F> __device__ __forceinline__ void for_each(F f) const {
-    const int iv0 = (e0 + row.s) / NE;            // vector holding entry e0
-    const int iv1 = (e1 - 1 + row.s) / NE + 1;    // one past the vector holding e1 - 1
+    const int iv0 = this->iv0(), iv1 = this->iv1();
     for (int base = iv0 + (int)threadIdx.x; base < iv1; base += kTopkThreads * kU) {
       u32x4 d[kU];
 #pragma unroll
@@ -157,10 +176,15 @@ template <int DT> struct StreamRow {
         float z[NE];
         decode<DT>(d[u], z);
         const int ev = (base + u * kTopkThreads) * NE - row.s;
+        if (ev >= e0 && ev + NE <= e1) {  // the whole vector is inside (no test per entry)
 #pragma unroll
-        for (int e = 0; e < NE; ++e) {
-          const int v = ev + e;
-          if (v >= e0 && v < e1 && base + u * kTopkThreads < iv1) f(z[e], v);
+          for (int e = 0; e < NE; ++e) f(z[e], ev + e);
+        } else {
+#pragma unroll
+          for (int e = 0; e < NE; ++e) {
+            const int v = ev + e;
+            if (v >= e0 && v < e1 && base + u * kTopkThreads < iv1) f(z[e], v);
+          }
         }
       }
     }
@@ -206,7 +230,7 @@ __device__ __forceinline__ Selected select_threshold(TopkShared &sh, const Src &
     any = true;
   });
   sh.tmax[tid] = any ? orderable(zmax) : 0u;  // 0: no entry (every real key is > 0)
-  if (tid == 0) { sh.ncand = 0u; sh.nkept = 0u; }
+  if (tid == 0) { sh.ncand = 0u; sh.nkept = 0u; sh.nhot = 0u; }
   __syncthreads();
 
   // Phase B: lower bound L = K-th largest per-thread maximum: K threads own an
@@ -216,15 +240,27 @@ __device__ __forceinline__ Selected select_threshold(TopkShared &sh, const Src &
   const bool take_all = L == 0u;
   const float Lf = take_all ? -INFINITY : from_orderable(L);
 
-  // Phase C (a second pass, served from cache): gather every entry with
-  // logit >= L into LDS as its 64-bit key (-0 also passes a +0 bound, which
-  // only adds a candidate).
-  src.for_each([&](float z, int v) {
+  // Phase C (a second pass): gather every entry with logit >= L into LDS as
+  // its 64-bit key (-0 also passes a +0 bound, which only adds a candidate).
+  // Such an entry lies at or below its thread's maximum, so only the vectors
+  // of threads whose maximum reaches L (about K threads) are read again, all
+  // of them at once: the block deals them out one vector per thread.
+  auto gather = [&](float z, int v) {
     if (take_all || z >= Lf) {
       const unsigned int slot = atomicAdd(&sh.ncand, 1u);
       if (slot < (unsigned int)kCap) sh.cand[slot] = entry_key(z, (uint32_t)v);
     }
-  });
+  };
+  if (take_all) {
+    src.for_each(gather);
+  } else {
+    // the per-thread maxima are read; their array now lists those threads
+    if (any && zmax >= Lf) sh.tmax[atomicAdd(&sh.nhot, 1u)] = (unsigned int)tid;
+    __syncthreads();
+    const int per = src.vectors_per_thread();
+    const int nvis = (int)sh.nhot * per;
+    for (int i = tid; i < nvis; i += kTopkThreads) src.for_vector_of((int)sh.tmax[i / per], i % per, gather);
+  }
   __syncthreads();
   const unsigned int ncand = sh.ncand;
   const bool in_lds = ncand <= (unsigned int)kCap;
@@ -427,7 +463,8 @@ __device__ __forceinline__ Judged judge_topk(const Args &a, int b, int j) {
 // judges the previous window [p0, w0) of its sequence (wave 0, lane l:
 // position p0 + l; a ballot finds the first rejection).
 template <int DT>
-__global__ __launch_bounds__(kTopkThreads) void k_topk_step(Args a, int launch, int p0, int w0, int w1) {
+// Two blocks per compute unit (eight waves per SIMD) keep enough rows in flight.
+__global__ __launch_bounds__(kTopkThreads, 8) void k_topk_step(Args a, int launch, int p0, int w0, int w1) {
   __shared__ TopkShared sh;
   const int dw = w1 - w0;
   const int per_seq = dw > 0 ? 2 * dw : 1;
