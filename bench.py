@@ -4,8 +4,9 @@
 A step is one sv_verify call over one batch of a synthetic workload (every
 kernel of the hot path: softmax statistics, acceptance ratios, first-rejection
 ballot, residual / bonus Gumbel-max sampling).  Inputs are resident in HBM
-before timing starts; for workloads smaller than 1 GiB several copies are
-rotated so repeated steps do not hit the 256 MB last-level cache.
+before timing starts; at least two copies (more for workloads under 1 GiB)
+are rotated, so a step never finds rows the previous step left in the 256 MB
+last-level cache.
 
 Prints ONE JSON line: verified draft positions per second on the headline
 workload (c4b: B=1024, gamma=4, V=50257, fp32, draft noise sigma 1), the
@@ -118,7 +119,7 @@ def run_workload(name: str, steps: int, warmup: int, hip: Hip, seed: int = 3000)
     gen_s = time.time() - t0
     dev = torch.device("cuda:0")
     nbytes = w.target.nbytes + w.draft.nbytes
-    copies = max(1, min(8, int(np.ceil((1 << 30) / nbytes))))
+    copies = max(2, min(8, int(np.ceil((1 << 30) / nbytes))))
     if w.is_bf16:
         tgt0 = torch.from_numpy(w.target.view(np.int16)).view(torch.bfloat16)
         drf0 = torch.from_numpy(w.draft.view(np.int16)).view(torch.bfloat16)

@@ -567,17 +567,18 @@ __global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int launch, int w0
     n_stat = min(max(uni(a.lcnt[2 * li + 1]), 0), a.B);
   }
   if (blockIdx.x == 0 && threadIdx.x < 2) a.lcnt[2 * list_set(launch + (FIRST ? 1 : 2)) + threadIdx.x] = 0;
-  // about two sampling items per block, each thread keeping at least one
-  // group block
-  const int cs = n_samp > 0 ? max(1, min(a.cs_max, (int)((2 * gridDim.x + n_samp - 1) / n_samp))) : 1;
-  const long long s_items = (long long)n_samp * cs;
-  // chunks per row: fixed in launch 0 (k_judge reads them); later, more when
-  // few rows and few sampling items are left, so about kTargetItems items
-  // keep the chip busy
+  // Chunks per row: fixed in launch 0 (k_judge reads them).  Later launches
+  // share the grid between the row pairs to read (statistics) and the rows to
+  // sample, the same number of blocks per row pair for both kinds, so that
+  // every block takes one item and all finish about together (sampling chunks
+  // are capped: past a few per row, more blocks only add fixed costs).
+  const int G = (int)gridDim.x;
   const int dw = w1 - w0;
-  const int want = (int)max(0ll, (long long)kTargetItems - s_items);
-  const int rows = max(1, n_stat * dw);
-  const int nch = FIRST ? a.nch : max(a.nch, min(a.nch_max, (want + rows - 1) / rows));
+  const int rows = n_stat * dw;
+  const int per_pair = max(1, G / max(1, rows + n_samp));
+  const int nch = FIRST ? a.nch : min(a.nch_max, per_pair);
+  const int cs = n_samp > 0 ? max(1, min(a.cs_max, (G - rows * nch) / n_samp)) : 1;
+  const long long s_items = (long long)n_samp * cs;
   const int cv = (a.nvec + nch - 1) / nch;
   const int per_stat = dw * nch;
   const long long total = s_items + (long long)n_stat * per_stat;
