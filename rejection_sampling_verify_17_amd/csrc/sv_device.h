@@ -29,10 +29,12 @@ struct Philox4 {
   uint32_t w[4];
 };
 
-__device__ __forceinline__ Philox4 philox(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
-                                          uint32_t k0, uint32_t k1) {
+// Rounds FIRST .. 9 of Philox4x32-10 from the words and keys of round FIRST.
+template <int FIRST>
+__device__ __forceinline__ Philox4 philox_rounds(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1) {
 #pragma unroll
-  for (int round = 0; round < 10; ++round) {
+  for (int round = FIRST; round < 10; ++round) {
     const uint32_t mA = 0xD2511F53u, mB = 0xCD9E8D57u;
     // one v_mad_u64_u32 gives both halves of each product
     uint64_t pA, pB, ccA, ccB;
@@ -56,6 +58,41 @@ __device__ __forceinline__ Philox4 philox(uint32_t c0, uint32_t c1, uint32_t c2,
   r.w[3] = c3;
   return r;
 }
+
+__device__ __forceinline__ Philox4 philox(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                          uint32_t k0, uint32_t k1) {
+  return philox_rounds<0>(c0, c1, c2, c3, k0, k1);
+}
+
+// The blocks of one (seq, pos, purpose) stream, group by group: only the
+// group word varies, so the first-round product of the seq word and the
+// second-round product of the first word are the same for every group and
+// are formed once (18 instead of 20 lane-wise products per block, same bits).
+struct PhiloxStream {
+  uint32_t k0, k1, purpose;
+  uint32_t w0, lo_b0;    // second-round words 0 and 1
+  uint32_t hi_a1, lo_a1;  // second-round product of word 0
+  __device__ __forceinline__ PhiloxStream(uint32_t key0, uint32_t key1, uint32_t seq, uint32_t pos, uint32_t pur)
+      : k0(key0), k1(key1), purpose(pur) {
+    const uint64_t pb0 = (uint64_t)0xCD9E8D57u * seq;
+    lo_b0 = (uint32_t)pb0;
+    w0 = (uint32_t)(pb0 >> 32) ^ pos ^ key0;
+    const uint64_t pa1 = (uint64_t)0xD2511F53u * w0;
+    hi_a1 = (uint32_t)(pa1 >> 32);
+    lo_a1 = (uint32_t)pa1;
+  }
+  __device__ __forceinline__ Philox4 block(uint32_t group) const {
+    uint64_t pA, pB, cc;
+    asm("v_mad_u64_u32 %0, %1, %2, %3, 0" : "=v"(pA), "=s"(cc) : "s"(0xD2511F53u), "v"(group));
+    const uint32_t hi_a0 = (uint32_t)(pA >> 32), lo_a0 = (uint32_t)pA;
+    const uint32_t c2 = hi_a0 ^ purpose ^ k1;  // first round done: words (w0, lo_b0, c2, lo_a0)
+    asm("v_mad_u64_u32 %0, %1, %2, %3, 0" : "=v"(pB), "=s"(cc) : "s"(0xCD9E8D57u), "v"(c2));
+    const uint32_t n0 = (uint32_t)(pB >> 32) ^ lo_b0 ^ (k0 + 0x9E3779B9u);
+    const uint32_t n2 = hi_a1 ^ lo_a0 ^ (k1 + 0xBB67AE85u);
+    // second round done: words (n0, lo(pB), n2, lo_a1), keys advanced twice
+    return philox_rounds<2>(n0, (uint32_t)pB, n2, lo_a1, k0 + 2u * 0x9E3779B9u, k1 + 2u * 0xBB67AE85u);
+  }
+};
 
 // The four words of vocabulary group g (entries 4g .. 4g+3) at (seq, pos, purpose).
 __device__ __forceinline__ Philox4 stream_block(uint32_t k0, uint32_t k1, uint32_t seq, uint32_t pos,

@@ -318,6 +318,7 @@ __device__ unsigned long long chunk_winner(const Args &a, int b, int pos, float4
   const Row<DT> P(draft_row<DT>(a, b, RESID ? pos : 0), a.V);
   const float invSp = 1.0f / st.y, invSq = 1.0f / st.w;
   const uint32_t lim = (uint32_t)min(a.V, g1 * NE);  // entries at or past lim are masked
+  const PhiloxStream ps(a.key0, a.key1, seq, (uint32_t)pos, PURPOSE_SAMPLE);
   float bestk = -INFINITY;        // bonus: best key
   float bestr = 0.0f, bestE = 1.0f;  // residual: best r / E2 as a fraction
   uint32_t besti = 0xFFFFFFFFu;  // none
@@ -334,7 +335,7 @@ __device__ unsigned long long chunk_winner(const Args &a, int b, int pos, float4
 #pragma unroll
       for (int g = 0; g < NE / 4; ++g) {
         const uint32_t group = (uint32_t)(gb * (NE / 4) + g);
-        const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)pos, group, PURPOSE_SAMPLE);
+        const Philox4 blk = ps.block(group);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t idx = group * 4u + (uint32_t)e;
