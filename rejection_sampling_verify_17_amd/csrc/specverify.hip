@@ -56,7 +56,8 @@ bool shape_ok(int32_t B, int32_t gamma, int32_t V, int32_t dtype) {
          (dtype == SV_F32 || dtype == SV_BF16);
 }
 
-Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype) {
+// `resident`: k_rows blocks resident at once (the grid of a launch).
+Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype, int resident = 2048) {
   Plan p{};
   const int ne = dtype == SV_BF16 ? 8 : 4;
   p.nvec = (V + 2 * ne - 2) / ne;  // vectors covering a row at any 16-byte offset
@@ -69,12 +70,13 @@ Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype
     // reads them all; otherwise one position per launch.
     const double all_rows = 2.0 * B * gamma * (double)V * (dtype == SV_BF16 ? 2 : 4);
     p.window = all_rows <= kSmallRows ? gamma : 1;
-    // about kTargetItems statistics items per launch, each thread keeping at least two
-    // vectors (statistics) or two group blocks (sampling)
+    // launch 0: at most one statistics item per resident block, so no block
+    // takes a second one while others idle; every thread keeps at least two
+    // vectors
     const int max_ch = std::max(1, p.nvec / (2 * kThreads));
     const int rows = B * p.window;
     p.nch_max = max_ch;
-    p.nch = std::max(1, std::min((kTargetItems + rows - 1) / rows, max_ch));
+    p.nch = std::max(1, std::min(resident / rows, max_ch));
     // a sampled row is split so that every thread keeps at least one group block
     p.cs_max = std::max(1, std::min(kMaxSampleChunks, p.ngb / kThreads));
   }
@@ -176,7 +178,7 @@ sv_status verify_impl(const void *target, const void *draft, const int32_t *toke
   if (((uintptr_t)target % elem) || ((uintptr_t)draft % elem)) return SV_EINVAL;
   if (((uintptr_t)tokens % 4) || ((uintptr_t)out_tokens % 4) || ((uintptr_t)n_accepted % 4)) return SV_EINVAL;
   if ((uintptr_t)workspace % kAlign) return SV_EINVAL;
-  const Plan p = make_plan(B, gamma, V, top_k, dtype);
+  const Plan p = make_plan(B, gamma, V, top_k, dtype, kSlotsPerCU * compute_units());
   if (workspace_bytes < p.total) return SV_EINVAL;
   if (events && n_events < 0) return SV_EINVAL;
 

@@ -46,7 +46,6 @@ namespace sv {
 constexpr int kThreads = 256;
 constexpr int kJudgeWaves = 16;          // sequences judged side by side per k_judge block
 constexpr int kBonusRow = 0x10000;       // sampling-list flag: sample the bonus row
-constexpr int kTargetItems = 2048;       // statistics items per launch to aim for
 constexpr int kMaxSampleChunks = 8;      // chunks a sampled row is split into at most (each finishes with atomics on the row's counters)
 
 // Per-sequence state of the top-k path between launches: w >= 0 means
