@@ -45,6 +45,11 @@
  *  R7  output slots after the committed token hold -1.
  *  R8  a drafted token outside [0, V) marks the whole sequence invalid:
  *      n_accepted = -1 and the output row is all -1.
+ *  R9  temperature 0 is the arg-max mode of [SDE] "how it works": each
+ *      distribution is the point mass on the row's largest logit (the
+ *      smaller index among equal logits, as R5), and the rule is applied to
+ *      these distributions unchanged.  Top-k keeps the largest logit, so it
+ *      changes nothing there.
  *
  * Logits must be finite or -inf, and every row must keep at least one finite
  * logit; anything else is outside the method and not defined here.
@@ -164,10 +169,18 @@ static void svo_topk_keep(const void *row, int dtype, int V, int top_k, unsigned
 }
 
 /* prob[v] = softmax over kept entries of z/T (R1, R2); dropped entries get 0.
- * scratch_keep holds V bytes. */
+ * T = 0 is the arg-max mode (R9): the point mass on the largest logit, the
+ * smaller index among equal logits.  scratch_keep holds V bytes. */
 void svo_row_probs(const void *row, int dtype, int V, float temperature, int top_k,
                    double *prob, unsigned char *scratch_keep)
 {
+    if (temperature == 0.0f) {
+        int32_t best = 0;
+        for (int v = 1; v < V; ++v)
+            if (svo_logit(row, dtype, v) > svo_logit(row, dtype, best)) best = v;
+        for (int v = 0; v < V; ++v) prob[v] = v == best ? 1.0 : 0.0;
+        return;
+    }
     unsigned char *keep = scratch_keep;
     unsigned char *own = NULL;
     if (!keep) own = keep = (unsigned char *)malloc((size_t)V);
@@ -273,7 +286,7 @@ int svo_verify(const void *target, const void *draft, const int32_t *tokens,
 {
     if (!target || !draft || !tokens || !out_tokens || !n_accepted) return -1;
     if (B < 1 || gamma < 1 || V < 2 || (dtype != SVO_F32 && dtype != SVO_BF16)) return -1;
-    if (!(temperature > 0.0f) || !isfinite(temperature)) return -1;
+    if (!(temperature >= 0.0f) || !isfinite(temperature)) return -1;   /* R9: 0 = arg-max */
     const size_t esz = dtype == SVO_BF16 ? 2 : 4;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -354,7 +367,7 @@ int svo_token_probs(const void *target, const void *draft, const int32_t *tokens
                     int B, int gamma, int V, int dtype, float temperature, int top_k,
                     int nthreads, double *pt, double *qt)
 {
-    if (B < 1 || gamma < 1 || V < 2 || !(temperature > 0.0f)) return -1;
+    if (B < 1 || gamma < 1 || V < 2 || !(temperature >= 0.0f)) return -1;
     const size_t esz = dtype == SVO_BF16 ? 2 : 4;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);

@@ -31,6 +31,9 @@ MUTANTS = [
     ("token the target never emits is accepted",
      "if (!(q_t > 0.0)) return 0;", "if (!(q_t > 0.0)) return 1;", ["enumeration", "special"]),
     ("Philox key bump skipped", "k0 += PHX_W0;", "k0 += 0;", ["philox"]),
+    ("arg-max ties keep the larger index",
+     "if (svo_logit(row, dtype, v) > svo_logit(row, dtype, best)) best = v;",
+     "if (svo_logit(row, dtype, v) >= svo_logit(row, dtype, best)) best = v;", ["greedy"]),
 ]
 
 
@@ -51,6 +54,8 @@ def _run(check):
         C.check_row_probs_vs_torch()
     elif check == "topk":
         C.check_topk_vs_stable_sort()
+    elif check == "greedy":
+        C.check_greedy()
     elif check == "philox":
         import rocrand_ref
         rr = rocrand_ref.load()

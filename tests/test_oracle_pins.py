@@ -59,6 +59,11 @@ def test_special_cases():
     C.check_special_cases()
 
 
+def test_greedy_mode():
+    """T = 0 (arg-max mode of the ai-trend.me page, section "how it works")."""
+    C.check_greedy()
+
+
 def test_gumbel_sampler_is_multinomial():
     C.check_gumbel_sampler()
 
