@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 HEADLINE = "c4b"
-SWEEP = ["c2", "c3", "c4a", "c4c", "c1"]
+SWEEP = ["c2", "c3", "c4a", "c4c", "c1", "g4b", "g2"]
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "rejection_sampling_verify_17_amd", "csrc")
 
@@ -92,15 +92,21 @@ def algorithmic_bytes(w, n_accepted: np.ndarray) -> dict:
     first rejection is needed, so the statistics read row pairs 0..n_b
     (min(n_b + 1, gamma) pairs, 2 V b bytes each); the resample then reads
     row pair n_b again (2 V b; with top-k it works from the kept lists
-    instead) or the bonus row (V b).  Plus tokens in and outputs out."""
+    instead) or the bonus row (V b).  Plus tokens in and outputs out.  In the
+    arg-max mode (T = 0) only target rows 0..n_b are needed, once each."""
     B, gamma, V = w.B, w.gamma, w.V
     b = 2 if w.is_bf16 else 4
     n = n_accepted[n_accepted >= 0].astype(np.int64)
+    io = 4 * B * gamma + 4 * B * (gamma + 1) + 4 * B
+    if w.temperature == 0.0:
+        # arg-max mode: target rows 0..n_b, once each (the last one holds the token)
+        rows = int(np.sum(n + 1)) * V * b
+        return {"stats": rows, "sample": 0, "io": io, "total": rows + io,
+                "all_rows_once": B * (gamma + 1) * V * b}
     stats = int(np.sum(np.minimum(n + 1, gamma))) * 2 * V * b
     rej = int(np.sum(n < gamma))
     bonus = int(np.sum(n == gamma))
     sample = (0 if 0 < w.top_k < V else rej * 2 * V * b) + bonus * V * b
-    io = 4 * B * gamma + 4 * B * (gamma + 1) + 4 * B
     all_rows = 2 * B * gamma * V * b  # every draft and target row 0..gamma-1 once
     return {"stats": stats, "sample": sample, "io": io, "total": stats + sample + io,
             "all_rows_once": all_rows}
@@ -134,7 +140,7 @@ def run_workload(name: str, steps: int, warmup: int, hip: Hip, seed: int = 3000)
     nacc = torch.empty((w.B,), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = int(stream.cuda_stream)
-    names = S.launch_names(w.B, w.gamma, w.V, dt, w.top_k)
+    names = S.launch_names(w.B, w.gamma, w.V, dt, w.top_k, w.temperature)
     nl = len(names)
 
     def step(i, events=None):
@@ -281,7 +287,7 @@ def _find(d, suffix):
 
 
 def _short(name: str) -> str:
-    for k in ("k_topk_step", "k_rows", "k_judge"):
+    for k in ("k_topk_step", "k_greedy_step", "k_rows", "k_judge"):
         if k in name:
             return k
     return name[:60]

@@ -36,6 +36,15 @@
  *   - Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) with key
  *     (seed mod 2^32, seed >> 32), counter (v >> 2, pos, seq mod 2^32,
  *     purpose); the word is output (v mod 4).  seq = seq_offset + b.
+ *   - temperature 0 is the arg-max mode (page ai-trend.me, "어떻게 작동하나":
+ *     arg-max decoding is sampling from an adjusted distribution): every
+ *     distribution is the point mass on its row's largest logit, the smaller
+ *     index among equal logits (-0 equals +0).  The rule above then keeps
+ *     draft j iff t_j = argmax q_j, and the token after the kept prefix is
+ *     argmax q_n (the residual's only entry, or q_n itself when the residual
+ *     is empty) or argmax q_gamma.  Draft logits are not read, no random
+ *     number is drawn, top_k changes nothing, and token_probs / accept_ur of
+ *     sv_verify_debug are all NaN.
  *   Results are a pure function of (inputs, temperature, top_k, seed,
  *   seq_offset): independent of launch geometry and repeatable bit for bit.
  *
@@ -60,7 +69,7 @@
  *
  * Errors: argument errors return SV_EINVAL before anything is enqueued
  * (null pointer, B < 1, gamma not in [1, 64], V < 2 or V > 2^28, temperature
- * not finite or <= 0, unknown dtype, a logits pointer not aligned to its
+ * not finite or < 0, unknown dtype, a logits pointer not aligned to its
  * element size, workspace too small or misaligned).  A failed launch returns
  * SV_EHIP.  Calls never synchronise.
  */
@@ -83,7 +92,8 @@ extern "C" {
 typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 typedef enum { SV_OK = 0, SV_EINVAL = 1, SV_EHIP = 2 } sv_status;
 
-/* Bytes of device workspace sv_verify needs for this shape (0 on bad shape). */
+/* Bytes of device workspace sv_verify needs for this shape, at any temperature
+ * (0 on bad shape). */
 SV_API size_t sv_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype);
 
 /* One verification step; see the top of this file.  All pointers are device
@@ -128,7 +138,7 @@ SV_API sv_status sv_verify_timed(const void *target_logits, const void *draft_lo
 /* Name of kernel launch i of a call with these arguments (for matching event
  * timings to profiler rows); NULL past the last launch. */
 SV_API const char *sv_launch_name(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
-                           int32_t top_k, int32_t i);
+                           int32_t top_k, float temperature, int32_t i);
 
 /* Human-readable status. */
 SV_API const char *sv_status_string(sv_status s);

@@ -52,7 +52,7 @@ def lib() -> ctypes.CDLL:
                 L.sv_verify_debug.restype = i32
                 L.sv_verify_timed.argtypes = common + [vp, i32, vp]
                 L.sv_verify_timed.restype = i32
-                L.sv_launch_name.argtypes = [i32, i32, i32, i32, i32, i32]
+                L.sv_launch_name.argtypes = [i32, i32, i32, i32, i32, flt, i32]
                 L.sv_launch_name.restype = ctypes.c_char_p
                 L.sv_status_string.argtypes = [i32]
                 L.sv_status_string.restype = ctypes.c_char_p
@@ -74,10 +74,10 @@ def workspace_bytes(B: int, gamma: int, V: int, top_k: int, dtype: int) -> int:
     return int(lib().sv_workspace_bytes(B, gamma, V, top_k, dtype))
 
 
-def launch_names(B: int, gamma: int, V: int, dtype: int, top_k: int) -> list[str]:
+def launch_names(B: int, gamma: int, V: int, dtype: int, top_k: int, temperature: float = 1.0) -> list[str]:
     out, i = [], 0
     while True:
-        n = lib().sv_launch_name(B, gamma, V, dtype, top_k, i)
+        n = lib().sv_launch_name(B, gamma, V, dtype, top_k, float(temperature), i)
         if n is None:
             return out
         out.append(n.decode())

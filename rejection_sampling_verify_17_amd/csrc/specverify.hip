@@ -9,6 +9,7 @@
 #include <cstring>
 
 #include "specverify.h"
+#include "sv_greedy.h"
 #include "sv_kernels.h"
 #include "sv_topk.h"
 
@@ -42,12 +43,16 @@ int compute_units() {
   return n;
 }
 
+constexpr int kMaxWindows = 9;  // windows [0,1), [1,2), [2,4), ... over at most 65 rows
+
 struct Plan {
-  bool topk;
+  bool topk, greedy;
   int window;  // positions whose statistics one launch computes (dense path)
   int nch, nch_max, nvec, ngb, cs_max, klist;
+  // arg-max mode: windows [gw0, gw1) of target rows with gnch chunks per row
+  int nwin, gw0[kMaxWindows], gw1[kMaxWindows], gnch[kMaxWindows], gstride;
   size_t off_part, off_ztok, off_slist, off_sst, off_tlist, off_lcnt, off_icnt, off_pcnt, off_pbest;
-  size_t off_nseq, off_state, off_rowinfo, off_lists;
+  size_t off_nseq, off_state, off_rowinfo, off_lists, off_gpart;
   size_t total;
 };
 
@@ -57,14 +62,30 @@ bool shape_ok(int32_t B, int32_t gamma, int32_t V, int32_t dtype) {
 }
 
 // `resident`: k_rows blocks resident at once (the grid of a launch).
-Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype, int resident = 2048) {
+// `greedy`: the arg-max mode (temperature 0), where top-k changes nothing.
+Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype, bool greedy,
+               int resident = 2048) {
   Plan p{};
   const int ne = dtype == SV_BF16 ? 8 : 4;
   p.nvec = (V + 2 * ne - 2) / ne;  // vectors covering a row at any 16-byte offset
   p.ngb = (V + ne - 1) / ne;       // group blocks of ne entries
-  p.topk = top_k > 0 && top_k < V;
+  p.greedy = greedy;
+  p.topk = !greedy && top_k > 0 && top_k < V;
   p.klist = (p.topk && top_k <= kListMax) ? top_k : 0;
-  if (!p.topk) {
+  if (greedy) {
+    // every thread keeps at least kGreedyU vectors; a launch gets about one
+    // block per resident slot (dead sequences' blocks return at once)
+    p.gstride = std::max(1, p.nvec / (kGreedyThreads * kGreedyU));
+    for (int w0 = 0, size = 1; w0 <= gamma; ++p.nwin) {
+      const int w1 = std::min(gamma + 1, w0 + size);
+      const long long rows = (long long)B * (w1 - w0);
+      p.gw0[p.nwin] = w0;
+      p.gw1[p.nwin] = w1;
+      p.gnch[p.nwin] = (int)std::max(1LL, std::min<long long>(p.gstride, (resident + rows - 1) / rows));
+      if (w0 > 0) size *= 2;
+      w0 = w1;
+    }
+  } else if (!p.topk) {
     // Reading rows past the first rejection costs bytes; every extra launch
     // costs a fixed ~10 us.  When all rows together are small, one launch
     // reads them all; otherwise one position per launch.
@@ -84,7 +105,7 @@ Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
   // Nothing here is read before this call writes it: the workspace needs no
   // initialisation and may serve calls of any shape in turn.
-  const size_t dense = p.topk ? 0 : 1;
+  const size_t dense = (p.topk || p.greedy) ? 0 : 1;
   p.off_part = take(dense * B * gamma * p.nch_max * sizeof(float4));
   p.off_ztok = take(dense * B * gamma * sizeof(float2));
   p.off_slist = take(dense * 3 * B * sizeof(int2));
@@ -95,12 +116,19 @@ Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype
   p.off_pcnt = take(dense * B * sizeof(int32_t));
   p.off_pbest = take(dense * B * sizeof(unsigned long long));
   p.off_nseq = take((size_t)B * sizeof(int32_t));
-  p.off_state = take(p.topk ? 2 * (size_t)B * sizeof(int32_t) : 0);
+  p.off_state = take((p.topk || p.greedy) ? 2 * (size_t)B * sizeof(int32_t) : 0);
   const size_t slots = (size_t)B * (2 * gamma);
   p.off_rowinfo = take(p.topk ? slots * sizeof(uint4) : 0);
   p.off_lists = take(p.klist ? slots * (size_t)p.klist * sizeof(int2) : 0);
+  p.off_gpart = take(p.greedy ? (size_t)B * (gamma + 1) * p.gstride * sizeof(unsigned long long) : 0);
   p.total = off;
   return p;
+}
+
+// One workspace size serves every temperature.
+size_t workspace_total(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype) {
+  return std::max(make_plan(B, gamma, V, top_k, dtype, false).total,
+                  make_plan(B, gamma, V, top_k, dtype, true).total);
 }
 
 template <int DT>
@@ -120,7 +148,22 @@ struct Launches {
       return hipGetLastError() == hipSuccess;
     };
     bool ok = true;
-    if (!p.topk) {
+    if (p.greedy) {
+      // one launch per window of target rows, then one that judges the last
+      int p0 = 0, nprev = 1;
+      for (int L = 0; L <= p.nwin; ++L) {
+        const int w0 = L < p.nwin ? p.gw0[L] : a.gamma + 1;
+        const int w1 = L < p.nwin ? p.gw1[L] : a.gamma + 1;
+        const int nch = L < p.nwin ? p.gnch[L] : 1;
+        const long long grid = (long long)a.B * std::max(1, w1 - w0) * nch;
+        before();
+        hipLaunchKernelGGL(k_greedy_step<DT>, dim3((unsigned)grid), dim3(kGreedyThreads), 0, stream, a, L, p0, w0,
+                           w1, nch, nprev);
+        ok = ok && after();
+        p0 = w0;
+        nprev = nch;
+      }
+    } else if (!p.topk) {
       const int slots = kSlotsPerCU * compute_units();
       auto grid = [&](long long items) { return (unsigned)std::max(1LL, std::min<long long>(slots, items)); };
       int w0 = std::min(a.gamma, p.window);
@@ -173,13 +216,16 @@ sv_status verify_impl(const void *target, const void *draft, const int32_t *toke
   if (n_launches) *n_launches = 0;
   if (!target || !draft || !tokens || !out_tokens || !n_accepted || !workspace) return SV_EINVAL;
   if (!shape_ok(B, gamma, V, dtype)) return SV_EINVAL;
-  if (!std::isfinite(temperature) || !(temperature > 0.0f)) return SV_EINVAL;
+  if (!std::isfinite(temperature) || !(temperature >= 0.0f)) return SV_EINVAL;  // 0: arg-max mode
+  const bool greedy = temperature == 0.0f;
   const uintptr_t elem = dtype == SV_BF16 ? 2 : 4;
   if (((uintptr_t)target % elem) || ((uintptr_t)draft % elem)) return SV_EINVAL;
   if (((uintptr_t)tokens % 4) || ((uintptr_t)out_tokens % 4) || ((uintptr_t)n_accepted % 4)) return SV_EINVAL;
   if ((uintptr_t)workspace % kAlign) return SV_EINVAL;
-  const Plan p = make_plan(B, gamma, V, top_k, dtype, kSlotsPerCU * compute_units());
+  const Plan p = make_plan(B, gamma, V, top_k, dtype, greedy, kSlotsPerCU * compute_units());
   if (workspace_bytes < p.total) return SV_EINVAL;
+  // overflow guard for the arg-max grid (B * rows * chunks blocks)
+  if (greedy && (long long)B * (gamma + 1) * p.gstride > 0x7FFFFFFFLL) return SV_EINVAL;
   if (events && n_events < 0) return SV_EINVAL;
 
   char *ws = (char *)workspace;
@@ -191,7 +237,7 @@ sv_status verify_impl(const void *target, const void *draft, const int32_t *toke
   a.gamma = gamma;
   a.V = V;
   a.top_k = p.topk ? top_k : 0;
-  a.c = (float)(1.4426950408889634 / (double)temperature);
+  a.c = greedy ? 0.0f : (float)(1.4426950408889634 / (double)temperature);
   a.key0 = (uint32_t)seed;
   a.key1 = (uint32_t)(seed >> 32);
   a.seq_offset = seq_offset;
@@ -214,11 +260,17 @@ sv_status verify_impl(const void *target, const void *draft, const int32_t *toke
   a.ngb = p.ngb;
   a.cs_max = p.cs_max;
   a.nseq = (int32_t *)(ws + p.off_nseq);
-  a.state = p.topk ? (int32_t *)(ws + p.off_state) : nullptr;
+  a.state = (p.topk || p.greedy) ? (int32_t *)(ws + p.off_state) : nullptr;
   a.rowinfo = p.topk ? (uint4 *)(ws + p.off_rowinfo) : nullptr;
   a.lists = p.klist ? (int2 *)(ws + p.off_lists) : nullptr;
   a.klist = p.klist;
+  a.gpart = p.greedy ? (unsigned long long *)(ws + p.off_gpart) : nullptr;
+  a.gstride = p.gstride;
 
+  // the state and key buffers of the chosen path point into the workspace
+  // (kernels of the top-k and arg-max paths store to them unconditionally)
+  if ((p.topk || p.greedy) && !a.state) return SV_EINVAL;
+  if (p.greedy && !a.gpart) return SV_EINVAL;
   (void)hipGetLastError();  // start from a clean error state
   hipStream_t s = (hipStream_t)stream;
   if (dtype == SV_BF16) return Launches<DT_BF16>::run(a, p, s, events, n_events, n_launches);
@@ -231,7 +283,7 @@ extern "C" {
 
 size_t sv_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype) {
   if (!shape_ok(B, gamma, V, dtype)) return 0;
-  return make_plan(B, gamma, V, top_k, dtype).total;
+  return workspace_total(B, gamma, V, top_k, dtype);
 }
 
 sv_status sv_verify(const void *target_logits, const void *draft_logits, const int32_t *draft_tokens, int32_t B,
@@ -263,10 +315,12 @@ sv_status sv_verify_timed(const void *target_logits, const void *draft_logits, c
                      events, n_events, n_launches);
 }
 
-const char *sv_launch_name(int32_t B, int32_t gamma, int32_t V, int32_t dtype, int32_t top_k, int32_t i) {
+const char *sv_launch_name(int32_t B, int32_t gamma, int32_t V, int32_t dtype, int32_t top_k, float temperature,
+                           int32_t i) {
   if (!shape_ok(B, gamma, V, dtype)) return nullptr;
-  const Plan p = make_plan(B, gamma, V, top_k, dtype);
+  const Plan p = make_plan(B, gamma, V, top_k, dtype, temperature == 0.0f);
   if (i < 0) return nullptr;
+  if (p.greedy) return i <= p.nwin ? "k_greedy_step" : nullptr;
   if (p.topk) {
     int launches = 1;  // windows [0,1), [1,2), [2,4), ... then the judgement
     for (int w0 = 0, size = 1; w0 < gamma; ++launches) {

@@ -87,6 +87,9 @@ struct Args {
   uint4 *rowinfo;          // [B][2*gamma] {thr lo, thr hi, R bits, S bits}
   int2 *lists;             // [B][2*gamma][K] (index, logit bits) or null
   int32_t klist;           // K when lists are kept, else 0
+  // arg-max mode (temperature 0)
+  unsigned long long *gpart;  // [B][gamma+1][gstride] packed arg-max key per chunk
+  int32_t gstride;            // chunks per row at most
 };
 
 __device__ __forceinline__ uint32_t seq_of(const Args &a, int b) {

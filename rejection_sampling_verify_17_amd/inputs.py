@@ -13,6 +13,8 @@ Workloads (B sequences, gamma drafts, vocabulary V):
   c3   B=256,  gamma=8, V=152064, bf16, as c2 with draft noise sigma 2, T=0.8, top-k 50
   c4a/b/c B=1024, gamma=4, V=50257, fp32, target N(0, 3^2), draft = target + N(0, s^2),
        s = 0.25 / 1 / 4, T=1
+  g2   c2's logits at T=0 (arg-max mode)
+  g4b  c4b's logits at T=0 (arg-max mode)
 
 The Zipf bias of a target row is -1.1 * ln(rank), rank = pi(v) + 1 for a fresh
 uniform permutation pi of the vocabulary per target row; a draft row inherits
@@ -22,7 +24,7 @@ noise".  bf16 logits are rounded from fp32 to nearest-even.
 Drafted tokens stand in for the draft model's own sampling (outside the
 verification step): token j of a sequence is drawn from the draft row's
 adjusted distribution softmax(top-k(z) / T) by inverse CDF with a numpy
-generator.  The top-k here keeps the K largest logits, the smaller index on
+generator; at T=0 it is the draft row's first largest logit.  The top-k here keeps the K largest logits, the smaller index on
 equal logits, so drafted tokens lie inside the draft's kept set.
 """
 from __future__ import annotations
@@ -59,6 +61,8 @@ SPECS = {
     "c4a": Spec("c4a", 1024, 4, 50257, "f32", 1.0, 0, 3.0, 1.0, 0.25, False, 1040, 2040),
     "c4b": Spec("c4b", 1024, 4, 50257, "f32", 1.0, 0, 3.0, 1.0, 1.0, False, 1041, 2041),
     "c4c": Spec("c4c", 1024, 4, 50257, "f32", 1.0, 0, 3.0, 1.0, 4.0, False, 1042, 2042),
+    "g2": Spec("g2", 64, 5, 128256, "bf16", 0.0, 0, 3.0, 1.0, 1.0, True, 1002, 2002),
+    "g4b": Spec("g4b", 1024, 4, 50257, "f32", 0.0, 0, 3.0, 1.0, 1.0, False, 1041, 2041),
 }
 
 
@@ -129,8 +133,11 @@ def _adjusted(z: np.ndarray, temperature: float, top_k: int) -> np.ndarray:
 
 def sample_rows(z: np.ndarray, temperature: float, top_k: int, rng: np.random.Generator,
                 chunk: int = 256) -> np.ndarray:
-    """One token per row of z [R, V] from the row's adjusted distribution."""
+    """One token per row of z [R, V] from the row's adjusted distribution
+    (T = 0: the first largest logit)."""
     R, V = z.shape
+    if temperature == 0.0:
+        return np.argmax(np.asarray(z), axis=1).astype(np.int32)
     out = np.empty(R, dtype=np.int32)
     for s in range(0, R, chunk):
         p = _adjusted(np.asarray(z[s:s + chunk], dtype=np.float64), temperature, top_k)

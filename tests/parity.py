@@ -2,7 +2,9 @@
 
 Bar (per sequence, against the fp64 oracle on the same stored inputs and the
 same Philox streams):
-  * n_accepted and out_tokens equal bit for bit, except
+  * n_accepted and out_tokens equal bit for bit; at temperature 0 (arg-max
+    mode: every decision compares stored logits exactly) without exception,
+    otherwise except
       - from the first judged position j where the oracle's |u_j - ratio_j| <
         1e-5 onward (a knife-edge acceptance; everything after it depends on
         it), and
@@ -121,6 +123,11 @@ def compare(w, seed: int, g: GpuResult, seq_offset: int = 0, rows=None, nthreads
             b = lo + i
             rep.sequences += 1
             _compare_seq(rep, w, b, i, res, g)
+            if w.temperature == 0.0:
+                if g.token_probs is not None and not (np.all(np.isnan(g.token_probs[b])) and
+                                                      np.all(np.isnan(g.accept_ur[b]))):
+                    rep.prob_failures += 1
+                continue
             if check_probs and g.token_probs is not None:
                 n_o, n_g = int(res.n_accepted[i]), int(g.n_accepted[b])
                 if n_o >= 0 and n_g >= 0:
@@ -139,7 +146,8 @@ def _compare_seq(rep: Report, w, b: int, i: int, res, g: GpuResult):
             rep.mismatch_examples.append(("invalid-flag", b, n_o, n_g))
         return
     judged = min(n_o + 1, gamma)
-    edge = [j for j in range(judged) if abs(res.u[i, j] - res.ratio[i, j]) < KNIFE]
+    exact = w.temperature == 0.0
+    edge = [] if exact else [j for j in range(judged) if abs(res.u[i, j] - res.ratio[i, j]) < KNIFE]
     if edge:
         j0 = edge[0]
         rep.exempt_accept += 1
@@ -158,7 +166,7 @@ def _compare_seq(rep: Report, w, b: int, i: int, res, g: GpuResult):
         rep.mismatch_examples.append(("prefix", b))
         return
     if res.out_tokens[i, n_o] != g.out_tokens[b, n_o]:
-        if res.gap[i] < KNIFE:
+        if res.gap[i] < KNIFE and not exact:
             rep.exempt_token += 1
         else:
             rep.mismatches += 1

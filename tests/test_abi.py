@@ -54,6 +54,8 @@ def test_workspace_bytes(L):
     assert b >= 256 * 16 * 50 * 8
     # top-k off when K <= 0 or K >= V
     assert S.workspace_bytes(8, 3, 32000, 0, 0) == S.workspace_bytes(8, 3, 32000, 32000, 0)
+    # the arg-max mode's chunk keys fit: B * (gamma + 1) * 8 bytes at least
+    assert S.workspace_bytes(4096, 64, 2, 50, 0) >= 4096 * 65 * 8
 
 
 def test_launch_names(L):
@@ -68,6 +70,12 @@ def test_launch_names(L):
     assert S.launch_names(256, 8, 152064, 1, 50) == ["k_topk_step"] * 5
     assert S.launch_names(16, 1, 152064, 1, 50) == ["k_topk_step"] * 2
     assert S.launch_names(4, 3, 152064, 1, 300) == ["k_topk_step"] * 4
+    # the arg-max mode (T = 0): windows [0,1), [1,2), [2,4), [4,5) of target
+    # rows 0..gamma, then the judgement of the last window; top-k changes nothing
+    assert S.launch_names(1024, 4, 50257, 0, 0, 0.0) == ["k_greedy_step"] * 5
+    assert S.launch_names(1024, 4, 50257, 0, 50, 0.0) == ["k_greedy_step"] * 5
+    assert S.launch_names(3, 64, 100, 1, 0, 0.0) == ["k_greedy_step"] * 9
+    assert S.launch_names(3, 1, 100, 1, 0, 0.0) == ["k_greedy_step"] * 3
 
 
 def _call(L, **over):
@@ -84,7 +92,7 @@ def _call(L, **over):
 @pytest.mark.parametrize("over", [
     dict(target=None), dict(draft=None), dict(tokens=None), dict(out=None), dict(n=None), dict(ws=None),
     dict(B=0), dict(B=-3), dict(gamma=0), dict(gamma=65), dict(V=1), dict(V=(1 << 28) + 1),
-    dict(dtype=2), dict(T=0.0), dict(T=-1.0), dict(T=float("nan")), dict(T=float("inf")),
+    dict(dtype=2), dict(T=-1e-30), dict(T=-1.0), dict(T=float("nan")), dict(T=float("inf")),
     dict(wsb=16), dict(target=0x100002), dict(dtype=1, draft=0x200001), dict(tokens=0x300002),
     dict(ws=0x600010),
 ], ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))

@@ -243,3 +243,105 @@ def test_non_default_stream():
     s.synchronize()
     g = PT.GpuResult(out.cpu().numpy(), n.cpu().numpy())
     _check(PT.compare(w, 9, g, check_probs=False), "stream")
+
+
+# ---------------------------------------------------------------------------
+# Arg-max mode (temperature 0): exact, no knife-edges
+# ---------------------------------------------------------------------------
+GREEDY = [("g2", 8), ("g4b", 96), ("g2", None), ("g4b", None)]
+
+
+@pytest.mark.parametrize("name,B", GREEDY, ids=[f"{n}-B{b or 'full'}" for n, b in GREEDY])
+def test_greedy_parity(name, B):
+    """Every sequence equals the oracle bit for bit (full size: the benchmark's
+    launch geometry); the seed changes nothing; the debug outputs are NaN."""
+    w = I.make(name, B=B)
+    _say(f"case greedy {name} B={w.B} gamma={w.gamma} V={w.V} dtype={w.spec.dtype}")
+    tensors = PT.to_device(w)
+    g = PT.run_gpu(w, 5, tensors=tensors)
+    _check(PT.compare(w, 5, g), f"greedy {name}")
+    g2 = PT.run_gpu(w, 6, tensors=tensors, debug=False)
+    assert np.array_equal(g.out_tokens, g2.out_tokens) and np.array_equal(g.n_accepted, g2.n_accepted)
+    n = g.n_accepted
+    _say(f"{name}: mean accepted {n.mean():.3f}, all-kept {np.mean(n == w.gamma):.3f}")
+
+
+def _greedy_edges():
+    rng = np.random.default_rng(321)
+    out = []
+
+    def argmax_tokens(t, frac):
+        a = np.argmax(I.logits_f32(t)[:, :-1], axis=2)
+        r = rng.integers(0, t.shape[2], a.shape)
+        return np.where(rng.random(a.shape) < frac, a, r).astype(np.int32)
+
+    # heavy ties (integer logits), both dtypes, drafts mostly the target's choice
+    t = rng.integers(-3, 4, (24, 5, 700)).astype(np.float32)
+    d = rng.integers(-3, 4, (24, 4, 700)).astype(np.float32)
+    tok = argmax_tokens(t, 0.85)
+    out.append(("ties", I.from_arrays(t, d, tok, temperature=0.0)))
+    out.append(("ties-bf16", I.from_arrays(I.f32_to_bf16_bits(t), I.f32_to_bf16_bits(d), tok, temperature=0.0)))
+    # signed zeros: -0 and +0 are equal, the first of them wins
+    t = np.zeros((6, 3, 300), np.float32)
+    t[:, :, ::3] = -0.0
+    t[3:, :, 0] = -1.0
+    tok = np.array([[0, 0], [0, 1], [1, 0], [1, 1], [1, 2], [2, 1]], np.int32)
+    out.append(("signed-zero", I.from_arrays(t, t[:, :2].copy(), tok, temperature=0.0)))
+    # -inf entries (masked vocabulary) and a single finite entry
+    t = rng.normal(0, 2, (8, 4, 333)).astype(np.float32)
+    t[:, :, 10:300] = -np.inf
+    t[:4, 1, :] = -np.inf
+    t[:4, 1, 200] = 5.0
+    out.append(("neg-inf", I.from_arrays(t, t[:, :3].copy(), argmax_tokens(t, 0.9), temperature=0.0)))
+    # gamma = 64 (eight windows) with long accepted prefixes
+    t = rng.normal(0, 1, (5, 65, 100)).astype(np.float32)
+    out.append(("gamma64", I.from_arrays(t, t[:, :64].copy(), argmax_tokens(t, 0.97), temperature=0.0)))
+    # V = 2, gamma = 1
+    t = rng.normal(0, 1, (40, 2, 2)).astype(np.float32)
+    out.append(("V2", I.from_arrays(t, t[:, :1].copy(), argmax_tokens(t, 0.5), temperature=0.0)))
+    # bf16 with odd V: rows start at every 2-byte offset of a 16-byte block
+    t = rng.normal(0, 3, (9, 4, 4099)).astype(np.float32)
+    tb = I.f32_to_bf16_bits(t)
+    out.append(("bf16-oddV", I.from_arrays(tb, tb[:, :3].copy(), argmax_tokens(tb, 0.7), temperature=0.0)))
+    # the maximum at the first and at the last entry of a row
+    t = rng.normal(0, 1, (4, 3, 5003)).astype(np.float32)
+    t[:2, :, 0] = 9.0
+    t[2:, :, -1] = 9.0
+    out.append(("ends", I.from_arrays(t, t[:, :2].copy(), argmax_tokens(t, 0.8), temperature=0.0)))
+    # top-k given: changes nothing in the arg-max mode
+    t = rng.normal(0, 2, (16, 4, 2000)).astype(np.float32)
+    out.append(("topk-ignored", I.from_arrays(t, t[:, :3].copy(), argmax_tokens(t, 0.8), temperature=0.0,
+                                              top_k=5)))
+    return out
+
+
+GREEDY_EDGES = _greedy_edges()
+
+
+@pytest.mark.parametrize("name,w", GREEDY_EDGES, ids=[e[0] for e in GREEDY_EDGES])
+def test_greedy_edge_cases(name, w):
+    _say(f"case greedy edge {name} B={w.B} gamma={w.gamma} V={w.V} dtype={w.target.dtype}")
+    g = PT.run_gpu(w, 11)
+    _check(PT.compare(w, 11, g), f"greedy edge {name}")
+
+
+def test_greedy_invalid_tokens_and_workspace_reuse():
+    """Invalid drafts flag their sequence; one dirty workspace serves greedy,
+    sampling and top-k calls in turn."""
+    import torch
+    import rejection_sampling_verify_17_amd as S
+    ws = torch.full((S.workspace_bytes(256, 8, 152064, 50, S.SV_BF16) + (1 << 20),), 0x5A, dtype=torch.uint8,
+                    device="cuda")
+    w = I.make("g4b", B=64)
+    tok = w.tokens.copy()
+    tok[3, 2] = w.V
+    tok[7, 0] = -1
+    wi = I.from_arrays(w.target, w.draft, tok, temperature=0.0)
+    for name, wk in (("g4b-invalid", wi), ("c3", I.make("c3", B=4)), ("g2", I.make("g2", B=6)),
+                     ("c1", I.make("c1")), ("g4b-invalid", wi)):
+        tgt, drf, tk = PT.to_device(wk)
+        out, n = S.verify(tgt, drf, tk, wk.temperature, wk.top_k, seed=2, workspace=ws)
+        torch.cuda.synchronize()
+        g = PT.GpuResult(out.cpu().numpy(), n.cpu().numpy())
+        _check(PT.compare(wk, 2, g, check_probs=False), f"reuse {name}")
+    assert g.n_accepted[3] == -1 and g.n_accepted[7] == -1 and np.all(g.out_tokens[3] == -1)
