@@ -243,11 +243,14 @@ __device__ __forceinline__ void fold_vecs(float &R, float &S, const float (&z)[U
 }
 
 // Partial statistics of draft row j and target row j over vectors [v0, v1);
-// the chunk whose vectors hold the drafted token also records its two logits
-// (loaded up front by thread 0, so the load overlaps the stream).  Each
-// iteration loads U vectors of each row and folds them 8 entries at a time;
-// entries outside the row or the chunk (only in edge iterations) are masked
-// to -inf first.
+// the chunk whose vectors hold the drafted token also records its two logits.
+// Each step loads U vectors of each row and folds them 8 entries at a time;
+// entries outside the row or the chunk (only in edge steps) are masked to
+// -inf first.  The drafted token and its logits are loaded only after the
+// first step's vectors: vector loads complete in order, so loading them
+// first would hold the wave back by two memory round trips before its stream
+// starts.  The token index is a scalar load (counted apart from vector loads),
+// waited for only where it is first used.
 template <int DT>
 __device__ float4 chunk_stats(const Args &a, int b, int j, int v0, int v1) {
   constexpr int NE = Elem<DT>::kVec;
@@ -257,16 +260,14 @@ __device__ float4 chunk_stats(const Args &a, int b, int j, int v0, int v1) {
   const Row<DT> Q(target_row<DT>(a, b, j), a.V);
   const int V = a.V;
   const float c = a.c;
-  const int t = a.tokens[(size_t)b * a.gamma + j];
-  const bool tv = t >= 0 && t < V;
-  const bool capp = tv && threadIdx.x == 0 && (t + P.s) / NE >= v0 && (t + P.s) / NE < v1;
-  const bool capq = tv && threadIdx.x == 0 && (t + Q.s) / NE >= v0 && (t + Q.s) / NE < v1;
-  const float zpt = capp ? P.load_one(t) : 0.0f;
-  const float zqt = capq ? Q.load_one(t) : 0.0f;
   // vectors [ilo, ihi) hold no entry outside the row in either row
   const int ilo = (max(P.s, Q.s) + NE - 1) / NE;
   const int ihi = min((V + P.s) / NE, (V + Q.s) / NE);
   float Rp = -INFINITY, Sp = 0.0f, Rq = -INFINITY, Sq = 0.0f;
+  const int t = a.tokens[(size_t)b * a.gamma + j];  // b, j uniform: a scalar load
+  bool capp = false, capq = false;
+  float zpt = 0.0f, zqt = 0.0f;
+  bool first = true;
   for (int base = v0 + (int)threadIdx.x; base < v1; base += kThreads * U) {
     float zp[U][NE], zq[U][NE];
 #pragma unroll
@@ -274,6 +275,14 @@ __device__ float4 chunk_stats(const Args &a, int b, int j, int v0, int v1) {
       const int iv = base + u * kThreads;
       P.load_vec(iv, zp[u]);  // past the row: zeros or neighbours, masked below
       Q.load_vec(iv, zq[u]);
+    }
+    if (first) {
+      first = false;
+      const bool tv = t >= 0 && t < V;
+      capp = tv && threadIdx.x == 0 && (t + P.s) / NE >= v0 && (t + P.s) / NE < v1;
+      capq = tv && threadIdx.x == 0 && (t + Q.s) / NE >= v0 && (t + Q.s) / NE < v1;
+      if (capp) zpt = P.load_one(t);
+      if (capq) zqt = Q.load_one(t);
     }
     const int top = base + (U - 1) * kThreads;
     const bool edge = base < ilo || top >= ihi || top >= v1;
