@@ -25,6 +25,7 @@ F32 = 0
 BF16 = 1
 ACCEPT = 0
 SAMPLE = 1
+DRAFT = 2
 
 
 def build(force: bool = True, src: str = SRC, out: str = LIB) -> str:
@@ -69,6 +70,8 @@ def load(path: str) -> ctypes.CDLL:
     L.svo_verify.restype = i32
     L.svo_token_probs.argtypes = [vp, vp, vp, i32, i32, i32, i32, flt, i32, i32, vp, vp]
     L.svo_token_probs.restype = i32
+    L.svo_draft_sample.argtypes = [vp, i32, i32, i32, i32, flt, i32, u64, u64, i32, vp, vp]
+    L.svo_draft_sample.restype = i32
     L.svo_max_threads.argtypes = []
     L.svo_max_threads.restype = i32
     return L
@@ -226,6 +229,21 @@ def token_probs(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray, tempe
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return pt, qt
+
+
+def draft_sample(draft: np.ndarray, temperature: float, top_k: int = 0, seed: int = 0, seq_offset: int = 0,
+                 nthreads: int = 0):
+    """Draft tokens [B, gamma] drawn from each draft row's adjusted distribution
+    on the DRAFT stream, and the key gap of each draw [B, gamma]."""
+    draft = np.ascontiguousarray(draft)
+    B, gamma, V = draft.shape
+    tok = np.zeros((B, gamma), dtype=np.int32)
+    gap = np.zeros((B, gamma), dtype=np.float64)
+    rc = lib().svo_draft_sample(_ptr(draft), B, gamma, V, _dtype_code(draft), temperature, top_k, seed,
+                                seq_offset, nthreads, _ptr(tok), _ptr(gap))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return tok, gap
 
 
 def max_threads() -> int:

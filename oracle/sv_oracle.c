@@ -68,6 +68,7 @@
 /* Purposes of a Philox stream (the fourth counter word). */
 #define SVO_ACCEPT 0u
 #define SVO_SAMPLE 1u
+#define SVO_DRAFT 2u
 
 /* ------------------------------------------------------------------------ */
 /* [PHX] Philox4x32-10.                                                      */
@@ -241,19 +242,26 @@ int svo_residual(const double *q, const double *p, int V, double *r)
  * w[v] > 0 of ln w[v] - ln E_v, E_v the exponential variate of the SAMPLE
  * stream at (seed, seq, pos, v).  *gap receives best key - second-best key
  * (+inf with a single candidate).  Returns -1 when no weight is positive. */
-int32_t svo_gumbel_sample(const double *w, int V, uint64_t seed, uint64_t seq, uint32_t pos,
-                          double *gap)
+static int32_t svo_gumbel_draw(const double *w, int V, uint64_t seed, uint64_t seq, uint32_t pos,
+                               uint32_t purpose, double *gap)
 {
     int32_t best = -1;
     double k1 = -INFINITY, k2 = -INFINITY;
     for (int v = 0; v < V; ++v) {
         if (!(w[v] > 0.0)) continue;
-        double key = log(w[v]) - log(svo_exponential(svo_word(seed, seq, pos, (uint32_t)v, SVO_SAMPLE)));
+        double key = log(w[v]) - log(svo_exponential(svo_word(seed, seq, pos, (uint32_t)v, purpose)));
         if (key > k1) { k2 = k1; k1 = key; best = v; }
         else if (key > k2) { k2 = key; }
     }
     if (gap) *gap = k1 - k2;
     return best;
+}
+
+/* The verification's draws use the SAMPLE stream. */
+int32_t svo_gumbel_sample(const double *w, int V, uint64_t seed, uint64_t seq, uint32_t pos,
+                          double *gap)
+{
+    return svo_gumbel_draw(w, V, seed, seq, pos, SVO_SAMPLE, gap);
 }
 
 /* n draws from the same weights at sequences seq0 .. seq0+n-1 (position pos):
@@ -357,6 +365,45 @@ int svo_verify(const void *target, const void *draft, const int32_t *tokens,
             if (diag_gap) diag_gap[b] = gap;
         }
         free(q); free(p); free(r); free(keep);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Draft tokens: the draft model's own sampling step, which [SDE] "how it     */
+/* works" puts before verification (the small model proposes gamma tokens).  */
+/* Token j of sequence b is drawn from the draft row's adjusted distribution  */
+/* p_j (R1, R2, R9) by the same Gumbel-max as R4 on the DRAFT stream          */
+/* (purpose 2) at (seq = seq_offset + b, pos = j).  gap [B][gamma] (may be    */
+/* NULL): best minus second-best key of the row.                              */
+/* ------------------------------------------------------------------------ */
+int svo_draft_sample(const void *draft, int B, int gamma, int V, int dtype, float temperature, int top_k,
+                     uint64_t seed, uint64_t seq_offset, int nthreads, int32_t *tokens, double *gap)
+{
+    if (!draft || !tokens || B < 1 || gamma < 1 || V < 2) return -1;
+    if (dtype != SVO_F32 && dtype != SVO_BF16) return -1;
+    if (!(temperature >= 0.0f) || !isfinite(temperature)) return -1;
+    const size_t esz = dtype == SVO_BF16 ? 2 : 4;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double *p = (double *)malloc(sizeof(double) * (size_t)V);
+        unsigned char *keep = (unsigned char *)malloc((size_t)V);
+#pragma omp for schedule(dynamic, 1) collapse(2)
+        for (int b = 0; b < B; ++b)
+            for (int j = 0; j < gamma; ++j) {
+                const char *prow = (const char *)draft + ((size_t)b * gamma + j) * V * esz;
+                svo_row_probs(prow, dtype, V, temperature, top_k, p, keep);
+                double g = INFINITY;
+                tokens[(size_t)b * gamma + j] =
+                    svo_gumbel_draw(p, V, seed, seq_offset + (uint64_t)b, (uint32_t)j, SVO_DRAFT, &g);
+                if (gap) gap[(size_t)b * gamma + j] = g;
+            }
+        free(p); free(keep);
     }
     return 0;
 }

@@ -409,3 +409,40 @@ def check_greedy(seed: int = 31):
     g0 = O.verify(zq, zp, tok, 0.0, 0, seed=5)
     gs = O.verify(zq, zp, tok, 1e-3, 0, seed=5)
     assert np.array_equal(g0.out_tokens, gs.out_tokens) and np.array_equal(g0.n_accepted, gs.n_accepted)
+
+
+# ---------------------------------------------------------------------------
+# Draft sampler (the draft's own step before verification, DRAFT stream)
+# ---------------------------------------------------------------------------
+def check_draft_sampler(n: int = 200_000, seed: int = 41):
+    """Tokens follow the draft row's adjusted distribution (chi-square, with T
+    and top-k; never outside the kept set); T = 0 gives the first largest
+    logit; the DRAFT stream is not the SAMPLE stream; seq_offset shifts the
+    streams like the sequence index."""
+    rng = np.random.default_rng(seed)
+    V = 64
+    z = rng.normal(0, 2, V).astype(np.float32)
+    for T, K in ((1.0, 0), (0.7, 5), (1.3, 40)):
+        rows = np.broadcast_to(z, (n, 1, V)).copy()
+        tok, gap = O.draft_sample(rows, T, K, seed=seed + 1)
+        p = O.row_probs(z, T, K)
+        counts = np.bincount(tok[:, 0], minlength=V)
+        assert np.all(counts[p == 0] == 0), (T, K)
+        pv = chi2_pvalue(counts, p)
+        assert pv > 1e-6, f"draft sampler T={T} K={K}: chi2 p = {pv}"
+        assert np.all(gap > 0)
+    # T = 0: the first largest logit, whatever the seed
+    zi = rng.integers(-3, 4, (50, 3, 30)).astype(np.float32)
+    tok0, _ = O.draft_sample(zi, 0.0, 0, seed=5)
+    assert np.array_equal(tok0, np.argmax(zi, axis=2))
+    # the DRAFT stream differs from the SAMPLE stream at the same (seq, pos):
+    # on a uniform row each stream's draw is its own arg-max of -ln E
+    flat = np.zeros((2000, 1, V), np.float32)
+    dtok, _ = O.draft_sample(flat, 1.0, 0, seed=9)
+    stok = O.gumbel_sample_many(np.full(V, 1.0), seed=9, seq0=0, n=2000, pos=0)
+    assert np.mean(dtok[:, 0] == stok) < 0.05
+    # seq_offset: sequence b at offset o is sequence b + o at offset 0
+    rows = rng.normal(0, 1, (12, 2, V)).astype(np.float32)
+    full, _ = O.draft_sample(rows, 1.0, 0, seed=3)
+    part, _ = O.draft_sample(rows[5:], 1.0, 0, seed=3, seq_offset=5)
+    assert np.array_equal(full[5:], part)

@@ -31,6 +31,11 @@ MUTANTS = [
     ("token the target never emits is accepted",
      "if (!(q_t > 0.0)) return 0;", "if (!(q_t > 0.0)) return 1;", ["enumeration", "special"]),
     ("Philox key bump skipped", "k0 += PHX_W0;", "k0 += 0;", ["philox"]),
+    ("draft tokens drawn on the SAMPLE stream",
+     "svo_gumbel_draw(p, V, seed, seq_offset + (uint64_t)b, (uint32_t)j, SVO_DRAFT, &g)",
+     "svo_gumbel_draw(p, V, seed, seq_offset + (uint64_t)b, (uint32_t)j, SVO_SAMPLE, &g)", ["draft"]),
+    ("draft row without temperature", "svo_row_probs(prow, dtype, V, temperature, top_k, p, keep);\n                double g",
+     "svo_row_probs(prow, dtype, V, 1.0f, top_k, p, keep);\n                double g", ["draft"]),
     ("arg-max ties keep the larger index",
      "if (svo_logit(row, dtype, v) > svo_logit(row, dtype, best)) best = v;",
      "if (svo_logit(row, dtype, v) >= svo_logit(row, dtype, best)) best = v;", ["greedy"]),
@@ -54,6 +59,8 @@ def _run(check):
         C.check_row_probs_vs_torch()
     elif check == "topk":
         C.check_topk_vs_stable_sort()
+    elif check == "draft":
+        C.check_draft_sampler(n=100_000)
     elif check == "greedy":
         C.check_greedy()
     elif check == "philox":

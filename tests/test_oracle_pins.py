@@ -64,6 +64,11 @@ def test_greedy_mode():
     C.check_greedy()
 
 
+def test_draft_sampler():
+    """Draft tokens for a step ([SDE] "how it works": the draft proposes first)."""
+    C.check_draft_sampler()
+
+
 def test_gumbel_sampler_is_multinomial():
     C.check_gumbel_sampler()
 
