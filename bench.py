@@ -219,6 +219,44 @@ def run_workload(name: str, steps: int, warmup: int, hip: Hip, seed: int = 3000)
 
 
 # ---------------------------------------------------------------------------
+# Draft-token sampling (the step before verification)
+# ---------------------------------------------------------------------------
+def run_draft(name: str, steps: int, warmup: int, hip: Hip, seed: int = 3000) -> dict:
+    """sv_draft_sample over the draft rows of a workload: every row read once,
+    one Philox word and two logarithms per entry (no top-k)."""
+    import torch
+    import rejection_sampling_verify_17_amd as S
+    from rejection_sampling_verify_17_amd import inputs as I
+    w = I.make(name)
+    dev = torch.device("cuda:0")
+    copies = max(2, min(8, int(np.ceil((1 << 30) / w.draft.nbytes))))
+    if w.is_bf16:
+        d0 = torch.from_numpy(w.draft.view(np.int16)).view(torch.bfloat16)
+    else:
+        d0 = torch.from_numpy(w.draft)
+    drfs = [d0.to(dev) for _ in range(copies)]
+    out = torch.empty((w.B, w.gamma), dtype=torch.int32, device=dev)
+    sp = int(torch.cuda.current_stream(dev).cuda_stream)
+    for i in range(warmup):
+        S.draft_sample(drfs[i % copies], w.temperature, w.top_k, seed=seed, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, sp)
+    for i in range(steps):
+        S.draft_sample(drfs[i % copies], w.temperature, w.top_k, seed=seed, out=out)
+    hip.record(e1, sp)
+    hip.sync(e1)
+    us = hip.ms(e0, e1) / steps * 1e3
+    hip.destroy(e0)
+    hip.destroy(e1)
+    rows = w.B * w.gamma
+    nbytes = w.draft.nbytes + 4 * rows
+    return {"workload": f"{name} draft rows", "kernel": "k_draft_sample", "us_per_call": us,
+            "drafted_tokens_per_s": rows / (us * 1e-6), "GBps": nbytes / (us * 1e-6) / 1e9,
+            "entries_per_s": rows * w.V / (us * 1e-6)}
+
+
+# ---------------------------------------------------------------------------
 # Traffic from committed rocprofv3 PMC summaries
 # ---------------------------------------------------------------------------
 def read_traffic(kernel: str, workload: str) -> float | None:
@@ -287,7 +325,7 @@ def _find(d, suffix):
 
 
 def _short(name: str) -> str:
-    for k in ("k_topk_step", "k_greedy_step", "k_rows", "k_judge"):
+    for k in ("k_topk_step", "k_greedy_step", "k_draft_sample", "k_accept_hist", "k_rows", "k_judge"):
         if k in name:
             return k
     return name[:60]
@@ -429,6 +467,10 @@ def main():
             sweep.append({k: r[k] for k in ("workload", "ms_per_step", "positions_per_s", "GBps_step",
                                             "frac_peak_step", "dominant", "dominant_GBps", "kernels",
                                             "mean_accepted", "input_copies")})
+    draft = None
+    if not args.no_sweep:
+        draft = run_draft(HEADLINE, max(10, args.steps // 2), max(3, args.warmup // 2), hip)
+        print(f"# draft sampling {HEADLINE}: {draft['us_per_call']:.1f} us/call", file=sys.stderr, flush=True)
     line = {
         "metric": "verified draft positions/sec (and HBM GB/s, fraction of MI355X peak) at 1 GPU",
         "value": head["positions_per_s"], "unit": "verified draft positions/s", "n_gpus": 1,
@@ -440,7 +482,8 @@ def main():
                    "B": w.B, "gamma": w.gamma, "V": w.V, "parallelism": "single GPU"},
         "GBps_step": head["GBps_step"], "frac_peak_step": head["frac_peak_step"],
         "kernels": head["kernels"], "mean_accepted": head["mean_accepted"],
-        "roofline": roofline, "cpu_baseline": cpu, "sweep": sweep, "source_digest": source_digest(),
+        "roofline": roofline, "cpu_baseline": cpu, "sweep": sweep, "draft_sampling": draft,
+        "source_digest": source_digest(),
     }
     print(json.dumps(line))
 

@@ -140,6 +140,33 @@ SV_API sv_status sv_verify_timed(const void *target_logits, const void *draft_lo
 SV_API const char *sv_launch_name(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
                            int32_t top_k, float temperature, int32_t i);
 
+/* Draft tokens for a verification step: token j of sequence b drawn on the
+ * GPU from the draft row's adjusted distribution p_j = softmax(topk(z) / T)
+ * (the same temperature, top-k and arg-max conventions as sv_verify), the
+ * step the small model takes before the large one verifies (page ai-trend.me,
+ * section "어떻게 작동하나").  The draw is Gumbel-max: the arg-max over the kept
+ * entries of ln p_v - ln E_v, E_v = -ln U_v, U_v = (2 * (w >> 9) + 1) * 2^-24,
+ * w the Philox4x32-10 word at (seq = seq_offset + b, pos = j, v, purpose 2);
+ * ties go to the smaller v.  At temperature 0 the token is the row's first
+ * largest logit.
+ *   draft_logits [B][gamma][V] of dtype `dtype` (device); draft_tokens
+ *   [B][gamma] int32 (device, caller-owned).  No workspace; nothing is
+ *   allocated.  Errors: SV_EINVAL for null pointers, a bad shape or dtype,
+ *   temperature not finite or < 0, misaligned pointers; SV_EHIP for a failed
+ *   launch.  Enqueued on `stream`, never synchronises. */
+SV_API sv_status sv_draft_sample(const void *draft_logits, int32_t B, int32_t gamma, int32_t V, int32_t dtype,
+                          float temperature, int32_t top_k, uint64_t seed, uint64_t seq_offset,
+                          int32_t *draft_tokens, void *stream);
+
+/* Acceptance counts of a step: hist[0] = sequences flagged invalid
+ * (n_accepted < 0; values above gamma, which sv_verify never writes, are
+ * counted there too), hist[1 + i] = sequences with n_accepted = i, i in
+ * [0, gamma].  n_accepted [B] and hist [gamma + 2] are int32 device buffers
+ * (hist caller-owned, fully overwritten).  SV_EINVAL for null or misaligned
+ * pointers, B < 1 or gamma not in [1, 64]; SV_EHIP for a failed launch. */
+SV_API sv_status sv_accept_histogram(const int32_t *n_accepted, int32_t B, int32_t gamma, int32_t *hist,
+                              void *stream);
+
 /* Human-readable status. */
 SV_API const char *sv_status_string(sv_status s);
 

@@ -2,11 +2,12 @@
 
 The C ABI (include/specverify.h) is implemented by libspecverify.so, built
 from csrc/ with hipcc for gfx950; this package is its thin torch binding
-(`verify`, `verify_debug`, `verify_timed`) plus seeded synthetic inputs
-(`inputs`).
+(`verify`, `verify_debug`, `verify_timed`, `draft_sample`,
+`accept_histogram`) plus seeded synthetic inputs (`inputs`).
 """
-from ._binding import (SV_BF16, SV_EHIP, SV_EINVAL, SV_F32, SV_OK, SpecVerifyError, launch_names, lib,
-                       status_string, verify, verify_debug, verify_timed, version, workspace_bytes)
+from ._binding import (SV_BF16, SV_EHIP, SV_EINVAL, SV_F32, SV_OK, SpecVerifyError, accept_histogram,
+                       draft_sample, launch_names, lib, status_string, verify, verify_debug, verify_timed, version,
+                       workspace_bytes)
 
-__all__ = ["verify", "verify_debug", "verify_timed", "workspace_bytes", "launch_names", "lib", "version",
+__all__ = ["verify", "verify_debug", "verify_timed", "draft_sample", "accept_histogram", "workspace_bytes", "launch_names", "lib", "version",
            "status_string", "SpecVerifyError", "SV_F32", "SV_BF16", "SV_OK", "SV_EINVAL", "SV_EHIP"]

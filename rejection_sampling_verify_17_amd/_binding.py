@@ -54,6 +54,10 @@ def lib() -> ctypes.CDLL:
                 L.sv_verify_timed.restype = i32
                 L.sv_launch_name.argtypes = [i32, i32, i32, i32, i32, flt, i32]
                 L.sv_launch_name.restype = ctypes.c_char_p
+                L.sv_draft_sample.argtypes = [vp, i32, i32, i32, i32, flt, i32, u64, u64, vp, vp]
+                L.sv_draft_sample.restype = i32
+                L.sv_accept_histogram.argtypes = [vp, i32, i32, vp, vp]
+                L.sv_accept_histogram.restype = i32
                 L.sv_status_string.argtypes = [i32]
                 L.sv_status_string.restype = ctypes.c_char_p
                 L.sv_version.argtypes = []
@@ -212,3 +216,40 @@ def verify_timed(target, draft, tokens, temperature: float, events, top_k: int =
                   n_accepted, workspace, stream, (ctypes.cast(arr, ctypes.c_void_p), len(events),
                                                   ctypes.addressof(nl)))
     return out, n, nl.value
+
+
+def draft_sample(draft, temperature: float, top_k: int = 0, seed: int = 0, seq_offset: int = 0, out=None,
+                 stream=None):
+    """sv_draft_sample: draft tokens [B, gamma] int32 drawn on the GPU from the
+    draft rows [B, gamma, V] (float32 or bfloat16, contiguous)."""
+    torch = _torch()
+    if not draft.is_cuda or draft.dim() != 3 or not draft.is_contiguous():
+        raise ValueError("draft must be a contiguous [B, gamma, V] GPU tensor")
+    B, gamma, V = draft.shape
+    dt = _dtype_code(draft)
+    dev = draft.device
+    if out is None:
+        out = torch.empty((B, gamma), dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        st = lib().sv_draft_sample(draft.data_ptr(), B, gamma, V, dt, float(temperature), int(top_k),
+                                   int(seed) & 0xFFFFFFFFFFFFFFFF, int(seq_offset) & 0xFFFFFFFFFFFFFFFF,
+                                   out.data_ptr(), _stream_ptr(dev, stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_draft_sample")
+    return out
+
+
+def accept_histogram(n_accepted, gamma: int, out=None, stream=None):
+    """sv_accept_histogram: int32 [gamma + 2] counts (invalid, then n = 0..gamma)."""
+    torch = _torch()
+    if not n_accepted.is_cuda or n_accepted.dtype != torch.int32 or n_accepted.dim() != 1:
+        raise ValueError("n_accepted must be a 1-D int32 GPU tensor")
+    dev = n_accepted.device
+    if out is None:
+        out = torch.empty((gamma + 2,), dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        st = lib().sv_accept_histogram(n_accepted.contiguous().data_ptr(), n_accepted.shape[0], int(gamma),
+                                       out.data_ptr(), _stream_ptr(dev, stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_accept_histogram")
+    return out

@@ -9,6 +9,7 @@
 #include <cstring>
 
 #include "specverify.h"
+#include "sv_draft.h"
 #include "sv_greedy.h"
 #include "sv_kernels.h"
 #include "sv_topk.h"
@@ -336,6 +337,45 @@ const char *sv_launch_name(int32_t B, int32_t gamma, int32_t V, int32_t dtype, i
   if (i == 0) return "k_rows";
   if (i == 1) return "k_judge";
   return i < 2 + rows_after ? "k_rows" : nullptr;
+}
+
+sv_status sv_draft_sample(const void *draft_logits, int32_t B, int32_t gamma, int32_t V, int32_t dtype,
+                          float temperature, int32_t top_k, uint64_t seed, uint64_t seq_offset, int32_t *draft_tokens,
+                          void *stream) {
+  if (!draft_logits || !draft_tokens) return SV_EINVAL;
+  if (!shape_ok(B, gamma, V, dtype)) return SV_EINVAL;
+  if (!std::isfinite(temperature) || !(temperature >= 0.0f)) return SV_EINVAL;
+  const uintptr_t elem = dtype == SV_BF16 ? 2 : 4;
+  if (((uintptr_t)draft_logits % elem) || ((uintptr_t)draft_tokens % 4)) return SV_EINVAL;
+  if ((long long)B * gamma > 0x7FFFFFFFLL) return SV_EINVAL;
+  const bool argmax = temperature == 0.0f;
+  Args a{};
+  a.draft = draft_logits;
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.top_k = (!argmax && top_k > 0 && top_k < V) ? top_k : 0;
+  a.c = argmax ? 0.0f : (float)(1.4426950408889634 / (double)temperature);
+  a.argmax = argmax ? 1 : 0;
+  a.key0 = (uint32_t)seed;
+  a.key1 = (uint32_t)(seed >> 32);
+  a.seq_offset = seq_offset;
+  a.ngb = (V + (int)(16 / elem) - 1) / (int)(16 / elem);
+  a.drafted = draft_tokens;
+  (void)hipGetLastError();
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 grid((unsigned)(B * gamma));
+  if (dtype == SV_BF16) hipLaunchKernelGGL(k_draft_sample<DT_BF16>, grid, dim3(kTopkThreads), 0, s, a);
+  else hipLaunchKernelGGL(k_draft_sample<DT_F32>, grid, dim3(kTopkThreads), 0, s, a);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+sv_status sv_accept_histogram(const int32_t *n_accepted, int32_t B, int32_t gamma, int32_t *hist, void *stream) {
+  if (!n_accepted || !hist || B < 1 || gamma < 1 || gamma > kMaxGamma) return SV_EINVAL;
+  if (((uintptr_t)n_accepted % 4) || ((uintptr_t)hist % 4)) return SV_EINVAL;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_accept_hist, dim3(1), dim3(256), 0, (hipStream_t)stream, n_accepted, B, gamma, hist);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }
 
 const char *sv_status_string(sv_status s) {

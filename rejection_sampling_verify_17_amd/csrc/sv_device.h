@@ -16,7 +16,7 @@ constexpr int kWave = 64;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 enum { DT_F32 = 0, DT_BF16 = 1 };
-enum { PURPOSE_ACCEPT = 0u, PURPOSE_SAMPLE = 1u };
+enum { PURPOSE_ACCEPT = 0u, PURPOSE_SAMPLE = 1u, PURPOSE_DRAFT = 2u };
 
 // ---------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy

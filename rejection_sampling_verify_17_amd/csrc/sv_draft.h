@@ -1,0 +1,110 @@
+// The two ends of a speculative step around verification: drawing the draft
+// tokens, and counting how many of them a step kept.
+//
+// Page "추측 디코딩: 큰 모델을 빠르게 돌리는 법" (ai-trend.me), section "어떻게
+// 작동하나": the small model first proposes gamma tokens, each drawn from its
+// own adjusted distribution (temperature, top-k, arg-max), and only then does
+// the large model verify them.
+//
+// k_draft_sample: one block per draft row (b, j).  Token j of sequence b is
+// drawn from p_j = softmax(topk(z) / T) by Gumbel-max on Philox words of
+// purpose 2 (DRAFT) at (seq = seq_offset + b, pos = j, v): the arg-max over the
+// kept entries of z_v c - log2 E2_v, which orders like ln p_v - ln E_v
+// (E2 = E / ln 2, the exponential variate in base 2); ties go to the smaller
+// index.  Without top-k every entry is kept and the row is read once, in
+// groups of four entries that share one Philox block; with top-k the exact
+// K-th largest key comes from the top-k path's select and only the kept
+// entries draw variates.  T = 0 (arg-max mode): the first largest logit.
+//
+// k_accept_hist: one block counts n_accepted into gamma + 2 bins.
+#pragma once
+
+#include "sv_topk.h"
+
+namespace sv {
+
+// Gumbel-max over group blocks [g0, g1) of a row (every entry kept): key
+// z c - log2 E2 with words of `ps`.  Each thread walks its entries in
+// increasing index with a strict comparison (smaller index among equal keys).
+template <int DT, int NT>
+__device__ __forceinline__ unsigned long long gumbel_dense_row(const Row<DT> &R, int V, float c,
+                                                             const PhiloxStream &ps, int g0, int g1) {
+  constexpr int NE = Elem<DT>::kVec;
+  float bestk = -INFINITY;
+  uint32_t besti = 0xFFFFFFFFu;  // none
+  for (int gb = g0 + (int)threadIdx.x; gb < g1; gb += NT) {
+    float z[NE];
+    R.load_block(gb, z);  // entries NE gb .. NE gb + NE - 1; past the row: masked below
+#pragma unroll
+    for (int g = 0; g < NE / 4; ++g) {
+      const uint32_t group = (uint32_t)(gb * (NE / 4) + g);
+      const Philox4 blk = ps.block(group);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t idx = group * 4u + (uint32_t)e;
+        const float key = fmaf(z[g * 4 + e], c, -__builtin_amdgcn_logf(exp2_variate(blk.w[e])));
+        const bool take = idx < (uint32_t)V && key > bestk;
+        bestk = take ? key : bestk;
+        besti = take ? idx : besti;
+      }
+    }
+  }
+  return besti == 0xFFFFFFFFu ? 0ull : pack_key(bestk, besti);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kTopkThreads) void k_draft_sample(Args a) {
+  __shared__ TopkShared sh;
+  const int row = blockIdx.x;  // b * gamma + j
+  const int b = row / a.gamma, j = row - b * a.gamma;
+  if (b >= a.B) return;  // never taken: the grid is B * gamma
+  const Row<DT> P(draft_row<DT>(a, b, j), a.V);
+  const StreamRow<DT> src(P, a.V);
+  const uint32_t seq = seq_of(a, b);
+  unsigned long long best = 0ull;
+  if (a.argmax) {
+    // arg-max mode: the first largest logit
+    src.for_each([&](float z, int v) {
+      const unsigned long long k = entry_key(z == 0.0f ? 0.0f : z, (uint32_t)v);  // -0 counts as +0
+      best = k > best ? k : best;
+    });
+  } else if (a.top_k > 0) {
+    const Selected sel = select_threshold(sh, src, a.top_k);
+    auto consider = [&](float z, uint32_t v) {
+      if (z == -INFINITY || entry_key(z, v) < sel.thr) return;
+      const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)j, v >> 2, PURPOSE_DRAFT);
+      const float E = exp2_variate(word_of(blk, v & 3u));
+      const unsigned long long k = pack_key(fmaf(z, a.c, -__builtin_amdgcn_logf(E)), v);
+      best = k > best ? k : best;
+    };
+    if (sel.in_lds) {
+      for (unsigned int i = threadIdx.x; i < sel.ncand; i += kTopkThreads) {
+        const unsigned long long key = sh.cand[i];
+        consider(from_orderable((uint32_t)(key >> 32)), 0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
+      }
+    } else {
+      src.for_each([&](float z, int v) { consider(z, (uint32_t)v); });
+    }
+  } else {
+    const PhiloxStream ps(a.key0, a.key1, seq, (uint32_t)j, PURPOSE_DRAFT);
+    best = gumbel_dense_row<DT, kTopkThreads>(P, a.V, a.c, ps, 0, a.ngb);
+  }
+  best = block_max_u64_sh<kTopkThreads>(best, sh.red_u);
+  if (threadIdx.x == 0) a.drafted[row] = best == 0ull ? 0 : (int32_t)packed_index(best);
+}
+
+// Counts of n_accepted: hist[0] sequences flagged invalid (n < 0, or n >
+// gamma, which no call writes), hist[1 + i] sequences with n = i.
+__global__ __launch_bounds__(256) void k_accept_hist(const int32_t *n, int B, int gamma, int32_t *hist) {
+  __shared__ int cnt[66];  // gamma <= 64
+  for (int i = threadIdx.x; i < gamma + 2; i += 256) cnt[i] = 0;
+  __syncthreads();
+  for (int b = threadIdx.x; b < B; b += 256) {
+    const int v = n[b];
+    atomicAdd(&cnt[(v < 0 || v > gamma) ? 0 : v + 1], 1);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < gamma + 2; i += 256) hist[i] = cnt[i];
+}
+
+}  // namespace sv

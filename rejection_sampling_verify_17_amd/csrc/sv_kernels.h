@@ -90,6 +90,9 @@ struct Args {
   // arg-max mode (temperature 0)
   unsigned long long *gpart;  // [B][gamma+1][gstride] packed arg-max key per chunk
   int32_t gstride;            // chunks per row at most
+  // draft sampling
+  int32_t *drafted;           // [B][gamma] drawn draft tokens
+  int32_t argmax;             // 1: temperature 0 (the first largest logit)
 };
 
 __device__ __forceinline__ uint32_t seq_of(const Args &a, int b) {

@@ -24,7 +24,8 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     names = declared_symbols()
-    for required in ("sv_verify", "sv_workspace_bytes", "sv_verify_debug", "sv_status_string"):
+    for required in ("sv_verify", "sv_workspace_bytes", "sv_verify_debug", "sv_status_string", "sv_draft_sample",
+                     "sv_accept_histogram"):
         assert required in names
 
 
@@ -109,3 +110,25 @@ def test_product_path_does_not_touch_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 for needle in ("from oracle", "import oracle", "sv_oracle", "svo_"):
                     assert needle not in text, f"{f} mentions {needle}"
+
+
+@pytest.mark.parametrize("over", [
+    dict(draft=None), dict(out=None), dict(B=0), dict(gamma=0), dict(gamma=65), dict(V=1), dict(dtype=3),
+    dict(T=-1.0), dict(T=float("nan")), dict(T=float("inf")), dict(draft=0x200002), dict(out=0x400002),
+    dict(dtype=1, draft=0x200001),
+], ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_draft_sample_invalid_arguments(L, over):
+    args = dict(draft=0x200000, B=4, gamma=3, V=1000, dtype=0, T=1.0, K=0, seed=1, off=0, out=0x400000,
+                stream=None)
+    args.update(over)
+    assert L.sv_draft_sample(args["draft"], args["B"], args["gamma"], args["V"], args["dtype"], args["T"],
+                             args["K"], args["seed"], args["off"], args["out"], args["stream"]) == 1
+
+
+@pytest.mark.parametrize("over", [dict(n=None), dict(h=None), dict(B=0), dict(gamma=0), dict(gamma=65),
+                                  dict(n=0x100002), dict(h=0x200002)],
+                         ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_accept_histogram_invalid_arguments(L, over):
+    args = dict(n=0x100000, B=8, gamma=4, h=0x200000, stream=None)
+    args.update(over)
+    assert L.sv_accept_histogram(args["n"], args["B"], args["gamma"], args["h"], args["stream"]) == 1
