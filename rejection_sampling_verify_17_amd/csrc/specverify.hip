@@ -134,9 +134,10 @@ size_t workspace_total(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32
 
 template <int DT>
 struct Launches {
-  // Dense: k_rows for the first window, k_judge, then k_rows per further
-  // window and once more to sample.  Top-k: position 0, the other positions,
-  // then the judgement and draw.
+  // Dense: k_rows for the first window, k_rows that judges it in every block
+  // and reads the next window, then k_rows per further window and once more
+  // to sample.  Top-k: position 0, the other positions, then the judgement
+  // and draw.  Arg-max: windows of target rows, then the judgement.
   static sv_status run(const Args &a, const Plan &p, hipStream_t stream, void *const *events, int n_events,
                        int *n_launches) {
     int li = 0;
@@ -169,18 +170,35 @@ struct Launches {
       auto grid = [&](long long items) { return (unsigned)std::max(1LL, std::min<long long>(slots, items)); };
       int w0 = std::min(a.gamma, p.window);
       before();
-      hipLaunchKernelGGL((k_rows<DT, true>), dim3(grid((long long)a.B * w0 * p.nch)), dim3(kThreads), 0, stream, a, 0, 0,
-                         w0);
+      hipLaunchKernelGGL((k_rows<DT, 0>), dim3(grid((long long)a.B * w0 * p.nch)), dim3(kThreads), 0, stream, a, 0, 0,
+                         w0, 0, 0, 0);
       ok = ok && after();
-      before();
-      hipLaunchKernelGGL(k_judge<DT>, dim3((a.B + kJudgeWaves - 1) / kJudgeWaves), dim3(kJudgeWaves * kWave), 0,
-                         stream, a, w0);
-      ok = ok && after();
+      // Every position read at once: each block of launch 1 judges its
+      // sequence itself, then draws its chunk of the sampled row (saves a
+      // launch).  Otherwise k_judge judges the first window and lists the
+      // work of launch 1: a judgement in every block would hold back the
+      // statistics stream of the next window, which costs more than the
+      // launch.
+      const bool judge_in_block = w0 == a.gamma;
+      if (!judge_in_block) {
+        before();
+        hipLaunchKernelGGL(k_judge<DT>, dim3((a.B + kJudgeWaves - 1) / kJudgeWaves), dim3(kJudgeWaves * kWave), 0,
+                           stream, a, w0);
+        ok = ok && after();
+      }
       for (int launch = 1;; ++launch) {
         const int w1 = std::min(a.gamma, w0 + p.window);
         before();
-        const long long items = (long long)a.B * std::max((w1 - w0) * p.nch_max, p.cs_max);
-        hipLaunchKernelGGL((k_rows<DT, false>), dim3(grid(items)), dim3(kThreads), 0, stream, a, launch, w0, w1);
+        if (launch == 1 && judge_in_block) {
+          // kb blocks per sequence, each judges, then draws one chunk
+          const int cs1 = std::max(1, std::min(p.cs_max, slots / a.B));
+          hipLaunchKernelGGL((k_rows<DT, 1>), dim3((unsigned)((long long)a.B * cs1)), dim3(kThreads), 0, stream, a,
+                             1, w0, w1, cs1, 0, cs1);
+        } else {
+          const long long items = (long long)a.B * std::max((w1 - w0) * p.nch_max, p.cs_max);
+          hipLaunchKernelGGL((k_rows<DT, 2>), dim3(grid(items)), dim3(kThreads), 0, stream, a, launch, w0, w1, 0, 0,
+                             0);
+        }
         ok = ok && after();
         if (w0 == a.gamma) break;
         w0 = w1;
@@ -331,9 +349,10 @@ const char *sv_launch_name(int32_t B, int32_t gamma, int32_t V, int32_t dtype, i
     }
     return i < launches ? "k_topk_step" : nullptr;
   }
-  // k_rows (first window), k_judge, then one k_rows per further window and
-  // one to sample after the last
+  // k_rows for the first window, k_judge unless that window holds every
+  // position, then one k_rows per further window and one to sample
   const int rows_after = (gamma + p.window - 1) / p.window;
+  if (p.window >= gamma) return i < 2 ? "k_rows" : nullptr;
   if (i == 0) return "k_rows";
   if (i == 1) return "k_judge";
   return i < 2 + rows_after ? "k_rows" : nullptr;

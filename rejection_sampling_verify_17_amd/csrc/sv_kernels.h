@@ -8,22 +8,25 @@
 //   k_rows (launch 0)  statistics of rows 0..w1-1 of every sequence: partial
 //                      base-2 softmax statistics (R, S) of each draft and
 //                      target row, one vocabulary chunk per work item, and the
-//                      two logits at the drafted token.
-//   k_judge            one wave per sequence judges that first window (lane l
-//                      merges row pair l's partials, evaluates q(t)/p(t) in
-//                      registers and draws u; a ballot finds the first
-//                      rejection), writes the outputs and puts the sequence
-//                      on a list for the next launch: statistics of the next
-//                      window, or sampling (the residual max(0, q - p) of the
-//                      rejected row, or the bonus row gamma).
+//                      two logits at the drafted token; clears the counters of
+//                      the launches to come.
+//   k_rows (launch 1)  a fixed number of blocks per sequence; wave 0 of each
+//                      judges that first window (lane l merges row pair l's
+//                      partials, evaluates q(t)/p(t) in registers and draws u;
+//                      a ballot finds the first rejection; one block writes
+//                      the outputs), then the block takes its share of what
+//                      the judgement leaves: a statistics chunk of the next
+//                      window, or a chunk of the sampled row (the residual
+//                      max(0, q - p) of the rejected row, or the bonus row
+//                      gamma).
 //   k_rows (launch i)  a grid sized to the chip walks the two lists, sampling
 //                      items (Gumbel-max winner over one chunk of a row,
 //                      VALU-bound) first, then statistics items of window i
 //                      (memory-bound), so both kinds share every compute unit.
-//                      The block that finishes a sequence's last statistics
-//                      item judges the window at once and appends the sequence
-//                      to the lists of launch i+1; the block that finishes a
-//                      sampled row's last chunk writes the token.
+//   From launch 1 on, the block that finishes a sequence's last statistics
+//   item judges the window at once and appends the sequence to the lists of
+//   the next launch; the block that finishes a sampled row's last chunk
+//   writes the token.
 //
 // Blocks of one launch talk only through per-sequence counters: an item's
 // results are written with stores that bypass the (per-die, mutually
@@ -392,8 +395,8 @@ __device__ __forceinline__ int pow2_at_least(int x) {
 }
 
 template <int DT>
-__device__ void judge_window(const Args &a, int b, int lane, int p0, int w0, int nch, bool first, int &mode,
-                             int &row, float4 &st) {
+__device__ void judge_window(const Args &a, int b, int lane, int p0, int w0, int nch, bool first, bool write,
+                             int &mode, int &row, float4 &st) {
   const int gamma = a.gamma;
   const int nj = w0 - p0;
   mode = -1;
@@ -437,10 +440,10 @@ __device__ void judge_window(const Args &a, int b, int lane, int p0, int w0, int
     }
   }
   if (first) {
+    // (launch 0 has filled the diagnostics with NaN)
     const bool ok = __ballot(lane < gamma && (tok < 0 || tok >= a.V)) == 0ull;
-    for (int k = lane; k < gamma; k += kWave) write_diag(a, b, k, NAN, NAN, NAN, NAN);
     if (!ok) {
-      write_invalid(a, b, lane);
+      if (write) write_invalid(a, b, lane);
       return;
     }
   }
@@ -450,7 +453,7 @@ __device__ void judge_window(const Args &a, int b, int lane, int p0, int w0, int
   if (act) jr = judge_one(a, seq_of(a, b), jpos, zp, zq, zp == -INFINITY, zq == -INFINITY, Rp, Sp, Rq, Sq);
   const unsigned long long mask = __ballot(act && jr.accept);
   const int k = (mask == ~0ull) ? kWave : __builtin_ctzll(~mask);  // first clear bit
-  if (act && lane <= k) write_diag(a, b, jpos, jr.pt, jr.qt, jr.u, jr.ratio);
+  if (write && act && lane <= k) write_diag(a, b, jpos, jr.pt, jr.qt, jr.u, jr.ratio);
   int n;
   if (k < nj) {
     n = p0 + k;
@@ -464,6 +467,7 @@ __device__ void judge_window(const Args &a, int b, int lane, int p0, int w0, int
     return;
   }
   row = n;
+  if (!write) return;
   // outputs: the accepted prefix, -1 after the sampled slot n (written by
   // the block that finishes the sampled row)
   int32_t *out = a.out_tokens + (size_t)b * (gamma + 1);
@@ -498,27 +502,19 @@ __device__ __forceinline__ void append(const Args &a, int li, int mode, int b, i
   }
 }
 
-// First judgement (window [0, w0) of every sequence, measured by launch 0):
-// one wave per sequence.  Also clears the per-sequence counters of the
-// launches to come and the list set launch 1 appends to.  A block reserves
-// its list slots with one atomic per list.
+// First judgement (window [0, w0) of every sequence, measured by launch 0)
+// when a statistics window follows: one wave per sequence; the sequence goes
+// on a list of set 1 for launch 1.  A block reserves its list slots with one
+// atomic per list.
 template <int DT>
 __global__ __launch_bounds__(kJudgeWaves *kWave) void k_judge(Args a, int w0) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int b = blockIdx.x * kJudgeWaves + wave;
   __shared__ int sh_mode[kJudgeWaves], sh_row[kJudgeWaves];
   __shared__ float4 sh_st[kJudgeWaves];
-  if (blockIdx.x == 0 && threadIdx.x < 2) a.lcnt[2 * list_set(2) + threadIdx.x] = 0;
   int mode = -1, row = 0;
   float4 st = make_float4(0.f, 1.f, 0.f, 1.f);
-  if (b < a.B) {
-    if (lane == 0) {
-      a.icnt[b] = 0;
-      a.pcnt[b] = 0;
-      a.pbest[b] = 0ull;
-    }
-    judge_window<DT>(a, b, lane, 0, w0, a.nch, true, mode, row, st);
-  }
+  if (b < a.B) judge_window<DT>(a, b, lane, 0, w0, a.nch, true, true, mode, row, st);
   if (lane == 0) {
     sh_mode[wave] = mode;
     sh_row[wave] = row;
@@ -559,50 +555,111 @@ __device__ __forceinline__ float uni(float x) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
 }
 
-// Launch 0: statistics of rows [w0, w1) of every sequence (judged by
-// k_judge).  Launch i >= 1: the lists of set i: sampling items, then
-// statistics items of rows [w0, w1) (none when w0 = w1).  A block takes its
-// items in rounds of up to kQueue; each item's result goes out at once
-// (partial statistics by coherent store, chunk winner kept in LDS), and at the
-// end of a round the block finishes all its items together: winners folded
-// into the row's best key, per-sequence counters advanced, and for every
-// sequence whose window or sampled row it completed, the judgement (window)
-// or the token (row).
-template <int DT, bool FIRST>
-__global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int launch, int w0, int w1) {
+// Launch 0 (MODE 0): statistics of rows [w0, w1) of every sequence; also
+// clears the per-sequence counters of the launches to come.  When launch 0
+// read every position (w0 = gamma), launch 1 runs in MODE 1: kb blocks per
+// sequence; wave 0 of each judges the sequence (one block writes the
+// outputs), then the block draws chunk `slot` of the sampled row (cs1
+// chunks); kb = cs1 and nch1 = 0 then, though the code also takes statistics
+// chunks of rows [w0, w1) (nch1 per row).  Otherwise k_judge judges the first
+// window and every later launch runs in MODE 2: the lists of set i: sampling
+// items, then statistics items of rows [w0, w1) (none when w0 = w1).  A block takes its items in rounds of
+// up to kQueue; each item's result goes out at once (partial statistics by
+// coherent store, chunk winner kept in LDS), and at the end of a round the
+// block finishes all its items together: winners folded into the row's best
+// key, per-sequence counters advanced, and for every sequence whose window or
+// sampled row it completed, the judgement (window) or the token (row).
+template <int DT, int MODE>
+__global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int launch, int w0, int w1, int kb, int nch1,
+                                                     int cs1) {
   constexpr int kQueue = 64;
   __shared__ int sh_nq;
   __shared__ int q_b[kQueue], q_row[kQueue];  // row >= 0: sampled row; -1: statistics item
   __shared__ int q_fin[kQueue];               // 1: finished the sequence's window or row
   __shared__ unsigned long long q_w[kQueue];  // chunk winner, then the row's best key
+  __shared__ int sh_mode, sh_row;
+  __shared__ float4 sh_st;
   const int li = list_set(launch);
+  // launch 0 clears the sets k_judge (1) and launch 1 (2) append to; launch
+  // i >= 1 the set launch i + 1 appends to
+  if (blockIdx.x == 0 && threadIdx.x < (MODE == 0 ? 4 : 2))
+    a.lcnt[2 * list_set(launch + (MODE == 0 ? 1 : 2)) + threadIdx.x] = 0;
+  if (threadIdx.x == 0) sh_nq = 0;
+  const int dw = w1 - w0;
+  int nch, cs, per_stat;
+  if (MODE == 1) {
+    // one item per block, after the block's own judgement of window [0, w0)
+    nch = nch1;
+    cs = cs1;
+    per_stat = dw * nch;
+    const int b = blockIdx.x / kb, slot = blockIdx.x - b * kb;
+    if (threadIdx.x < kWave) {
+      int mode = -1, row = 0;
+      float4 st = make_float4(0.f, 1.f, 0.f, 1.f);
+      if (b < a.B) judge_window<DT>(a, b, threadIdx.x, 0, w0, a.nch, true, slot == 0, mode, row, st);
+      if (threadIdx.x == 0) {
+        sh_mode = mode;
+        sh_row = row;
+        sh_st = st;
+      }
+    }
+    __syncthreads();
+    const int mode = sh_mode, row = sh_row;
+    if (mode == 0 && slot < per_stat) {
+      const int r = slot / nch, ch = slot - r * nch;
+      const int j = w0 + r;
+      const int cv = (a.nvec + nch - 1) / nch;
+      const int v0 = ch * cv;
+      const float4 pst = chunk_stats<DT>(a, b, j, v0, min(a.nvec, v0 + cv));
+      if (threadIdx.x == 0) {
+        store_coherent(a.part + ((size_t)b * a.gamma + j) * a.nch_max + ch, pst);
+        sh_nq = 1;
+        q_b[0] = b;
+        q_row[0] = -1;
+      }
+    } else if (mode >= 1 && slot < cs) {
+      const int gper = (a.ngb + cs - 1) / cs;
+      const int g0 = slot * gper, g1 = min(a.ngb, g0 + gper);
+      const float4 st = make_float4(uni(sh_st.x), uni(sh_st.y), uni(sh_st.z), uni(sh_st.w));
+      const unsigned long long w = mode == 2
+          ? chunk_winner<DT, false>(a, b, row, make_float4(0.f, 1.f, 0.f, 1.f), g0, g1)
+          : chunk_winner<DT, true>(a, b, row, st, g0, g1);
+      if (threadIdx.x == 0) {
+        sh_nq = 1;
+        q_b[0] = b;
+        q_row[0] = row;
+        q_w[0] = w;
+      }
+    }
+  }
+  // Chunks per row in later launches: the grid is shared between the row
+  // pairs to read (statistics) and the rows to sample, the same number of
+  // blocks per row pair for both kinds, so that every block takes one item and
+  // all finish about together (sampling chunks are capped: past a few per
+  // row, more blocks only add fixed costs).
   int n_samp = 0, n_stat = a.B;
-  if (!FIRST) {
+  if (MODE == 2) {
     n_samp = min(max(uni(a.lcnt[2 * li]), 0), a.B);
     n_stat = min(max(uni(a.lcnt[2 * li + 1]), 0), a.B);
+    const int G = (int)gridDim.x;
+    const int rows = n_stat * dw;
+    const int per_pair = max(1, G / max(1, rows + n_samp));
+    nch = min(a.nch_max, per_pair);
+    cs = n_samp > 0 ? max(1, min(a.cs_max, (G - rows * nch) / n_samp)) : 1;
+    per_stat = dw * nch;
+  } else if (MODE == 0) {
+    nch = a.nch;  // fixed: the first judgement reads these chunks
+    cs = 1;
+    per_stat = dw * nch;
   }
-  if (blockIdx.x == 0 && threadIdx.x < 2) a.lcnt[2 * list_set(launch + (FIRST ? 1 : 2)) + threadIdx.x] = 0;
-  // Chunks per row: fixed in launch 0 (k_judge reads them).  Later launches
-  // share the grid between the row pairs to read (statistics) and the rows to
-  // sample, the same number of blocks per row pair for both kinds, so that
-  // every block takes one item and all finish about together (sampling chunks
-  // are capped: past a few per row, more blocks only add fixed costs).
-  const int G = (int)gridDim.x;
-  const int dw = w1 - w0;
-  const int rows = n_stat * dw;
-  const int per_pair = max(1, G / max(1, rows + n_samp));
-  const int nch = FIRST ? a.nch : min(a.nch_max, per_pair);
-  const int cs = n_samp > 0 ? max(1, min(a.cs_max, (G - rows * nch) / n_samp)) : 1;
-  const long long s_items = (long long)n_samp * cs;
-  const int cv = (a.nvec + nch - 1) / nch;
-  const int per_stat = dw * nch;
-  const long long total = s_items + (long long)n_stat * per_stat;
+  const long long s_items = MODE == 2 ? (long long)n_samp * cs : 0;
+  const long long total = MODE == 1 ? 0 : s_items + (long long)n_stat * per_stat;
   const long long round = (long long)kQueue * gridDim.x;
-  if (threadIdx.x == 0) sh_nq = 0;
-  for (long long k0 = blockIdx.x; k0 < total; k0 += round) {
+  // (a MODE 1 block passes once, with no item to take, to finish the one it has)
+  for (long long k0 = blockIdx.x; k0 < total || (MODE == 1 && k0 == (long long)blockIdx.x); k0 += round) {
     const long long kend = min(total, k0 + round);
     for (long long k = k0; k < kend; k += gridDim.x) {
-      if (!FIRST && k < s_items) {
+      if (MODE == 2 && k < s_items) {
         const int l = (int)(k / cs);
         const int ch = (int)(k - (long long)l * cs);
         const int2 e = a.slist[(size_t)li * a.B + l];
@@ -628,14 +685,23 @@ __global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int launch, int w0
         const int l = (int)(k2 / per_stat);
         const int rc = (int)(k2 - (long long)l * per_stat);
         const int r = rc / nch, ch = rc - r * nch;
-        const int b = FIRST ? l : uni(a.tlist[(size_t)li * a.B + l]);
+        const int b = MODE == 0 ? l : uni(a.tlist[(size_t)li * a.B + l]);
         if ((unsigned)b >= (unsigned)a.B) continue;  // never taken: entries come from append()
         const int j = w0 + r;
+        if (MODE == 0 && r == 0 && ch == 0 && threadIdx.x == 0) {
+          // counters of the launches to come (read there after this launch
+          // ends), and diagnostics NaN for every position until one is judged
+          a.icnt[b] = 0;
+          a.pcnt[b] = 0;
+          a.pbest[b] = 0ull;
+          for (int k = 0; k < a.gamma; ++k) write_diag(a, b, k, NAN, NAN, NAN, NAN);
+        }
+        const int cv = (a.nvec + nch - 1) / nch;
         const int v0 = ch * cv;
         const float4 pst = chunk_stats<DT>(a, b, j, v0, min(a.nvec, v0 + cv));
         if (threadIdx.x == 0) {
           store_coherent(a.part + ((size_t)b * a.gamma + j) * a.nch_max + ch, pst);
-          if (!FIRST) {
+          if (MODE == 2) {
             const int q = sh_nq++;
             q_b[q] = b;
             q_row[q] = -1;
@@ -643,7 +709,7 @@ __global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int launch, int w0
         }
       }
     }
-    if (FIRST) continue;
+    if (MODE == 0) continue;
     // finish the round's items, one thread each
     __syncthreads();
     const int nq = sh_nq;
@@ -673,7 +739,7 @@ __global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int launch, int w0
       const int b = q_b[q];
       int mode, row;
       float4 st;
-      judge_window<DT>(a, b, threadIdx.x % kWave, w0, w1, nch, false, mode, row, st);
+      judge_window<DT>(a, b, threadIdx.x % kWave, w0, w1, nch, false, true, mode, row, st);
       if (threadIdx.x % kWave == 0) {
         // every item of this window is counted: the counter starts over for the next
         if (mode == 0) __hip_atomic_store(a.icnt + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -61,8 +61,9 @@ def test_workspace_bytes(L):
 
 def test_launch_names(L):
     import rejection_sampling_verify_17_amd as S
-    # small inputs: statistics of every row, the judgement, the sampling
-    assert S.launch_names(64, 5, 128256, 1, 0) == ["k_rows", "k_judge", "k_rows"]
+    # small inputs: statistics of every row, then the judgement (in every
+    # block) and the sampling
+    assert S.launch_names(64, 5, 128256, 1, 0) == ["k_rows", "k_rows"]
     # large inputs: statistics of position 0 and its judgement, then one launch
     # per further position (each judges its position in place) and one to sample
     assert S.launch_names(1024, 4, 50257, 0, 0) == ["k_rows", "k_judge"] + ["k_rows"] * 4
