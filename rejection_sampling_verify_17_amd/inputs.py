@@ -226,3 +226,27 @@ def from_arrays(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray,
                 temperature, top_k, 0.0, 0.0, 0.0, False, -1, -1)
     return Workload(spec, np.ascontiguousarray(target), np.ascontiguousarray(draft),
                     np.ascontiguousarray(tokens, dtype=np.int32))
+
+
+# ---------------------------------------------------------------------------
+# Token-dependent rows: a first-order Markov "model" pair
+# ---------------------------------------------------------------------------
+@dataclass
+class MarkovPair:
+    """Logit tables of a target and a draft model whose next-token logits
+    depend on the previous token only: row x of `target` ([V, V] float32) is
+    the target's logits after token x, row x of `draft` the draft's."""
+    target: np.ndarray
+    draft: np.ndarray
+
+    @property
+    def V(self):
+        return self.target.shape[0]
+
+
+def markov_pair(V: int = 64, target_sigma: float = 3.0, draft_sigma: float = 1.0, seed: int = 1077) -> MarkovPair:
+    """Target table N(0, target_sigma^2); draft table = target + N(0, draft_sigma^2)."""
+    rng = np.random.default_rng(seed)
+    t = (rng.standard_normal((V, V), dtype=np.float32) * np.float32(target_sigma)).astype(np.float32)
+    d = (t + rng.standard_normal((V, V), dtype=np.float32) * np.float32(draft_sigma)).astype(np.float32)
+    return MarkovPair(t, d)
