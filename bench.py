@@ -362,11 +362,12 @@ def rocprof_summary(args) -> None:
     wl = args.workload
     out = []
     out.append(f"# rocprofv3 kernel trace, workload {wl}")
+    extra = "--draft-only" if args.draft_only else "--no-cpu --no-sweep"
     out.append(f"command: rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace -o run -- "
-               f"python3 bench.py --workload {wl} --steps {args.steps} --warmup {args.warmup} --no-cpu --no-sweep")
+               f"python3 bench.py --workload {wl} --steps {args.steps} --warmup {args.warmup} {extra}")
     out.append(f"source_digest: {source_digest()}")
     out += kernel_stats_summary(os.path.join(d, "trace"))
-    with open(os.path.join(d, f"kernel_trace_{wl}.txt"), "w") as f:
+    with open(os.path.join(d, f"kernel_trace_{wl}{'_draft' if args.draft_only else ''}.txt"), "w") as f:
         f.write("\n".join(out) + "\n")
     print("\n".join(out))
     fetch = counter_means(os.path.join(d, "fetch"))
@@ -394,7 +395,7 @@ def rocprof_summary(args) -> None:
         hbm = v * 1024.0 * ff + wkib * 1024.0 * wf
         lines = [f"# HBM traffic of {k}, workload {wl}",
                  f"command: rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch -o run -- python3 bench.py "
-                 f"--workload {wl} --steps {args.steps} --warmup {args.warmup} --no-cpu --no-sweep ; the same with "
+                 f"--workload {wl} --steps {args.steps} --warmup {args.warmup} {extra} ; the same with "
                  f"--pmc WRITE_SIZE ; and both counters on: python3 bench.py --copy-calib-mb {args.copy_calib_mb}",
                  f"source_digest: {source_digest()}",
                  f"dispatches: {n}",
@@ -421,6 +422,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration) and exit")
+    ap.add_argument("--draft-only", action="store_true",
+                    help="only time draft-token sampling on the workload's draft rows and print its JSON")
     ap.add_argument("--rocprof-summary", metavar="DIR", default=None,
                     help="summarise rocprofv3 CSV output under DIR (see rocprof_summary) and exit")
     args = ap.parse_args()
@@ -446,6 +449,9 @@ def main():
     import rejection_sampling_verify_17_amd as S
     S.lib()
     hip = Hip()
+    if args.draft_only:
+        print(json.dumps(run_draft(args.workload, args.steps, args.warmup, hip)))
+        return
     print(f"# bench {args.workload}: steps {args.steps} warmup {args.warmup}", file=sys.stderr, flush=True)
     head, w = run_workload(args.workload, args.steps, args.warmup, hip)
     print(f"# {args.workload}: {head['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
