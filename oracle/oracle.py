@@ -55,6 +55,8 @@ def load(path: str) -> ctypes.CDLL:
     L.svo_exponential.restype = dbl
     L.svo_row_probs.argtypes = [vp, i32, i32, flt, i32, vp, vp]
     L.svo_row_probs.restype = None
+    L.svo_row_probs_p.argtypes = [vp, i32, i32, flt, i32, flt, vp, vp, vp]
+    L.svo_row_probs_p.restype = None
     L.svo_accept.argtypes = [dbl, dbl, dbl]
     L.svo_accept.restype = i32
     L.svo_accept_count.argtypes = [dbl, dbl]
@@ -65,10 +67,10 @@ def load(path: str) -> ctypes.CDLL:
     L.svo_gumbel_sample.restype = i32
     L.svo_gumbel_sample_many.argtypes = [vp, i32, u64, u64, i32, u32, vp]
     L.svo_gumbel_sample_many.restype = None
-    L.svo_verify.argtypes = [vp, vp, vp, i32, i32, i32, i32, flt, i32, u64, u64, i32,
-                             vp, vp, vp, vp, vp, vp]
+    L.svo_verify.argtypes = [vp, vp, vp, i32, i32, i32, i32, flt, i32, flt, u64, u64, i32,
+                             vp, vp, vp, vp, vp, vp, vp]
     L.svo_verify.restype = i32
-    L.svo_token_probs.argtypes = [vp, vp, vp, i32, i32, i32, i32, flt, i32, i32, vp, vp]
+    L.svo_token_probs.argtypes = [vp, vp, vp, i32, i32, i32, i32, flt, i32, flt, i32, vp, vp]
     L.svo_token_probs.restype = i32
     L.svo_draft_sample.argtypes = [vp, i32, i32, i32, i32, flt, i32, u64, u64, i32, vp, vp]
     L.svo_draft_sample.restype = i32
@@ -137,12 +139,22 @@ def exponential(w: int) -> float:
 # --------------------------------------------------------------------------
 # Rows and rule pieces
 # --------------------------------------------------------------------------
-def row_probs(row: np.ndarray, temperature: float, top_k: int = 0) -> np.ndarray:
+def row_probs(row: np.ndarray, temperature: float, top_k: int = 0, top_p: float = 1.0) -> np.ndarray:
     row = np.ascontiguousarray(row)
     out = np.zeros(row.shape[-1], dtype=np.float64)
-    lib().svo_row_probs(_ptr(row), _dtype_code(row), row.shape[-1], temperature, top_k,
-                        _ptr(out), None)
+    lib().svo_row_probs_p(_ptr(row), _dtype_code(row), row.shape[-1], temperature, top_k, top_p,
+                          _ptr(out), None, None)
     return out
+
+
+def nucleus_margin(row: np.ndarray, temperature: float, top_k: int, top_p: float) -> float:
+    """How far the row's nucleus cut lies from flipping (+inf without a cut)."""
+    row = np.ascontiguousarray(row)
+    out = np.zeros(row.shape[-1], dtype=np.float64)
+    m = np.zeros(1, dtype=np.float64)
+    lib().svo_row_probs_p(_ptr(row), _dtype_code(row), row.shape[-1], temperature, top_k, top_p,
+                          _ptr(out), None, _ptr(m))
+    return float(m[0])
 
 
 def accept(u: float, p_t: float, q_t: float) -> bool:
@@ -186,10 +198,12 @@ class OracleResult:
     ratio: np.ndarray        # [B, gamma] q(t)/p(t)            (NaN after the first rejection)
     gap: np.ndarray          # [B] best - second-best key of the sampled row
     flags: np.ndarray        # [B] bit 0: empty residual, q sampled instead
+    margin: np.ndarray       # [B] smallest nucleus-cut margin over the rows used (+inf without top-p)
 
 
 def verify(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray, temperature: float,
-           top_k: int = 0, seed: int = 0, seq_offset: int = 0, nthreads: int = 0) -> OracleResult:
+           top_k: int = 0, seed: int = 0, seq_offset: int = 0, nthreads: int = 0,
+           top_p: float = 1.0) -> OracleResult:
     """Oracle verification step.  target [B, gamma+1, V], draft [B, gamma, V]
     (float32, or uint16 holding bf16 bits), tokens [B, gamma] int32."""
     target = np.ascontiguousarray(target)
@@ -205,16 +219,17 @@ def verify(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray, temperatur
     ratio = np.zeros((B, gamma), dtype=np.float64)
     gap = np.zeros(B, dtype=np.float64)
     flags = np.zeros(B, dtype=np.int32)
+    margin = np.zeros(B, dtype=np.float64)
     rc = lib().svo_verify(_ptr(target), _ptr(draft), _ptr(tokens), B, gamma, V,
-                          _dtype_code(target), temperature, top_k, seed, seq_offset, nthreads,
-                          _ptr(out), _ptr(n), _ptr(u), _ptr(ratio), _ptr(gap), _ptr(flags))
+                          _dtype_code(target), temperature, top_k, top_p, seed, seq_offset, nthreads,
+                          _ptr(out), _ptr(n), _ptr(u), _ptr(ratio), _ptr(gap), _ptr(flags), _ptr(margin))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
-    return OracleResult(out, n, u, ratio, gap, flags)
+    return OracleResult(out, n, u, ratio, gap, flags, margin)
 
 
 def token_probs(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray, temperature: float,
-                top_k: int = 0, nthreads: int = 0):
+                top_k: int = 0, nthreads: int = 0, top_p: float = 1.0):
     """(p_j(t_j), q_j(t_j)) for every draft position, each [B, gamma] float64."""
     target = np.ascontiguousarray(target)
     draft = np.ascontiguousarray(draft)
@@ -224,7 +239,7 @@ def token_probs(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray, tempe
     pt = np.zeros((B, gamma), dtype=np.float64)
     qt = np.zeros((B, gamma), dtype=np.float64)
     rc = lib().svo_token_probs(_ptr(target), _ptr(draft), _ptr(tokens), B, gamma, V,
-                               _dtype_code(target), temperature, top_k, nthreads,
+                               _dtype_code(target), temperature, top_k, top_p, nthreads,
                                _ptr(pt), _ptr(qt))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")

@@ -45,6 +45,12 @@
  *  R7  output slots after the committed token hold -1.
  *  R8  a drafted token outside [0, V) marks the whole sequence invalid:
  *      n_accepted = -1 and the output row is all -1.
+ *  R10 top-p (nucleus, [SDE] "how it works" lists it among the adjusted
+ *      distributions): after temperature and top-k, walk the kept entries in
+ *      the R2 order (larger logit first, smaller index among equal logits)
+ *      and keep them until their probability mass reaches P (the entry that
+ *      reaches it is kept); renormalise.  top_p <= 0 or >= 1: off.  Applied
+ *      to every row of p and q, as R1.
  *  R9  temperature 0 is the arg-max mode of [SDE] "how it works": each
  *      distribution is the point mass on the row's largest logit (the
  *      smaller index among equal logits, as R5), and the rule is applied to
@@ -171,10 +177,15 @@ static void svo_topk_keep(const void *row, int dtype, int V, int top_k, unsigned
 
 /* prob[v] = softmax over kept entries of z/T (R1, R2); dropped entries get 0.
  * T = 0 is the arg-max mode (R9): the point mass on the largest logit, the
- * smaller index among equal logits.  scratch_keep holds V bytes. */
-void svo_row_probs(const void *row, int dtype, int V, float temperature, int top_k,
-                   double *prob, unsigned char *scratch_keep)
+ * smaller index among equal logits.  0 < top_p < 1 applies the nucleus cut
+ * of R10 after top-k; *margin (may be NULL) receives how far the cut lies
+ * from flipping: min(C_m - P, P - C_{m-1}), C_i the cumulative mass of the
+ * first i + 1 entries in the R2 order and m the last kept one (+inf without
+ * a cut).  scratch_keep holds V bytes. */
+void svo_row_probs_p(const void *row, int dtype, int V, float temperature, int top_k, float top_p,
+                     double *prob, unsigned char *scratch_keep, double *margin)
 {
+    if (margin) *margin = INFINITY;
     if (temperature == 0.0f) {
         int32_t best = 0;
         for (int v = 1; v < V; ++v)
@@ -200,6 +211,35 @@ void svo_row_probs(const void *row, int dtype, int V, float temperature, int top
     }
     for (int v = 0; v < V; ++v) prob[v] /= S;
     free(own);
+    if (top_p > 0.0f && top_p < 1.0f) {
+        /* R10: walk the kept entries from the largest logit down (the R2
+         * order) and keep them until their mass reaches P; renormalise. */
+        const double P = (double)top_p;
+        int n = 0;
+        for (int v = 0; v < V; ++v) n += prob[v] > 0.0;
+        svo_entry *e = (svo_entry *)malloc(sizeof(svo_entry) * (size_t)(n > 0 ? n : 1));
+        n = 0;
+        for (int v = 0; v < V; ++v)
+            if (prob[v] > 0.0) { e[n].z = svo_logit(row, dtype, v); e[n].v = v; ++n; }
+        qsort(e, (size_t)n, sizeof(svo_entry), svo_entry_cmp);
+        double cum = 0.0, before = 0.0;
+        int m = n - 1;
+        for (int i = 0; i < n; ++i) {
+            before = cum;
+            cum += prob[e[i].v];
+            if (cum >= P) { m = i; break; }
+        }
+        if (margin) *margin = fmin(cum - P, P - before);
+        for (int i = m + 1; i < n; ++i) prob[e[i].v] = 0.0;
+        for (int v = 0; v < V; ++v) prob[v] /= cum;
+        free(e);
+    }
+}
+
+void svo_row_probs(const void *row, int dtype, int V, float temperature, int top_k,
+                   double *prob, unsigned char *scratch_keep)
+{
+    svo_row_probs_p(row, dtype, V, temperature, top_k, 1.0f, prob, scratch_keep, NULL);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -287,10 +327,11 @@ void svo_gumbel_sample_many(const double *w, int V, uint64_t seed, uint64_t seq0
 /* Returns 0, or -1 on arguments the rule is not defined for.                */
 /* ------------------------------------------------------------------------ */
 int svo_verify(const void *target, const void *draft, const int32_t *tokens,
-               int B, int gamma, int V, int dtype, float temperature, int top_k,
+               int B, int gamma, int V, int dtype, float temperature, int top_k, float top_p,
                uint64_t seed, uint64_t seq_offset, int nthreads,
                int32_t *out_tokens, int32_t *n_accepted,
-               double *diag_u, double *diag_ratio, double *diag_gap, int32_t *diag_flags)
+               double *diag_u, double *diag_ratio, double *diag_gap, int32_t *diag_flags,
+               double *diag_margin)
 {
     if (!target || !draft || !tokens || !out_tokens || !n_accepted) return -1;
     if (B < 1 || gamma < 1 || V < 2 || (dtype != SVO_F32 && dtype != SVO_BF16)) return -1;
@@ -318,10 +359,12 @@ int svo_verify(const void *target, const void *draft, const int32_t *tokens,
             if (diag_ratio) for (int j = 0; j < gamma; ++j) diag_ratio[(size_t)b * gamma + j] = NAN;
             if (diag_gap) diag_gap[b] = NAN;
             if (diag_flags) diag_flags[b] = 0;
+            double margin = INFINITY, mg;
 
             int valid = 1;
             for (int j = 0; j < gamma; ++j)
                 if (tok[j] < 0 || tok[j] >= V) valid = 0;
+            if (diag_margin) diag_margin[b] = INFINITY;
             if (!valid) {                                   /* R8 */
                 n_accepted[b] = -1;
                 for (int i = 0; i <= gamma; ++i) out[i] = -1;
@@ -333,8 +376,10 @@ int svo_verify(const void *target, const void *draft, const int32_t *tokens,
             for (int j = 0; j < gamma; ++j) {
                 const char *qrow = (const char *)target + ((size_t)b * (gamma + 1) + j) * V * esz;
                 const char *prow = (const char *)draft + ((size_t)b * gamma + j) * V * esz;
-                svo_row_probs(qrow, dtype, V, temperature, top_k, q, keep);
-                svo_row_probs(prow, dtype, V, temperature, top_k, p, keep);
+                svo_row_probs_p(qrow, dtype, V, temperature, top_k, top_p, q, keep, &mg);
+                margin = fmin(margin, mg);
+                svo_row_probs_p(prow, dtype, V, temperature, top_k, top_p, p, keep, &mg);
+                margin = fmin(margin, mg);
                 const int t = tok[j];
                 const double u = svo_uniform_accept(svo_word(seed, seq, (uint32_t)j, 0u, SVO_ACCEPT));
                 const double ratio = p[t] > 0.0 ? q[t] / p[t] : INFINITY;
@@ -353,7 +398,8 @@ int svo_verify(const void *target, const void *draft, const int32_t *tokens,
             } else {
                 /* All gamma kept: one more token from target row gamma. */
                 const char *qrow = (const char *)target + ((size_t)b * (gamma + 1) + gamma) * V * esz;
-                svo_row_probs(qrow, dtype, V, temperature, top_k, q, keep);
+                svo_row_probs_p(qrow, dtype, V, temperature, top_k, top_p, q, keep, &mg);
+                margin = fmin(margin, mg);
                 sampled = svo_gumbel_sample(q, V, seed, seq, (uint32_t)gamma, &gap);
             }
 
@@ -363,6 +409,7 @@ int svo_verify(const void *target, const void *draft, const int32_t *tokens,
             for (int i = n + 1; i <= gamma; ++i) out[i] = -1;
             n_accepted[b] = n;
             if (diag_gap) diag_gap[b] = gap;
+            if (diag_margin) diag_margin[b] = margin;
         }
         free(q); free(p); free(r); free(keep);
     }
@@ -411,7 +458,7 @@ int svo_draft_sample(const void *draft, int B, int gamma, int V, int dtype, floa
 /* p_j(t_j) and q_j(t_j) for every draft position (not only the judged ones):
  * pt, qt are [B][gamma].  Used to compare probabilities, not by the rule. */
 int svo_token_probs(const void *target, const void *draft, const int32_t *tokens,
-                    int B, int gamma, int V, int dtype, float temperature, int top_k,
+                    int B, int gamma, int V, int dtype, float temperature, int top_k, float top_p,
                     int nthreads, double *pt, double *qt)
 {
     if (B < 1 || gamma < 1 || V < 2 || !(temperature >= 0.0f)) return -1;
@@ -436,9 +483,9 @@ int svo_token_probs(const void *target, const void *draft, const int32_t *tokens
                     qt[(size_t)b * gamma + j] = NAN;
                     continue;
                 }
-                svo_row_probs(qrow, dtype, V, temperature, top_k, row, keep);
+                svo_row_probs_p(qrow, dtype, V, temperature, top_k, top_p, row, keep, NULL);
                 qt[(size_t)b * gamma + j] = row[t];
-                svo_row_probs(prow, dtype, V, temperature, top_k, row, keep);
+                svo_row_probs_p(prow, dtype, V, temperature, top_k, top_p, row, keep, NULL);
                 pt[(size_t)b * gamma + j] = row[t];
             }
         free(row); free(keep);

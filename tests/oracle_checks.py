@@ -74,7 +74,7 @@ def tv(a, b) -> float:
 
 
 def replicated(q_rows: np.ndarray, p_rows: np.ndarray, B: int, rng: np.random.Generator,
-               temperature: float, top_k: int = 0):
+               temperature: float, top_k: int = 0, top_p: float = 1.0):
     """B sequences that all carry the same rows: target q_rows [gamma+1, V], draft
     p_rows [gamma, V] (float32 logits); drafted tokens drawn from the oracle's p_j."""
     g1, V = q_rows.shape
@@ -83,7 +83,7 @@ def replicated(q_rows: np.ndarray, p_rows: np.ndarray, B: int, rng: np.random.Ge
     draft = np.ascontiguousarray(np.broadcast_to(p_rows, (B, gamma, V)), dtype=np.float32)
     tokens = np.empty((B, gamma), dtype=np.int32)
     for j in range(gamma):
-        pj = O.row_probs(p_rows[j], temperature, top_k)
+        pj = O.row_probs(p_rows[j], temperature, top_k, top_p)
         tokens[:, j] = rng.choice(V, size=B, p=pj / pj.sum())
     return target, draft, tokens
 
@@ -217,16 +217,17 @@ def check_accept_rate_and_n_distribution(B: int = 400_000, seed: int = 21):
     assert abs(acc0 - a0) < 4 * math.sqrt(a0 * (1 - a0) / B), (acc0, a0)
 
 
-def check_output_is_q(B: int = 200_000, seed: int = 5, temperature: float = 0.9, top_k: int = 0):
+def check_output_is_q(B: int = 200_000, seed: int = 5, temperature: float = 0.9, top_k: int = 0,
+                      top_p: float = 1.0):
     """gamma = 1: the committed first token is distributed as q_0 (the page's
     claim that the rule is exact, not approximate)."""
     rng = np.random.default_rng(seed)
     V = 8
     zq = rng.normal(0, 1.5, (2, V)).astype(np.float32)
     zp = rng.normal(0, 1.5, (1, V)).astype(np.float32)
-    target, draft, tokens = replicated(zq, zp, B, rng, temperature, top_k)
-    res = O.verify(target, draft, tokens, temperature, top_k, seed=99)
-    q0 = O.row_probs(zq[0], temperature, top_k)
+    target, draft, tokens = replicated(zq, zp, B, rng, temperature, top_k, top_p)
+    res = O.verify(target, draft, tokens, temperature, top_k, seed=99, top_p=top_p)
+    q0 = O.row_probs(zq[0], temperature, top_k, top_p)
     counts = np.bincount(res.out_tokens[:, 0], minlength=V)
     pv = chi2_pvalue(counts, q0)
     assert pv > 1e-6, f"first token vs q0: chi2 p = {pv}; counts {counts}; q0*B {q0 * B}"
@@ -446,3 +447,62 @@ def check_draft_sampler(n: int = 200_000, seed: int = 41):
     full, _ = O.draft_sample(rows, 1.0, 0, seed=3)
     part, _ = O.draft_sample(rows[5:], 1.0, 0, seed=3, seq_offset=5)
     assert np.array_equal(full[5:], part)
+
+
+# ---------------------------------------------------------------------------
+# Nucleus (top-p), reading R10 of the oracle
+# ---------------------------------------------------------------------------
+def _nucleus_numpy(z: np.ndarray, T: float, K: int, P: float):
+    """Written out with numpy: softmax of top-k(z)/T, then the shortest prefix
+    of the stable descending order with mass >= P, renormalised.  Returns the
+    probabilities and the distance of the cut from flipping."""
+    z64 = z.astype(np.float64)
+    V = z.shape[0]
+    order = np.argsort(-z64, kind="stable")
+    kept = order[:K] if 0 < K < V else order
+    x = z64[kept] / float(np.float32(T))
+    e = np.exp(x - x.max())
+    pk = e / e.sum()
+    probs = np.zeros(V)
+    margin = np.inf
+    P = float(np.float32(P))  # top_p crosses the C ABI as a float
+    if 0 < P < 1:
+        cum = np.cumsum(pk)
+        m = int(np.searchsorted(cum, P, side="left"))
+        m = min(m, len(pk) - 1)
+        margin = min(cum[m] - P, P - (cum[m - 1] if m > 0 else 0.0))
+        pk = pk[: m + 1] / cum[m]
+        kept = kept[: m + 1]
+    probs[kept] = pk
+    return probs, margin
+
+
+def check_nucleus(seed: int = 51):
+    """Top-p kept sets and probabilities equal a numpy statement of R10 (rows
+    with many tied logits included); P >= 1 or <= 0 changes nothing; a tiny P
+    keeps only the first largest logit; the verified first token follows q
+    under top-p (chi-square)."""
+    rng = np.random.default_rng(seed)
+    checked = 0
+    for trial in range(300):
+        V = int(rng.choice([5, 50, 700]))
+        z = (rng.integers(-4, 5, V) if trial % 2 else rng.normal(0, 2, V)).astype(np.float32)
+        T = float(rng.choice([1.0, 0.7, 1.6]))
+        K = int(rng.choice([0, 3, 20, V]))
+        P = float(rng.choice([0.3, 0.75, 0.9, 0.999]))
+        want, margin = _nucleus_numpy(z, T, K, P)
+        if margin < 1e-12:
+            continue  # a cut that rounding can move; not a test of the rule
+        got = O.row_probs(z, T, K, P)
+        assert np.array_equal(got > 0, want > 0), (V, T, K, P)
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=0)
+        assert abs(O.nucleus_margin(z, T, K, P) - margin) < 1e-9
+        checked += 1
+    assert checked > 250
+    z = rng.normal(0, 2, 64).astype(np.float32)
+    for P in (1.0, 1.5, 0.0, -1.0):
+        np.testing.assert_array_equal(O.row_probs(z, 0.8, 10, P), O.row_probs(z, 0.8, 10))
+    tiny = O.row_probs(z, 0.8, 0, 1e-9)
+    assert np.count_nonzero(tiny) == 1 and tiny[np.argmax(z)] == 1.0
+    check_output_is_q(temperature=0.9, top_k=0, top_p=0.8)
+    check_output_is_q(temperature=1.1, top_k=6, top_p=0.7)

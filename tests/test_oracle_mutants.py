@@ -36,6 +36,8 @@ MUTANTS = [
      "svo_gumbel_draw(p, V, seed, seq_offset + (uint64_t)b, (uint32_t)j, SVO_SAMPLE, &g)", ["draft"]),
     ("draft row without temperature", "svo_row_probs(prow, dtype, V, temperature, top_k, p, keep);\n                double g",
      "svo_row_probs(prow, dtype, V, 1.0f, top_k, p, keep);\n                double g", ["draft"]),
+    ("nucleus drops the entry that reaches P", "if (cum >= P) { m = i; break; }",
+     "if (cum >= P) { m = i - 1; cum = before; break; }", ["nucleus"]),
     ("arg-max ties keep the larger index",
      "if (svo_logit(row, dtype, v) > svo_logit(row, dtype, best)) best = v;",
      "if (svo_logit(row, dtype, v) >= svo_logit(row, dtype, best)) best = v;", ["greedy"]),
@@ -61,6 +63,8 @@ def _run(check):
         C.check_topk_vs_stable_sort()
     elif check == "draft":
         C.check_draft_sampler(n=100_000)
+    elif check == "nucleus":
+        C.check_nucleus()
     elif check == "greedy":
         C.check_greedy()
     elif check == "philox":

@@ -59,6 +59,12 @@ def test_special_cases():
     C.check_special_cases()
 
 
+def test_nucleus():
+    """Top-p (ai-trend.me, section "how it works": nucleus sampling is sampling
+    from an adjusted distribution)."""
+    C.check_nucleus()
+
+
 def test_greedy_mode():
     """T = 0 (arg-max mode of the ai-trend.me page, section "how it works")."""
     C.check_greedy()
