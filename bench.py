@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 HEADLINE = "c4b"
-SWEEP = ["c2", "c3", "c4a", "c4c", "c1", "g4b", "g2"]
+SWEEP = ["c2", "c3", "c3p", "c4a", "c4c", "c1", "g4b", "g2"]
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "rejection_sampling_verify_17_amd", "csrc")
 
@@ -147,10 +147,10 @@ def run_workload(name: str, steps: int, warmup: int, hip: Hip, seed: int = 3000)
         k = i % copies
         if events is None:
             S.verify(tgts[k], drfs[k], tok, w.temperature, w.top_k, seed=seed, out_tokens=out, n_accepted=nacc,
-                     workspace=ws)
+                     workspace=ws, top_p=w.top_p)
         else:
             S.verify_timed(tgts[k], drfs[k], tok, w.temperature, events, w.top_k, seed=seed, out_tokens=out,
-                           n_accepted=nacc, workspace=ws)
+                           n_accepted=nacc, workspace=ws, top_p=w.top_p)
 
     for i in range(warmup):
         step(i)
@@ -202,7 +202,7 @@ def run_workload(name: str, steps: int, warmup: int, hip: Hip, seed: int = 3000)
     dom_us = per_kernel[dominant]["avg_us"]
     res = {
         "workload": name, "B": w.B, "gamma": w.gamma, "V": w.V, "dtype": "bf16" if w.is_bf16 else "f32",
-        "temperature": w.temperature, "top_k": w.top_k, "input_copies": copies,
+        "temperature": w.temperature, "top_k": w.top_k, "top_p": w.top_p, "input_copies": copies,
         "ms_per_step": ms_step, "ms_per_step_with_kernel_events": ms_step_evented,
         "positions_per_s": positions / (ms_step * 1e-3),
         "algorithmic_bytes": ab, "GBps_step": ab["total"] / (ms_step * 1e-3) / 1e9,
@@ -290,17 +290,20 @@ def cpu_baseline(w, seed: int, budget_s: float = 12.0) -> dict:
     B = w.B
     n = min(B, max(cores, 8))
     t0 = time.perf_counter()
-    O.verify(w.target[:n], w.draft[:n], w.tokens[:n], w.temperature, w.top_k, seed=seed, nthreads=cores)
+    O.verify(w.target[:n], w.draft[:n], w.tokens[:n], w.temperature, w.top_k, seed=seed, nthreads=cores,
+             top_p=w.top_p)
     t1 = time.perf_counter() - t0
     if t1 < budget_s / 4 and n < B:
         n = int(min(B, max(n + 1, n * (budget_s / 2 / max(t1, 1e-3)))))
         t0 = time.perf_counter()
-        O.verify(w.target[:n], w.draft[:n], w.tokens[:n], w.temperature, w.top_k, seed=seed, nthreads=cores)
+        O.verify(w.target[:n], w.draft[:n], w.tokens[:n], w.temperature, w.top_k, seed=seed, nthreads=cores,
+             top_p=w.top_p)
         t1 = time.perf_counter() - t0
     reps = max(1, int(budget_s / max(t1, 1e-3)))
     t0 = time.perf_counter()
     for r in range(reps):
-        O.verify(w.target[:n], w.draft[:n], w.tokens[:n], w.temperature, w.top_k, seed=seed + r, nthreads=cores)
+        O.verify(w.target[:n], w.draft[:n], w.tokens[:n], w.temperature, w.top_k, seed=seed + r, nthreads=cores,
+                 top_p=w.top_p)
     t = time.perf_counter() - t0
     return {"value": reps * n * w.gamma / t, "unit": "verified draft positions/s", "cores": cores,
             "kind": "oracle",

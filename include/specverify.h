@@ -36,6 +36,14 @@
  *   - Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) with key
  *     (seed mod 2^32, seed >> 32), counter (v >> 2, pos, seq mod 2^32,
  *     purpose); the word is output (v mod 4).  seq = seq_offset + b.
+ *   - top_p in (0, 1) is nucleus sampling (page ai-trend.me, "어떻게 작동하나"):
+ *     after temperature and top-k, a row keeps its entries in the top-k order
+ *     (larger logit, then smaller index) until their probability mass
+ *     reaches top_p (the entry that reaches it is kept), renormalised; both
+ *     p and q.  It needs 0 < top_k <= 1024 and top_k < V (SV_EINVAL
+ *     otherwise); top_p <= 0 or >= 1 turns it off.  The cut is computed in
+ *     fp32: where the mass of a prefix lies within rounding of top_p, the
+ *     kept set can differ from an exact computation.
  *   - temperature 0 is the arg-max mode (page ai-trend.me, "어떻게 작동하나":
  *     arg-max decoding is sampling from an adjusted distribution): every
  *     distribution is the point mass on its row's largest logit, the smaller
@@ -69,7 +77,8 @@
  *
  * Errors: argument errors return SV_EINVAL before anything is enqueued
  * (null pointer, B < 1, gamma not in [1, 64], V < 2 or V > 2^28, temperature
- * not finite or < 0, unknown dtype, a logits pointer not aligned to its
+ * not finite or < 0, top_p NaN, top_p in (0, 1) without 0 < top_k <= 1024 <
+ * V, unknown dtype, a logits pointer not aligned to its
  * element size, workspace too small or misaligned).  A failed launch returns
  * SV_EHIP.  Calls never synchronise.
  */
@@ -101,7 +110,7 @@ SV_API size_t sv_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t to
 SV_API sv_status sv_verify(const void *target_logits, const void *draft_logits,
                     const int32_t *draft_tokens,
                     int32_t B, int32_t gamma, int32_t V, int32_t dtype,
-                    float temperature, int32_t top_k,
+                    float temperature, int32_t top_k, float top_p,
                     uint64_t seed, uint64_t seq_offset,
                     int32_t *out_tokens, int32_t *n_accepted,
                     void *workspace, size_t workspace_bytes, void *stream);
@@ -115,7 +124,7 @@ SV_API sv_status sv_verify(const void *target_logits, const void *draft_logits,
 SV_API sv_status sv_verify_debug(const void *target_logits, const void *draft_logits,
                           const int32_t *draft_tokens,
                           int32_t B, int32_t gamma, int32_t V, int32_t dtype,
-                          float temperature, int32_t top_k,
+                          float temperature, int32_t top_k, float top_p,
                           uint64_t seed, uint64_t seq_offset,
                           int32_t *out_tokens, int32_t *n_accepted,
                           void *workspace, size_t workspace_bytes, void *stream,
@@ -129,7 +138,7 @@ SV_API sv_status sv_verify_debug(const void *target_logits, const void *draft_lo
 SV_API sv_status sv_verify_timed(const void *target_logits, const void *draft_logits,
                           const int32_t *draft_tokens,
                           int32_t B, int32_t gamma, int32_t V, int32_t dtype,
-                          float temperature, int32_t top_k,
+                          float temperature, int32_t top_k, float top_p,
                           uint64_t seed, uint64_t seq_offset,
                           int32_t *out_tokens, int32_t *n_accepted,
                           void *workspace, size_t workspace_bytes, void *stream,

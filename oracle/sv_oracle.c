@@ -180,8 +180,8 @@ static void svo_topk_keep(const void *row, int dtype, int V, int top_k, unsigned
  * smaller index among equal logits.  0 < top_p < 1 applies the nucleus cut
  * of R10 after top-k; *margin (may be NULL) receives how far the cut lies
  * from flipping: min(C_m - P, P - C_{m-1}), C_i the cumulative mass of the
- * first i + 1 entries in the R2 order and m the last kept one (+inf without
- * a cut).  scratch_keep holds V bytes. */
+ * first i + 1 entries in the R2 order and m the last kept one (C_m - P when
+ * m = 0; +inf without a cut).  scratch_keep holds V bytes. */
 void svo_row_probs_p(const void *row, int dtype, int V, float temperature, int top_k, float top_p,
                      double *prob, unsigned char *scratch_keep, double *margin)
 {
@@ -229,7 +229,9 @@ void svo_row_probs_p(const void *row, int dtype, int V, float temperature, int t
             cum += prob[e[i].v];
             if (cum >= P) { m = i; break; }
         }
-        if (margin) *margin = fmin(cum - P, P - before);
+        /* with the first entry as the cut nothing precedes it: exactly 0 on
+         * any machine, so only C_0 - P can flip */
+        if (margin) *margin = m > 0 ? fmin(cum - P, P - before) : cum - P;
         for (int i = m + 1; i < n; ++i) prob[e[i].v] = 0.0;
         for (int v = 0; v < V; ++v) prob[v] /= cum;
         free(e);

@@ -43,7 +43,7 @@ def lib() -> ctypes.CDLL:
                 L = ctypes.CDLL(LIB_PATH)
                 vp, i32, u64, flt, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_float,
                                          ctypes.c_size_t)
-                common = [vp, vp, vp, i32, i32, i32, i32, flt, i32, u64, u64, vp, vp, vp, sz, vp]
+                common = [vp, vp, vp, i32, i32, i32, i32, flt, i32, flt, u64, u64, vp, vp, vp, sz, vp]
                 L.sv_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
                 L.sv_workspace_bytes.restype = sz
                 L.sv_verify.argtypes = common
@@ -159,7 +159,7 @@ def _check(target, draft, tokens):
 
 
 def _run(fn_name, target, draft, tokens, temperature, top_k, seed, seq_offset, out_tokens, n_accepted,
-         workspace, stream, extra):
+         workspace, stream, extra, top_p=1.0):
     torch = _torch()
     tokens, B, gamma, V = _check(target, draft, tokens)
     dt = _dtype_code(target)
@@ -175,7 +175,7 @@ def _run(fn_name, target, draft, tokens, temperature, top_k, seed, seq_offset, o
     with torch.cuda.device(dev):
         st = getattr(lib(), fn_name)(
             target.data_ptr(), draft.data_ptr(), tokens.data_ptr(), B, gamma, V, dt, float(temperature),
-            int(top_k), int(seed) & 0xFFFFFFFFFFFFFFFF, int(seq_offset) & 0xFFFFFFFFFFFFFFFF,
+            int(top_k), float(top_p), int(seed) & 0xFFFFFFFFFFFFFFFF, int(seq_offset) & 0xFFFFFFFFFFFFFFFF,
             out_tokens.data_ptr(), n_accepted.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr(dev, stream),
             *extra)
     if st != SV_OK:
@@ -184,17 +184,17 @@ def _run(fn_name, target, draft, tokens, temperature, top_k, seed, seq_offset, o
 
 
 def verify(target, draft, tokens, temperature: float, top_k: int = 0, seed: int = 0, seq_offset: int = 0,
-           out_tokens=None, n_accepted=None, workspace=None, stream=None):
+           out_tokens=None, n_accepted=None, workspace=None, stream=None, top_p: float = 1.0):
     """One verification step (sv_verify).  target [B, gamma+1, V], draft
     [B, gamma, V] (float32 or bfloat16, contiguous, on the GPU), tokens
     [B, gamma] int32.  Returns (out_tokens [B, gamma+1], n_accepted [B]),
     enqueued on the current stream (no synchronisation)."""
     return _run("sv_verify", target, draft, tokens, temperature, top_k, seed, seq_offset, out_tokens,
-                n_accepted, workspace, stream, ())
+                n_accepted, workspace, stream, (), top_p)
 
 
 def verify_debug(target, draft, tokens, temperature: float, top_k: int = 0, seed: int = 0,
-                 seq_offset: int = 0, workspace=None, stream=None):
+                 seq_offset: int = 0, workspace=None, stream=None, top_p: float = 1.0):
     """sv_verify_debug: also returns token_probs [B, gamma, 2] (p(t), q(t)) and
     accept_ur [B, gamma, 2] (u, ratio) as float32 tensors."""
     torch = _torch()
@@ -202,19 +202,20 @@ def verify_debug(target, draft, tokens, temperature: float, top_k: int = 0, seed
     tp = torch.empty((B, g1 - 1, 2), dtype=torch.float32, device=target.device)
     ur = torch.empty((B, g1 - 1, 2), dtype=torch.float32, device=target.device)
     out, n = _run("sv_verify_debug", target, draft, tokens, temperature, top_k, seed, seq_offset, None, None,
-                  workspace, stream, (tp.data_ptr(), ur.data_ptr()))
+                  workspace, stream, (tp.data_ptr(), ur.data_ptr()), top_p)
     return out, n, tp, ur
 
 
 def verify_timed(target, draft, tokens, temperature: float, events, top_k: int = 0, seed: int = 0,
-                 seq_offset: int = 0, out_tokens=None, n_accepted=None, workspace=None, stream=None):
+                 seq_offset: int = 0, out_tokens=None, n_accepted=None, workspace=None, stream=None,
+                 top_p: float = 1.0):
     """sv_verify_timed: `events` is a sequence of hipEvent_t handles (ints),
     recorded before/after each launch.  Returns (out, n, number of launches)."""
     arr = (ctypes.c_void_p * len(events))(*events)
     nl = ctypes.c_int32(0)
     out, n = _run("sv_verify_timed", target, draft, tokens, temperature, top_k, seed, seq_offset, out_tokens,
                   n_accepted, workspace, stream, (ctypes.cast(arr, ctypes.c_void_p), len(events),
-                                                  ctypes.addressof(nl)))
+                                                  ctypes.addressof(nl)), top_p)
     return out, n, nl.value
 
 

@@ -228,7 +228,7 @@ struct Launches {
 };
 
 sv_status verify_impl(const void *target, const void *draft, const int32_t *tokens, int32_t B, int32_t gamma,
-                      int32_t V, int32_t dtype, float temperature, int32_t top_k, uint64_t seed,
+                      int32_t V, int32_t dtype, float temperature, int32_t top_k, float top_p, uint64_t seed,
                       uint64_t seq_offset, int32_t *out_tokens, int32_t *n_accepted, void *workspace,
                       size_t workspace_bytes, void *stream, float *token_probs, float *accept_ur,
                       void *const *events, int32_t n_events, int32_t *n_launches) {
@@ -237,6 +237,11 @@ sv_status verify_impl(const void *target, const void *draft, const int32_t *toke
   if (!shape_ok(B, gamma, V, dtype)) return SV_EINVAL;
   if (!std::isfinite(temperature) || !(temperature >= 0.0f)) return SV_EINVAL;  // 0: arg-max mode
   const bool greedy = temperature == 0.0f;
+  // nucleus: 0 < top_p < 1 (else off); it cuts the top-k path's kept lists, so
+  // it needs 0 < top_k <= 1024 and top_k < V (the arg-max mode ignores both)
+  if (std::isnan(top_p)) return SV_EINVAL;
+  const bool nucleus = !greedy && top_p > 0.0f && top_p < 1.0f;
+  if (nucleus && !(top_k > 0 && top_k <= kListMax && top_k < V)) return SV_EINVAL;
   const uintptr_t elem = dtype == SV_BF16 ? 2 : 4;
   if (((uintptr_t)target % elem) || ((uintptr_t)draft % elem)) return SV_EINVAL;
   if (((uintptr_t)tokens % 4) || ((uintptr_t)out_tokens % 4) || ((uintptr_t)n_accepted % 4)) return SV_EINVAL;
@@ -256,6 +261,7 @@ sv_status verify_impl(const void *target, const void *draft, const int32_t *toke
   a.gamma = gamma;
   a.V = V;
   a.top_k = p.topk ? top_k : 0;
+  a.top_p = nucleus ? top_p : 1.0f;
   a.c = greedy ? 0.0f : (float)(1.4426950408889634 / (double)temperature);
   a.key0 = (uint32_t)seed;
   a.key1 = (uint32_t)(seed >> 32);
@@ -306,30 +312,30 @@ size_t sv_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t top_k, in
 }
 
 sv_status sv_verify(const void *target_logits, const void *draft_logits, const int32_t *draft_tokens, int32_t B,
-                    int32_t gamma, int32_t V, int32_t dtype, float temperature, int32_t top_k, uint64_t seed,
-                    uint64_t seq_offset, int32_t *out_tokens, int32_t *n_accepted, void *workspace,
+                    int32_t gamma, int32_t V, int32_t dtype, float temperature, int32_t top_k, float top_p,
+                    uint64_t seed, uint64_t seq_offset, int32_t *out_tokens, int32_t *n_accepted, void *workspace,
                     size_t workspace_bytes, void *stream) {
-  return verify_impl(target_logits, draft_logits, draft_tokens, B, gamma, V, dtype, temperature, top_k, seed,
+  return verify_impl(target_logits, draft_logits, draft_tokens, B, gamma, V, dtype, temperature, top_k, top_p, seed,
                      seq_offset, out_tokens, n_accepted, workspace, workspace_bytes, stream, nullptr, nullptr,
                      nullptr, 0, nullptr);
 }
 
 sv_status sv_verify_debug(const void *target_logits, const void *draft_logits, const int32_t *draft_tokens,
                           int32_t B, int32_t gamma, int32_t V, int32_t dtype, float temperature, int32_t top_k,
-                          uint64_t seed, uint64_t seq_offset, int32_t *out_tokens, int32_t *n_accepted,
+                          float top_p, uint64_t seed, uint64_t seq_offset, int32_t *out_tokens, int32_t *n_accepted,
                           void *workspace, size_t workspace_bytes, void *stream, float *token_probs,
                           float *accept_ur) {
-  return verify_impl(target_logits, draft_logits, draft_tokens, B, gamma, V, dtype, temperature, top_k, seed,
+  return verify_impl(target_logits, draft_logits, draft_tokens, B, gamma, V, dtype, temperature, top_k, top_p, seed,
                      seq_offset, out_tokens, n_accepted, workspace, workspace_bytes, stream, token_probs,
                      accept_ur, nullptr, 0, nullptr);
 }
 
 sv_status sv_verify_timed(const void *target_logits, const void *draft_logits, const int32_t *draft_tokens,
                           int32_t B, int32_t gamma, int32_t V, int32_t dtype, float temperature, int32_t top_k,
-                          uint64_t seed, uint64_t seq_offset, int32_t *out_tokens, int32_t *n_accepted,
+                          float top_p, uint64_t seed, uint64_t seq_offset, int32_t *out_tokens, int32_t *n_accepted,
                           void *workspace, size_t workspace_bytes, void *stream, void *const *events,
                           int32_t n_events, int32_t *n_launches) {
-  return verify_impl(target_logits, draft_logits, draft_tokens, B, gamma, V, dtype, temperature, top_k, seed,
+  return verify_impl(target_logits, draft_logits, draft_tokens, B, gamma, V, dtype, temperature, top_k, top_p, seed,
                      seq_offset, out_tokens, n_accepted, workspace, workspace_bytes, stream, nullptr, nullptr,
                      events, n_events, n_launches);
 }

@@ -61,6 +61,7 @@ struct Args {
   const void *draft;       // [B][gamma][V]
   const int32_t *tokens;   // [B][gamma]
   int32_t B, gamma, V, top_k;
+  float top_p;             // nucleus mass (1: off); only with 0 < top_k <= 1024
   float c;                 // log2(e) / T
   uint32_t key0, key1;     // Philox key = seed
   uint64_t seq_offset;

@@ -56,6 +56,9 @@ struct TopkShared {
   float red_f[kTopkThreads / kWave];
   unsigned long long red_u[kTopkThreads / kWave];
   int bcast_n;
+  unsigned long long srt[kTopkThreads];  // nucleus cut: the kept keys, sorted
+  int cut;
+  float cut_sum;
 };
 
 __device__ __forceinline__ unsigned long long entry_key(float z, uint32_t v) {
@@ -326,15 +329,95 @@ __device__ __forceinline__ TopkRow kept_stats(TopkShared &sh, const Keys &keys, 
   return TopkRow{thr, R, S, false, 0u};
 }
 
+// Nucleus cut (top-p) of a selected row: the kept entries (keys >= r.thr, K
+// of them, K <= kTopkThreads) are sorted in the top-k order (larger logit,
+// then smaller index), their base-2 weights 2^(z c - R) summed as a prefix,
+// and the row keeps the shortest prefix whose mass reaches P of the total:
+// the threshold rises to that prefix's last key and S becomes its sum (R
+// still bounds every kept logit).  Every reader of the row tests keys
+// against the threshold, so nothing else changes.
+template <class Keys>
+__device__ __forceinline__ void nucleus_cut(TopkShared &sh, const Keys &keys, float c, float P, TopkRow &r) {
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  if (tid == 0) {
+    sh.nkept = 0u;
+    sh.cut = kTopkThreads;
+  }
+  __syncthreads();
+  keys.for_each([&](unsigned long long key) {
+    if (key >= r.thr) {
+      const unsigned int slot = atomicAdd(&sh.nkept, 1u);
+      if (slot < (unsigned int)kTopkThreads) sh.srt[slot] = key;
+    }
+  });
+  __syncthreads();
+  const int n = (int)min(sh.nkept, (unsigned int)kTopkThreads);
+  if (tid >= n) sh.srt[tid] = 0ull;  // below every real key: sorts last
+  __syncthreads();
+  // bitonic sort of the kTopkThreads keys, descending, one per thread
+  for (int size = 2; size <= kTopkThreads; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const int partner = tid ^ stride;
+      if (partner > tid) {
+        const unsigned long long x = sh.srt[tid], y = sh.srt[partner];
+        const bool swap = ((tid & size) == 0) ? (x < y) : (x > y);
+        if (swap) {
+          sh.srt[tid] = y;
+          sh.srt[partner] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // inclusive prefix sum of the weights in that order
+  float e = 0.0f;
+  if (tid < n) {
+    const float z = from_orderable((uint32_t)(sh.srt[tid] >> 32));
+    if (z != -INFINITY) e = __builtin_amdgcn_exp2f(fmaf(z, c, -r.R));
+  }
+  float s = e;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const float y = __shfl_up(s, off, kWave);
+    if (lane >= off) s += y;
+  }
+  if (lane == kWave - 1) sh.red_f[wave] = s;
+  __syncthreads();
+  float below = 0.0f, total = 0.0f;
+  for (int w = 0; w < kTopkThreads / kWave; ++w) {
+    if (w < wave) below += sh.red_f[w];
+    total += sh.red_f[w];
+  }
+  const float cum = below + s;
+  // the first entry whose prefix reaches P of the total
+  const unsigned long long hit = __ballot(tid < n && cum >= P * total);
+  if (lane == 0 && hit != 0ull) atomicMin(&sh.cut, wave * kWave + __builtin_ctzll(hit));
+  __syncthreads();
+  const int m = sh.cut;
+  if (tid == m) sh.cut_sum = cum;
+  __syncthreads();
+  if (m < n) {
+    r.thr = sh.srt[m];
+    r.S = sh.cut_sum;
+  }
+  __syncthreads();
+}
+
 // Top-K of a row: exact threshold, statistics over the kept entries, and the
-// kept list when given.
+// kept list when given; then the nucleus cut when 0 < top_p < 1 (the caller
+// guarantees K <= kTopkThreads then).
 template <class Src>
-__device__ __forceinline__ TopkRow topk_row(TopkShared &sh, const Src &src, int K, float c, int2 *list) {
+__device__ __forceinline__ TopkRow topk_row(TopkShared &sh, const Src &src, int K, float c, float top_p,
+                                            int2 *list) {
   const Selected sel = select_threshold(sh, src, K);
   TopkRow r = sel.in_lds ? kept_stats(sh, LdsKeys<kTopkThreads>{sh.cand, sel.ncand}, sel.thr, c, list, K)
                          : kept_stats(sh, SrcKeys<Src>{src}, sel.thr, c, list, K);
   r.in_lds = sel.in_lds;
   r.ncand = sel.ncand;
+  if (top_p > 0.0f && top_p < 1.0f) {
+    if (sel.in_lds) nucleus_cut(sh, LdsKeys<kTopkThreads>{sh.cand, sel.ncand}, c, top_p, r);
+    else nucleus_cut(sh, SrcKeys<Src>{src}, c, top_p, r);
+  }
   return r;
 }
 
@@ -438,9 +521,10 @@ __device__ __forceinline__ size_t slot_of(const Args &a, int b, int s) {
 // wave 0 computes the same result).
 // Top-k of one global row.
 template <int DT>
-__device__ __forceinline__ TopkRow select_row(TopkShared &sh, const Row<DT> &row, int V, int K, float c, int2 *list) {
+__device__ __forceinline__ TopkRow select_row(TopkShared &sh, const Row<DT> &row, int V, int K, float c, float top_p,
+                                              int2 *list) {
   const StreamRow<DT> src(row, V);
-  return topk_row(sh, src, K, c, list);
+  return topk_row(sh, src, K, c, top_p, list);
 }
 
 template <int DT>
@@ -536,7 +620,7 @@ __global__ __launch_bounds__(kTopkThreads, 8) void k_topk_step(Args a, int launc
     const void *ptr = r == 0 ? draft_row<DT>(a, b, j) : target_row<DT>(a, b, j);
     const Row<DT> row(ptr, a.V);
     int2 *list = a.lists ? a.lists + slot_of(a, b, slot) * (size_t)a.klist : nullptr;
-    const TopkRow tr = select_row<DT>(sh, row, a.V, a.top_k, a.c, list);
+    const TopkRow tr = select_row<DT>(sh, row, a.V, a.top_k, a.c, a.top_p, list);
     if (threadIdx.x == 0) a.rowinfo[slot_of(a, b, slot)] = pack_rowinfo(tr);
   } else if (mode == 1) {
     const TopkRow pr = unpack_rowinfo(a.rowinfo[slot_of(a, b, n)]);
@@ -550,7 +634,7 @@ __global__ __launch_bounds__(kTopkThreads, 8) void k_topk_step(Args a, int launc
   } else {
     // every draft kept: top-k of target row gamma, then the bonus draw
     const Row<DT> Q(target_row<DT>(a, b, gamma), a.V);
-    const TopkRow qr = select_row<DT>(sh, Q, a.V, a.top_k, a.c, nullptr);
+    const TopkRow qr = select_row<DT>(sh, Q, a.V, a.top_k, a.c, a.top_p, nullptr);
     const unsigned long long k = gumbel_over_kept_q<DT>(sh, a, b, gamma, qr, nullptr, Q);
     if (threadIdx.x == 0) out[gamma] = (int32_t)packed_index(k);
   }

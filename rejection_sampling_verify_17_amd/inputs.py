@@ -13,6 +13,7 @@ Workloads (B sequences, gamma drafts, vocabulary V):
   c3   B=256,  gamma=8, V=152064, bf16, as c2 with draft noise sigma 2, T=0.8, top-k 50
   c4a/b/c B=1024, gamma=4, V=50257, fp32, target N(0, 3^2), draft = target + N(0, s^2),
        s = 0.25 / 1 / 4, T=1
+  c3p  c3 with top-p 0.9 after the top-k 50 (nucleus)
   g2   c2's logits at T=0 (arg-max mode)
   g4b  c4b's logits at T=0 (arg-max mode)
 
@@ -51,6 +52,7 @@ class Spec:
     zipf: bool
     data_seed: int
     draft_seed: int
+    top_p: float = 1.0       # nucleus mass (1: off)
 
 
 SPECS = {
@@ -61,6 +63,7 @@ SPECS = {
     "c4a": Spec("c4a", 1024, 4, 50257, "f32", 1.0, 0, 3.0, 1.0, 0.25, False, 1040, 2040),
     "c4b": Spec("c4b", 1024, 4, 50257, "f32", 1.0, 0, 3.0, 1.0, 1.0, False, 1041, 2041),
     "c4c": Spec("c4c", 1024, 4, 50257, "f32", 1.0, 0, 3.0, 1.0, 4.0, False, 1042, 2042),
+    "c3p": Spec("c3p", 256, 8, 152064, "bf16", 0.8, 50, 3.0, 1.0, 2.0, True, 1003, 2003, 0.9),
     "g2": Spec("g2", 64, 5, 128256, "bf16", 0.0, 0, 3.0, 1.0, 1.0, True, 1002, 2002),
     "g4b": Spec("g4b", 1024, 4, 50257, "f32", 0.0, 0, 3.0, 1.0, 1.0, False, 1041, 2041),
 }
@@ -83,6 +86,8 @@ class Workload:
     def temperature(self): return self.spec.temperature
     @property
     def top_k(self): return self.spec.top_k
+    @property
+    def top_p(self): return self.spec.top_p
     @property
     def is_bf16(self): return self.target.dtype == np.uint16
 
@@ -117,22 +122,34 @@ def logits_f32(a: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # Draft-token sampler (stand-in for the draft model)
 # ---------------------------------------------------------------------------
-def _adjusted(z: np.ndarray, temperature: float, top_k: int) -> np.ndarray:
-    """Rows of z [R, V] float64 -> softmax(top-k(z) / T) as float64 [R, V]."""
+def _adjusted(z: np.ndarray, temperature: float, top_k: int, top_p: float = 1.0) -> np.ndarray:
+    """Rows of z [R, V] float64 -> softmax(top-k(z) / T), then the nucleus of
+    mass top_p in the same order (larger logit, then smaller index), as
+    float64 [R, V]."""
     R, V = z.shape
     x = z / float(np.float32(temperature))
+    order = np.argsort(-z, axis=1, kind="stable")
     if 0 < top_k < V:
-        order = np.argsort(-z, axis=1, kind="stable")[:, :top_k]
         mask = np.zeros_like(z, dtype=bool)
-        np.put_along_axis(mask, order, True, axis=1)
+        np.put_along_axis(mask, order[:, :top_k], True, axis=1)
         x = np.where(mask, x, -np.inf)
     x = x - x.max(axis=1, keepdims=True)
     e = np.exp(x)
-    return e / e.sum(axis=1, keepdims=True)
+    p = e / e.sum(axis=1, keepdims=True)
+    P = float(np.float32(top_p))
+    if 0 < P < 1:
+        ps = np.take_along_axis(p, order, axis=1)
+        cum = np.cumsum(ps, axis=1)
+        keep_sorted = (cum - ps) < P          # entries before the one that reaches P, and it
+        keep = np.zeros_like(keep_sorted)
+        np.put_along_axis(keep, order, keep_sorted, axis=1)
+        p = np.where(keep, p, 0.0)
+        p = p / p.sum(axis=1, keepdims=True)
+    return p
 
 
 def sample_rows(z: np.ndarray, temperature: float, top_k: int, rng: np.random.Generator,
-                chunk: int = 256) -> np.ndarray:
+                chunk: int = 256, top_p: float = 1.0) -> np.ndarray:
     """One token per row of z [R, V] from the row's adjusted distribution
     (T = 0: the first largest logit)."""
     R, V = z.shape
@@ -140,7 +157,7 @@ def sample_rows(z: np.ndarray, temperature: float, top_k: int, rng: np.random.Ge
         return np.argmax(np.asarray(z), axis=1).astype(np.int32)
     out = np.empty(R, dtype=np.int32)
     for s in range(0, R, chunk):
-        p = _adjusted(np.asarray(z[s:s + chunk], dtype=np.float64), temperature, top_k)
+        p = _adjusted(np.asarray(z[s:s + chunk], dtype=np.float64), temperature, top_k, top_p)
         cdf = np.cumsum(p, axis=1)
         u = rng.random(p.shape[0]) * cdf[:, -1]
         t = (cdf <= u[:, None]).sum(axis=1)
@@ -198,7 +215,7 @@ def build(spec: Spec) -> Workload:
             draft[b] = d
     drng = np.random.default_rng(spec.draft_seed)
     z = logits_f32(draft.reshape(B * g, V))
-    tokens = sample_rows(z, spec.temperature, spec.top_k, drng).reshape(B, g)
+    tokens = sample_rows(z, spec.temperature, spec.top_k, drng, top_p=spec.top_p).reshape(B, g)
     return Workload(spec, target, draft, tokens)
 
 
@@ -220,10 +237,10 @@ def replicate_position(w: Workload, b: int, j: int, n_seq: int, seed: int) -> Wo
 
 
 def from_arrays(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray,
-                temperature: float = 1.0, top_k: int = 0, name: str = "custom") -> Workload:
+                temperature: float = 1.0, top_k: int = 0, name: str = "custom", top_p: float = 1.0) -> Workload:
     B, g1, V = target.shape
     spec = Spec(name, B, g1 - 1, V, "bf16" if target.dtype == np.uint16 else "f32",
-                temperature, top_k, 0.0, 0.0, 0.0, False, -1, -1)
+                temperature, top_k, 0.0, 0.0, 0.0, False, -1, -1, top_p)
     return Workload(spec, np.ascontiguousarray(target), np.ascontiguousarray(draft),
                     np.ascontiguousarray(tokens, dtype=np.int32))
 

@@ -470,7 +470,7 @@ def _nucleus_numpy(z: np.ndarray, T: float, K: int, P: float):
         cum = np.cumsum(pk)
         m = int(np.searchsorted(cum, P, side="left"))
         m = min(m, len(pk) - 1)
-        margin = min(cum[m] - P, P - (cum[m - 1] if m > 0 else 0.0))
+        margin = min(cum[m] - P, P - cum[m - 1]) if m > 0 else cum[0] - P
         pk = pk[: m + 1] / cum[m]
         kept = kept[: m + 1]
     probs[kept] = pk

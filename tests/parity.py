@@ -11,6 +11,9 @@ same Philox streams):
       - the sampled token when the oracle's two best Gumbel keys are within
         1e-5 (a knife-edge arg-max);
   * the rate of non-exempt mismatches is <= 1e-4;
+  * with top-p, a sequence is exempt when one of the oracle's rows it used
+    has its nucleus cut within 1e-5 of flipping (the kept set is decided by
+    an fp32 prefix sum on the GPU);
   * p_j(t_j), q_j(t_j) within 1e-5 relative of the oracle where the oracle's
     value is >= 1e-30, and the acceptance uniforms equal exactly, at every
     position both sides judged; positions the GPU did not judge (after its
@@ -42,6 +45,7 @@ class Report:
     sequences: int = 0
     exempt_accept: int = 0
     exempt_token: int = 0
+    exempt_nucleus: int = 0
     mismatches: int = 0
     mismatch_examples: list = field(default_factory=list)
     prob_checked: int = 0
@@ -53,6 +57,7 @@ class Report:
         self.sequences += o.sequences
         self.exempt_accept += o.exempt_accept
         self.exempt_token += o.exempt_token
+        self.exempt_nucleus += o.exempt_nucleus
         self.mismatches += o.mismatches
         self.mismatch_examples += o.mismatch_examples[: max(0, 10 - len(self.mismatch_examples))]
         self.prob_checked += o.prob_checked
@@ -71,7 +76,8 @@ class Report:
     def summary(self) -> dict:
         return {"sequences": self.sequences, "mismatches": self.mismatches,
                 "mismatch_rate": self.mismatch_rate, "exempt_accept": self.exempt_accept,
-                "exempt_token": self.exempt_token, "prob_checked": self.prob_checked,
+                "exempt_token": self.exempt_token, "exempt_nucleus": self.exempt_nucleus,
+                "prob_checked": self.prob_checked,
                 "prob_max_rel": self.prob_max_rel, "prob_failures": self.prob_failures,
                 "u_failures": self.u_failures, "examples": self.mismatch_examples[:5]}
 
@@ -94,10 +100,11 @@ def run_gpu(w, seed: int, seq_offset: int = 0, debug: bool = True, tensors=None)
     import rejection_sampling_verify_17_amd as S
     tgt, drf, tok = tensors if tensors is not None else to_device(w)
     if debug:
-        out, n, tp, ur = S.verify_debug(tgt, drf, tok, w.temperature, w.top_k, seed=seed, seq_offset=seq_offset)
+        out, n, tp, ur = S.verify_debug(tgt, drf, tok, w.temperature, w.top_k, seed=seed, seq_offset=seq_offset,
+                                        top_p=w.top_p)
         torch.cuda.synchronize()
         return GpuResult(out.cpu().numpy(), n.cpu().numpy(), tp.cpu().numpy(), ur.cpu().numpy())
-    out, n = S.verify(tgt, drf, tok, w.temperature, w.top_k, seed=seed, seq_offset=seq_offset)
+    out, n = S.verify(tgt, drf, tok, w.temperature, w.top_k, seed=seed, seq_offset=seq_offset, top_p=w.top_p)
     torch.cuda.synchronize()
     return GpuResult(out.cpu().numpy(), n.cpu().numpy())
 
@@ -115,13 +122,16 @@ def compare(w, seed: int, g: GpuResult, seq_offset: int = 0, rows=None, nthreads
         groups = [(int(r), int(r) + 1) for r in rows]
     for lo, hi in groups:
         res = O.verify(w.target[lo:hi], w.draft[lo:hi], w.tokens[lo:hi], w.temperature, w.top_k, seed=seed,
-                       seq_offset=seq_offset + lo, nthreads=nthreads)
+                       seq_offset=seq_offset + lo, nthreads=nthreads, top_p=w.top_p)
         if check_probs and g.token_probs is not None:
             pt, qt = O.token_probs(w.target[lo:hi], w.draft[lo:hi], w.tokens[lo:hi], w.temperature, w.top_k,
-                                   nthreads=nthreads)
+                                   nthreads=nthreads, top_p=w.top_p)
         for i in range(hi - lo):
             b = lo + i
             rep.sequences += 1
+            if res.margin[i] < KNIFE:
+                rep.exempt_nucleus += 1
+                continue
             _compare_seq(rep, w, b, i, res, g)
             if w.temperature == 0.0:
                 if g.token_probs is not None and not (np.all(np.isnan(g.token_probs[b])) and

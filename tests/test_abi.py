@@ -84,11 +84,11 @@ def _call(L, **over):
     """sv_verify with fake, well-aligned device addresses; some argument is
     always invalid so nothing is ever launched."""
     args = dict(target=0x100000, draft=0x200000, tokens=0x300000, B=4, gamma=3, V=1000, dtype=0,
-                T=1.0, K=0, seed=1, off=0, out=0x400000, n=0x500000, ws=0x600000, wsb=1 << 30, stream=None)
+                T=1.0, K=0, P=1.0, seed=1, off=0, out=0x400000, n=0x500000, ws=0x600000, wsb=1 << 30, stream=None)
     args.update(over)
     return L.sv_verify(args["target"], args["draft"], args["tokens"], args["B"], args["gamma"], args["V"],
-                       args["dtype"], args["T"], args["K"], args["seed"], args["off"], args["out"], args["n"],
-                       args["ws"], args["wsb"], args["stream"])
+                       args["dtype"], args["T"], args["K"], args["P"], args["seed"], args["off"], args["out"],
+                       args["n"], args["ws"], args["wsb"], args["stream"])
 
 
 @pytest.mark.parametrize("over", [
@@ -96,7 +96,8 @@ def _call(L, **over):
     dict(B=0), dict(B=-3), dict(gamma=0), dict(gamma=65), dict(V=1), dict(V=(1 << 28) + 1),
     dict(dtype=2), dict(T=-1e-30), dict(T=-1.0), dict(T=float("nan")), dict(T=float("inf")),
     dict(wsb=16), dict(target=0x100002), dict(dtype=1, draft=0x200001), dict(tokens=0x300002),
-    dict(ws=0x600010),
+    dict(ws=0x600010), dict(P=float("nan")), dict(P=0.9), dict(P=0.9, K=2000), dict(P=0.5, K=1000),
+    dict(P=0.9, K=50, ws=None),
 ], ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
 def test_invalid_arguments_rejected_before_launch(L, over):
     assert _call(L, **over) == 1  # SV_EINVAL

@@ -345,3 +345,56 @@ def test_greedy_invalid_tokens_and_workspace_reuse():
         g = PT.GpuResult(out.cpu().numpy(), n.cpu().numpy())
         _check(PT.compare(wk, 2, g, check_probs=False), f"reuse {name}")
     assert g.n_accepted[3] == -1 and g.n_accepted[7] == -1 and np.all(g.out_tokens[3] == -1)
+
+
+# ---------------------------------------------------------------------------
+# Nucleus (top-p after top-k)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B", [8, None], ids=["B8", "Bfull"])
+def test_nucleus_parity(B):
+    w = I.make("c3p", B=B)
+    _say(f"case nucleus c3p B={w.B} gamma={w.gamma} V={w.V} T={w.temperature} K={w.top_k} P={w.top_p}")
+    tensors = PT.to_device(w)
+    for seed in ((3301, 3302) if B else (3303,)):
+        g = PT.run_gpu(w, seed, tensors=tensors)
+        _check(PT.compare(w, seed, g), f"c3p seed {seed}")
+
+
+def _nucleus_edges():
+    rng = np.random.default_rng(909)
+    out = []
+
+    def drafted(d, T, K, P):
+        return I.sample_rows(I.logits_f32(d).reshape(-1, d.shape[2]), T, K, rng, top_p=P).reshape(d.shape[:2])
+
+    for K, P in ((7, 0.6), (50, 1e-6), (20, 0.999)):
+        t = rng.integers(-4, 5, (6, 3, 500)).astype(np.float32)          # ties at and around the cut
+        d = rng.integers(-4, 5, (6, 2, 500)).astype(np.float32)
+        tok = drafted(d, 1.0, K, P)
+        out.append((f"ties-K{K}-P{P}", I.from_arrays(t, d, tok, top_k=K, top_p=P)))
+        out.append((f"ties-K{K}-P{P}-bf16", I.from_arrays(I.f32_to_bf16_bits(t), I.f32_to_bf16_bits(d), tok,
+                                                          top_k=K, top_p=P)))
+    t = rng.normal(0, 1, (3, 3, 6000)).astype(np.float32)                 # K at the maximum, flat rows
+    d = (t[:, :2] + rng.normal(0, 0.5, (3, 2, 6000))).astype(np.float32)
+    out.append(("K1024-P0.5", I.from_arrays(t, d, drafted(d, 1.0, 1024, 0.5), top_k=1024, top_p=0.5)))
+    tb = I.f32_to_bf16_bits(rng.normal(0, 3, (5, 3, 4099)).astype(np.float32))  # every 2-byte row offset
+    db = I.f32_to_bf16_bits((I.bf16_bits_to_f32(tb[:, :2]) + rng.normal(0, 1, (5, 2, 4099))).astype(np.float32))
+    out.append(("bf16-oddV", I.from_arrays(tb, db, drafted(db, 0.9, 40, 0.8), temperature=0.9, top_k=40,
+                                           top_p=0.8)))
+    t = rng.normal(0, 2, (16, 4, 3000)).astype(np.float32)               # p == q: all kept, bonus under top-p
+    out.append(("p-equals-q", I.from_arrays(t, t[:, :3].copy(), drafted(t[:, :3], 1.0, 30, 0.7), top_k=30,
+                                            top_p=0.7)))
+    return out
+
+
+NUCLEUS_EDGES = _nucleus_edges()
+
+
+@pytest.mark.parametrize("name,w", NUCLEUS_EDGES, ids=[e[0] for e in NUCLEUS_EDGES])
+def test_nucleus_edge_cases(name, w):
+    _say(f"case nucleus edge {name} B={w.B} gamma={w.gamma} V={w.V} K={w.top_k} P={w.top_p}")
+    for seed in (13, 14):
+        g = PT.run_gpu(w, seed)
+        _check(PT.compare(w, seed, g), f"nucleus edge {name} seed {seed}")
+    if name == "p-equals-q":
+        assert np.all(g.n_accepted == w.gamma)
