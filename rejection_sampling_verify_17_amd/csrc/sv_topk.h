@@ -352,6 +352,52 @@ __device__ __forceinline__ void nucleus_cut(TopkShared &sh, const Keys &keys, fl
   });
   __syncthreads();
   const int n = (int)min(sh.nkept, (unsigned int)kTopkThreads);
+  if (n <= kWave) {
+    // up to 64 kept entries: wave 0 sorts them in registers (bitonic, by
+    // shuffles) and scans them, with no block barrier in between
+    if (wave == 0) {
+      unsigned long long x = lane < n ? sh.srt[lane] : 0ull;  // 0 is below every real key
+#pragma unroll
+      for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          const unsigned long long y = __shfl_xor(x, stride, kWave);
+          const bool desc = (lane & size) == 0, lower = (lane & stride) == 0;
+          x = (lower == desc) ? (x > y ? x : y) : (x < y ? x : y);
+        }
+      }
+      float e = 0.0f;
+      if (lane < n) {
+        const float z = from_orderable((uint32_t)(x >> 32));
+        if (z != -INFINITY) e = __builtin_amdgcn_exp2f(fmaf(z, c, -r.R));
+      }
+      float s = e;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const float y = __shfl_up(s, off, kWave);
+        if (lane >= off) s += y;
+      }
+      const float total = __shfl(s, kWave - 1, kWave);
+      const unsigned long long hit = __ballot(lane < n && s >= P * total);
+      if (hit != 0ull) {
+        const int m = __builtin_ctzll(hit);
+        const unsigned long long km = __shfl(x, m, kWave);
+        const float sm = __shfl(s, m, kWave);
+        if (lane == 0) {
+          sh.cut = m;
+          sh.srt[0] = km;
+          sh.cut_sum = sm;
+        }
+      }
+    }
+    __syncthreads();
+    if (sh.cut < n) {
+      r.thr = sh.srt[0];
+      r.S = sh.cut_sum;
+    }
+    __syncthreads();
+    return;
+  }
   if (tid >= n) sh.srt[tid] = 0ull;  // below every real key: sorts last
   __syncthreads();
   // bitonic sort of the kTopkThreads keys, descending, one per thread
