@@ -238,12 +238,12 @@ def run_draft(name: str, steps: int, warmup: int, hip: Hip, seed: int = 3000) ->
     out = torch.empty((w.B, w.gamma), dtype=torch.int32, device=dev)
     sp = int(torch.cuda.current_stream(dev).cuda_stream)
     for i in range(warmup):
-        S.draft_sample(drfs[i % copies], w.temperature, w.top_k, seed=seed, out=out)
+        S.draft_sample(drfs[i % copies], w.temperature, w.top_k, seed=seed, out=out, top_p=w.top_p)
     torch.cuda.synchronize()
     e0, e1 = hip.event(), hip.event()
     hip.record(e0, sp)
     for i in range(steps):
-        S.draft_sample(drfs[i % copies], w.temperature, w.top_k, seed=seed, out=out)
+        S.draft_sample(drfs[i % copies], w.temperature, w.top_k, seed=seed, out=out, top_p=w.top_p)
     hip.record(e1, sp)
     hip.sync(e1)
     us = hip.ms(e0, e1) / steps * 1e3

@@ -151,7 +151,8 @@ SV_API const char *sv_launch_name(int32_t B, int32_t gamma, int32_t V, int32_t d
 
 /* Draft tokens for a verification step: token j of sequence b drawn on the
  * GPU from the draft row's adjusted distribution p_j = softmax(topk(z) / T)
- * (the same temperature, top-k and arg-max conventions as sv_verify), the
+ * (the same temperature, top-k, top-p and arg-max conventions as sv_verify,
+ * top-p again only with 0 < top_k <= 1024 < V), the
  * step the small model takes before the large one verifies (page ai-trend.me,
  * section "어떻게 작동하나").  The draw is Gumbel-max: the arg-max over the kept
  * entries of ln p_v - ln E_v, E_v = -ln U_v, U_v = (2 * (w >> 9) + 1) * 2^-24,
@@ -161,10 +162,11 @@ SV_API const char *sv_launch_name(int32_t B, int32_t gamma, int32_t V, int32_t d
  *   draft_logits [B][gamma][V] of dtype `dtype` (device); draft_tokens
  *   [B][gamma] int32 (device, caller-owned).  No workspace; nothing is
  *   allocated.  Errors: SV_EINVAL for null pointers, a bad shape or dtype,
- *   temperature not finite or < 0, misaligned pointers; SV_EHIP for a failed
- *   launch.  Enqueued on `stream`, never synchronises. */
+ *   temperature not finite or < 0, top_p NaN or on without a top-k it can
+ *   cut, misaligned pointers; SV_EHIP for a failed launch.  Enqueued on
+ *   `stream`, never synchronises. */
 SV_API sv_status sv_draft_sample(const void *draft_logits, int32_t B, int32_t gamma, int32_t V, int32_t dtype,
-                          float temperature, int32_t top_k, uint64_t seed, uint64_t seq_offset,
+                          float temperature, int32_t top_k, float top_p, uint64_t seed, uint64_t seq_offset,
                           int32_t *draft_tokens, void *stream);
 
 /* Acceptance counts of a step: hist[0] = sequences flagged invalid

@@ -72,7 +72,7 @@ def load(path: str) -> ctypes.CDLL:
     L.svo_verify.restype = i32
     L.svo_token_probs.argtypes = [vp, vp, vp, i32, i32, i32, i32, flt, i32, flt, i32, vp, vp]
     L.svo_token_probs.restype = i32
-    L.svo_draft_sample.argtypes = [vp, i32, i32, i32, i32, flt, i32, u64, u64, i32, vp, vp]
+    L.svo_draft_sample.argtypes = [vp, i32, i32, i32, i32, flt, i32, flt, u64, u64, i32, vp, vp, vp]
     L.svo_draft_sample.restype = i32
     L.svo_max_threads.argtypes = []
     L.svo_max_threads.restype = i32
@@ -247,18 +247,20 @@ def token_probs(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray, tempe
 
 
 def draft_sample(draft: np.ndarray, temperature: float, top_k: int = 0, seed: int = 0, seq_offset: int = 0,
-                 nthreads: int = 0):
+                 nthreads: int = 0, top_p: float = 1.0, with_margin: bool = False):
     """Draft tokens [B, gamma] drawn from each draft row's adjusted distribution
-    on the DRAFT stream, and the key gap of each draw [B, gamma]."""
+    on the DRAFT stream, and the key gap of each draw [B, gamma] (and the
+    nucleus-cut margin of each row when with_margin)."""
     draft = np.ascontiguousarray(draft)
     B, gamma, V = draft.shape
     tok = np.zeros((B, gamma), dtype=np.int32)
     gap = np.zeros((B, gamma), dtype=np.float64)
-    rc = lib().svo_draft_sample(_ptr(draft), B, gamma, V, _dtype_code(draft), temperature, top_k, seed,
-                                seq_offset, nthreads, _ptr(tok), _ptr(gap))
+    margin = np.zeros((B, gamma), dtype=np.float64)
+    rc = lib().svo_draft_sample(_ptr(draft), B, gamma, V, _dtype_code(draft), temperature, top_k, top_p, seed,
+                                seq_offset, nthreads, _ptr(tok), _ptr(gap), _ptr(margin))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
-    return tok, gap
+    return (tok, gap, margin) if with_margin else (tok, gap)
 
 
 def max_threads() -> int:

@@ -422,12 +422,14 @@ int svo_verify(const void *target, const void *draft, const int32_t *tokens,
 /* Draft tokens: the draft model's own sampling step, which [SDE] "how it     */
 /* works" puts before verification (the small model proposes gamma tokens).  */
 /* Token j of sequence b is drawn from the draft row's adjusted distribution  */
-/* p_j (R1, R2, R9) by the same Gumbel-max as R4 on the DRAFT stream          */
+/* p_j (R1, R2, R9, R10) by the same Gumbel-max as R4 on the DRAFT stream     */
 /* (purpose 2) at (seq = seq_offset + b, pos = j).  gap [B][gamma] (may be    */
-/* NULL): best minus second-best key of the row.                              */
+/* NULL): best minus second-best key of the row; margin [B][gamma] (may be    */
+/* NULL): the row's nucleus-cut margin.                                       */
 /* ------------------------------------------------------------------------ */
 int svo_draft_sample(const void *draft, int B, int gamma, int V, int dtype, float temperature, int top_k,
-                     uint64_t seed, uint64_t seq_offset, int nthreads, int32_t *tokens, double *gap)
+                     float top_p, uint64_t seed, uint64_t seq_offset, int nthreads, int32_t *tokens, double *gap,
+                     double *margin)
 {
     if (!draft || !tokens || B < 1 || gamma < 1 || V < 2) return -1;
     if (dtype != SVO_F32 && dtype != SVO_BF16) return -1;
@@ -446,7 +448,9 @@ int svo_draft_sample(const void *draft, int B, int gamma, int V, int dtype, floa
         for (int b = 0; b < B; ++b)
             for (int j = 0; j < gamma; ++j) {
                 const char *prow = (const char *)draft + ((size_t)b * gamma + j) * V * esz;
-                svo_row_probs(prow, dtype, V, temperature, top_k, p, keep);
+                double mg = INFINITY;
+                svo_row_probs_p(prow, dtype, V, temperature, top_k, top_p, p, keep, &mg);
+                if (margin) margin[(size_t)b * gamma + j] = mg;
                 double g = INFINITY;
                 tokens[(size_t)b * gamma + j] =
                     svo_gumbel_draw(p, V, seed, seq_offset + (uint64_t)b, (uint32_t)j, SVO_DRAFT, &g);

@@ -54,7 +54,7 @@ def lib() -> ctypes.CDLL:
                 L.sv_verify_timed.restype = i32
                 L.sv_launch_name.argtypes = [i32, i32, i32, i32, i32, flt, i32]
                 L.sv_launch_name.restype = ctypes.c_char_p
-                L.sv_draft_sample.argtypes = [vp, i32, i32, i32, i32, flt, i32, u64, u64, vp, vp]
+                L.sv_draft_sample.argtypes = [vp, i32, i32, i32, i32, flt, i32, flt, u64, u64, vp, vp]
                 L.sv_draft_sample.restype = i32
                 L.sv_accept_histogram.argtypes = [vp, i32, i32, vp, vp]
                 L.sv_accept_histogram.restype = i32
@@ -220,7 +220,7 @@ def verify_timed(target, draft, tokens, temperature: float, events, top_k: int =
 
 
 def draft_sample(draft, temperature: float, top_k: int = 0, seed: int = 0, seq_offset: int = 0, out=None,
-                 stream=None):
+                 stream=None, top_p: float = 1.0):
     """sv_draft_sample: draft tokens [B, gamma] int32 drawn on the GPU from the
     draft rows [B, gamma, V] (float32 or bfloat16, contiguous)."""
     torch = _torch()
@@ -232,7 +232,7 @@ def draft_sample(draft, temperature: float, top_k: int = 0, seed: int = 0, seq_o
     if out is None:
         out = torch.empty((B, gamma), dtype=torch.int32, device=dev)
     with torch.cuda.device(dev):
-        st = lib().sv_draft_sample(draft.data_ptr(), B, gamma, V, dt, float(temperature), int(top_k),
+        st = lib().sv_draft_sample(draft.data_ptr(), B, gamma, V, dt, float(temperature), int(top_k), float(top_p),
                                    int(seed) & 0xFFFFFFFFFFFFFFFF, int(seq_offset) & 0xFFFFFFFFFFFFFFFF,
                                    out.data_ptr(), _stream_ptr(dev, stream))
     if st != SV_OK:

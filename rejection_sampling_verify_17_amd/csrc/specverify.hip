@@ -365,11 +365,14 @@ const char *sv_launch_name(int32_t B, int32_t gamma, int32_t V, int32_t dtype, i
 }
 
 sv_status sv_draft_sample(const void *draft_logits, int32_t B, int32_t gamma, int32_t V, int32_t dtype,
-                          float temperature, int32_t top_k, uint64_t seed, uint64_t seq_offset, int32_t *draft_tokens,
-                          void *stream) {
+                          float temperature, int32_t top_k, float top_p, uint64_t seed, uint64_t seq_offset,
+                          int32_t *draft_tokens, void *stream) {
   if (!draft_logits || !draft_tokens) return SV_EINVAL;
   if (!shape_ok(B, gamma, V, dtype)) return SV_EINVAL;
   if (!std::isfinite(temperature) || !(temperature >= 0.0f)) return SV_EINVAL;
+  if (std::isnan(top_p)) return SV_EINVAL;
+  const bool nucleus = temperature != 0.0f && top_p > 0.0f && top_p < 1.0f;
+  if (nucleus && !(top_k > 0 && top_k <= kListMax && top_k < V)) return SV_EINVAL;
   const uintptr_t elem = dtype == SV_BF16 ? 2 : 4;
   if (((uintptr_t)draft_logits % elem) || ((uintptr_t)draft_tokens % 4)) return SV_EINVAL;
   if ((long long)B * gamma > 0x7FFFFFFFLL) return SV_EINVAL;
@@ -380,6 +383,7 @@ sv_status sv_draft_sample(const void *draft_logits, int32_t B, int32_t gamma, in
   a.gamma = gamma;
   a.V = V;
   a.top_k = (!argmax && top_k > 0 && top_k < V) ? top_k : 0;
+  a.top_p = nucleus ? top_p : 1.0f;
   a.c = argmax ? 0.0f : (float)(1.4426950408889634 / (double)temperature);
   a.argmax = argmax ? 1 : 0;
   a.key0 = (uint32_t)seed;

@@ -13,8 +13,9 @@
 // (E2 = E / ln 2, the exponential variate in base 2); ties go to the smaller
 // index.  Without top-k every entry is kept and the row is read once, in
 // groups of four entries that share one Philox block; with top-k the exact
-// K-th largest key comes from the top-k path's select and only the kept
-// entries draw variates.  T = 0 (arg-max mode): the first largest logit.
+// K-th largest key comes from the top-k path's select (then the nucleus cut,
+// when on) and only the kept entries draw variates.  T = 0 (arg-max mode):
+// the first largest logit.
 //
 // k_accept_hist: one block counts n_accepted into gamma + 2 bins.
 #pragma once
@@ -69,7 +70,8 @@ __global__ __launch_bounds__(kTopkThreads) void k_draft_sample(Args a) {
       best = k > best ? k : best;
     });
   } else if (a.top_k > 0) {
-    const Selected sel = select_threshold(sh, src, a.top_k);
+    // kept set: the exact top-K threshold, raised by the nucleus cut when on
+    const TopkRow sel = topk_row(sh, src, a.top_k, a.c, a.top_p, nullptr);
     auto consider = [&](float z, uint32_t v) {
       if (z == -INFINITY || entry_key(z, v) < sel.thr) return;
       const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)j, v >> 2, PURPOSE_DRAFT);

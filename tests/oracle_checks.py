@@ -423,10 +423,10 @@ def check_draft_sampler(n: int = 200_000, seed: int = 41):
     rng = np.random.default_rng(seed)
     V = 64
     z = rng.normal(0, 2, V).astype(np.float32)
-    for T, K in ((1.0, 0), (0.7, 5), (1.3, 40)):
+    for T, K, P in ((1.0, 0, 1.0), (0.7, 5, 1.0), (1.3, 40, 1.0), (1.0, 30, 0.8)):
         rows = np.broadcast_to(z, (n, 1, V)).copy()
-        tok, gap = O.draft_sample(rows, T, K, seed=seed + 1)
-        p = O.row_probs(z, T, K)
+        tok, gap = O.draft_sample(rows, T, K, seed=seed + 1, top_p=P)
+        p = O.row_probs(z, T, K, P)
         counts = np.bincount(tok[:, 0], minlength=V)
         assert np.all(counts[p == 0] == 0), (T, K)
         pv = chi2_pvalue(counts, p)

@@ -117,14 +117,14 @@ def test_product_path_does_not_touch_the_oracle():
 @pytest.mark.parametrize("over", [
     dict(draft=None), dict(out=None), dict(B=0), dict(gamma=0), dict(gamma=65), dict(V=1), dict(dtype=3),
     dict(T=-1.0), dict(T=float("nan")), dict(T=float("inf")), dict(draft=0x200002), dict(out=0x400002),
-    dict(dtype=1, draft=0x200001),
+    dict(dtype=1, draft=0x200001), dict(P=float("nan")), dict(P=0.9), dict(P=0.9, K=1000),
 ], ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
 def test_draft_sample_invalid_arguments(L, over):
-    args = dict(draft=0x200000, B=4, gamma=3, V=1000, dtype=0, T=1.0, K=0, seed=1, off=0, out=0x400000,
+    args = dict(draft=0x200000, B=4, gamma=3, V=1000, dtype=0, T=1.0, K=0, P=1.0, seed=1, off=0, out=0x400000,
                 stream=None)
     args.update(over)
     assert L.sv_draft_sample(args["draft"], args["B"], args["gamma"], args["V"], args["dtype"], args["T"],
-                             args["K"], args["seed"], args["off"], args["out"], args["stream"]) == 1
+                             args["K"], args["P"], args["seed"], args["off"], args["out"], args["stream"]) == 1
 
 
 @pytest.mark.parametrize("over", [dict(n=None), dict(h=None), dict(B=0), dict(gamma=0), dict(gamma=65),

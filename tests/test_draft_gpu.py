@@ -31,20 +31,22 @@ def _draft_tensor(w):
 
 
 def _compare_draft(w, seed, got, seq_offset=0):
-    want, gap = O.draft_sample(w.draft, w.temperature, w.top_k, seed=seed, seq_offset=seq_offset)
+    want, gap, margin = O.draft_sample(w.draft, w.temperature, w.top_k, seed=seed, seq_offset=seq_offset,
+                                       top_p=w.top_p, with_margin=True)
     diff = got != want
-    exempt = diff & (gap < KNIFE) if w.temperature != 0.0 else np.zeros_like(diff)
+    # knife-edges: near-tied best keys, or (top-p) a nucleus cut within rounding
+    exempt = diff & ((gap < KNIFE) | (margin < KNIFE)) if w.temperature != 0.0 else np.zeros_like(diff)
     bad = diff & ~exempt
     _say(f"rows {got.size}, differing {int(diff.sum())}, knife-edge {int(exempt.sum())}")
     assert not bad.any(), f"{int(bad.sum())} draws differ: first at {np.argwhere(bad)[:5].tolist()}"
     if w.top_k > 0 and w.temperature != 0.0:   # every draw lies in the kept set
         for b, j in zip(*np.nonzero(np.ones_like(got, dtype=bool))):
-            if (b * w.gamma + j) % 97 == 0:
-                assert O.row_probs(w.draft[b, j], w.temperature, w.top_k)[got[b, j]] > 0
+            if (b * w.gamma + j) % 97 == 0 and margin[b, j] >= KNIFE:
+                assert O.row_probs(w.draft[b, j], w.temperature, w.top_k, w.top_p)[got[b, j]] > 0
     return want
 
 
-CASES = [("c4b", 64), ("c4b", None), ("c2", 4), ("c3", 8), ("g4b", 32), ("c1", None)]
+CASES = [("c4b", 64), ("c4b", None), ("c2", 4), ("c3", 8), ("c3p", 8), ("g4b", 32), ("c1", None)]
 
 
 @pytest.mark.parametrize("name,B", CASES, ids=[f"{n}-B{b or 'full'}" for n, b in CASES])
@@ -55,7 +57,7 @@ def test_draft_sample_parity(name, B):
     _say(f"case draft {name} B={w.B} gamma={w.gamma} V={w.V} T={w.temperature} K={w.top_k}")
     d = _draft_tensor(w)
     for seed in (7, 8):
-        got = S.draft_sample(d, w.temperature, w.top_k, seed=seed)
+        got = S.draft_sample(d, w.temperature, w.top_k, seed=seed, top_p=w.top_p)
         torch.cuda.synchronize()
         _compare_draft(w, seed, got.cpu().numpy())
 
@@ -74,6 +76,9 @@ def _edge_drafts():
                                                 np.zeros((5, 2), np.int32), temperature=0.9, top_k=30)))
     z2 = rng.normal(0, 1, (40, 1, 2)).astype(np.float32)
     out.append(("V2", I.from_arrays(np.zeros((40, 2, 2), np.float32), z2, np.zeros((40, 1), np.int32))))
+    zt = rng.integers(-3, 4, (6, 3, 500)).astype(np.float32)
+    out.append(("ties-K20-P0.6", I.from_arrays(np.zeros((6, 4, 500), np.float32), zt, np.zeros((6, 3), np.int32),
+                                               top_k=20, top_p=0.6)))
     zi = rng.normal(0, 2, (4, 2, 3000)).astype(np.float32)
     zi[:, :, 100:2900] = -np.inf
     out.append(("neg-inf", I.from_arrays(np.zeros((4, 3, 3000), np.float32), zi, np.zeros((4, 2), np.int32))))
@@ -88,7 +93,7 @@ def test_draft_sample_edges(name, w):
     import torch
     import rejection_sampling_verify_17_amd as S
     _say(f"case draft edge {name} B={w.B} gamma={w.gamma} V={w.V} T={w.temperature} K={w.top_k}")
-    got = S.draft_sample(_draft_tensor(w), w.temperature, w.top_k, seed=3, seq_offset=11)
+    got = S.draft_sample(_draft_tensor(w), w.temperature, w.top_k, seed=3, seq_offset=11, top_p=w.top_p)
     torch.cuda.synchronize()
     _compare_draft(w, 3, got.cpu().numpy(), seq_offset=11)
 

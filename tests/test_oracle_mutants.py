@@ -34,8 +34,9 @@ MUTANTS = [
     ("draft tokens drawn on the SAMPLE stream",
      "svo_gumbel_draw(p, V, seed, seq_offset + (uint64_t)b, (uint32_t)j, SVO_DRAFT, &g)",
      "svo_gumbel_draw(p, V, seed, seq_offset + (uint64_t)b, (uint32_t)j, SVO_SAMPLE, &g)", ["draft"]),
-    ("draft row without temperature", "svo_row_probs(prow, dtype, V, temperature, top_k, p, keep);\n                double g",
-     "svo_row_probs(prow, dtype, V, 1.0f, top_k, p, keep);\n                double g", ["draft"]),
+    ("draft row without temperature",
+     "svo_row_probs_p(prow, dtype, V, temperature, top_k, top_p, p, keep, &mg);\n                if (margin)",
+     "svo_row_probs_p(prow, dtype, V, 1.0f, top_k, top_p, p, keep, &mg);\n                if (margin)", ["draft"]),
     ("nucleus drops the entry that reaches P", "if (cum >= P) { m = i; break; }",
      "if (cum >= P) { m = i - 1; cum = before; break; }", ["nucleus"]),
     ("arg-max ties keep the larger index",
