@@ -292,10 +292,6 @@ sv_status verify_impl(const void *target, const void *draft, const int32_t *toke
   a.gpart = p.greedy ? (unsigned long long *)(ws + p.off_gpart) : nullptr;
   a.gstride = p.gstride;
 
-  // the state and key buffers of the chosen path point into the workspace
-  // (kernels of the top-k and arg-max paths store to them unconditionally)
-  if ((p.topk || p.greedy) && !a.state) return SV_EINVAL;
-  if (p.greedy && !a.gpart) return SV_EINVAL;
   (void)hipGetLastError();  // start from a clean error state
   hipStream_t s = (hipStream_t)stream;
   if (dtype == SV_BF16) return Launches<DT_BF16>::run(a, p, s, events, n_events, n_launches);

@@ -153,6 +153,19 @@ def check_golden_examples():
         np.testing.assert_allclose(r / r.sum(), e["residual"], atol=1e-7, err_msg=e["name"])
 
 
+def check_golden_adjusted():
+    """Hand-worked top-k, nucleus and arg-max distributions (tests/golden)."""
+    with open(os.path.join(GOLDEN, "adjusted_distributions.json")) as f:
+        ex = json.load(f)["examples"]
+    for e in ex:
+        if "probs" in e:
+            z, T = log2_logits(e["probs"]), LN2_T
+        else:
+            z, T = np.asarray(e["logits"], dtype=np.float32), e["temperature"]
+        got = O.row_probs(z, T, e["top_k"], e["top_p"])
+        np.testing.assert_allclose(got, e["expected"], atol=1e-7, err_msg=e["name"])
+
+
 # ---------------------------------------------------------------------------
 # P1: exact enumeration at V = 4, gamma = 1 — the output distribution is q
 # ---------------------------------------------------------------------------

@@ -38,7 +38,7 @@ MUTANTS = [
      "svo_row_probs_p(prow, dtype, V, temperature, top_k, top_p, p, keep, &mg);\n                if (margin)",
      "svo_row_probs_p(prow, dtype, V, 1.0f, top_k, top_p, p, keep, &mg);\n                if (margin)", ["draft"]),
     ("nucleus drops the entry that reaches P", "if (cum >= P) { m = i; break; }",
-     "if (cum >= P) { m = i - 1; cum = before; break; }", ["nucleus"]),
+     "if (cum >= P) { m = i - 1; cum = before; break; }", ["nucleus", "golden_adjusted"]),
     ("arg-max ties keep the larger index",
      "if (svo_logit(row, dtype, v) > svo_logit(row, dtype, best)) best = v;",
      "if (svo_logit(row, dtype, v) >= svo_logit(row, dtype, best)) best = v;", ["greedy"]),
@@ -64,6 +64,8 @@ def _run(check):
         C.check_topk_vs_stable_sort()
     elif check == "draft":
         C.check_draft_sampler(n=100_000)
+    elif check == "golden_adjusted":
+        C.check_golden_adjusted()
     elif check == "nucleus":
         C.check_nucleus()
     elif check == "greedy":

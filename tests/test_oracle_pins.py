@@ -33,6 +33,11 @@ def test_golden_worked_examples():
     C.check_golden_examples()
 
 
+def test_golden_adjusted_distributions():
+    """Hand-worked top-k, nucleus and arg-max rows (tests/golden)."""
+    C.check_golden_adjusted()
+
+
 def test_enumeration_v4_output_equals_q():
     """P1 + P2: exact enumeration over all 2^24 acceptance uniforms."""
     C.check_enumeration_v4()
