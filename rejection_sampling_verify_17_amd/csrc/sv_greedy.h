@@ -22,7 +22,9 @@
 // mismatch).  If the sequence is still alive, the block writes the packed
 // arg-max key of its chunk; the lead block writes the per-sequence state and,
 // when the sequence ended, its outputs.  A last launch without rows only
-// judges.  Rows after a sequence's first rejection are never read.
+// judges.  Rows after a sequence's first rejection are never read.  The first
+// launch has nothing to judge: it reads row 0 of every sequence at once and
+// checks the drafted tokens afterwards.
 //
 // Key of entry v: (orderable(z) << 32) | (2^32 - 1 - v), so the u64 maximum is
 // the largest logit with the smallest index among equals; -0 counts as +0, as
@@ -112,48 +114,54 @@ __global__ __launch_bounds__(kGreedyThreads) void k_greedy_step(Args a, int laun
   if (b >= a.B) return;  // never taken: the grid is B * per_seq
   int32_t *state = a.state;
   int32_t *out = a.out_tokens + (size_t)b * (gamma + 1);
-  if (threadIdx.x < kWave) {
-    int alive;
-    if (launch == 0) {
+  if (launch == 0) {
+    // every sequence is read first (row 0 of an invalid sequence is read
+    // for nothing); the drafted tokens are checked after, so no wave waits
+    // for them before its stream starts
+    const int cv = (a.nvec + nch - 1) / nch;
+    const int v0 = rc * cv;  // window [0, 1): rc is the chunk
+    const unsigned long long key = chunk_argmax<DT>(a, b, 0, v0, min(a.nvec, v0 + cv));
+    if (threadIdx.x == 0) a.gpart[(size_t)b * (gamma + 1) * a.gstride + rc] = key;
+    if (lead && threadIdx.x < kWave) {
       const bool ok = tokens_valid(a, b, lane);
-      if (lead) {
-        for (int k = lane; k < gamma; k += kWave) write_diag(a, b, k, NAN, NAN, NAN, NAN);
-        if (!ok) write_invalid(a, b, lane);
-      }
-      alive = ok;
-    } else {
-      alive = state[(size_t)((launch - 1) & 1) * a.B + b] > 0;
-      if (alive) {
-        // lane l: row p0 + l of the previous window
-        const int nj = w0 - p0;
-        const int j = p0 + lane;
-        unsigned long long key = 0ull;
-        int tok = -1;
-        if (lane < nj) {
-          const unsigned long long *kp = a.gpart + ((size_t)b * (gamma + 1) + j) * a.gstride;
-          for (int c = 0; c < nch_prev; ++c) {
-            const unsigned long long k = kp[c];
-            key = k > key ? k : key;
-          }
-          if (j < gamma) tok = a.tokens[(size_t)b * gamma + j];
+      for (int k = lane; k < gamma; k += kWave) write_diag(a, b, k, NAN, NAN, NAN, NAN);
+      if (!ok) write_invalid(a, b, lane);
+      if (lane == 0) state[b] = ok ? 1 : 0;  // half 0: launch 0
+    }
+    return;
+  }
+  if (threadIdx.x < kWave) {
+    int alive = state[(size_t)((launch - 1) & 1) * a.B + b] > 0;
+    if (alive) {
+      // lane l: row p0 + l of the previous window
+      const int nj = w0 - p0;
+      const int j = p0 + lane;
+      unsigned long long key = 0ull;
+      int tok = -1;
+      if (lane < nj) {
+        const unsigned long long *kp = a.gpart + ((size_t)b * (gamma + 1) + j) * a.gstride;
+        for (int c = 0; c < nch_prev; ++c) {
+          const unsigned long long k = kp[c];
+          key = k > key ? k : key;
         }
-        const int am = key_token(key);
-        const unsigned long long miss = __ballot(lane < nj && (j == gamma || tok != am));
-        if (miss != 0ull) {
-          const int k = __builtin_ctzll(miss);
-          const int n = p0 + k;
-          const int token = __shfl(am, k, kWave);
-          alive = 0;
-          if (lead) {
-            for (int i = lane; i <= gamma; i += kWave) {
-              if (i < n) out[i] = a.tokens[(size_t)b * gamma + i];
-              else if (i == n) out[i] = token;
-              else out[i] = -1;
-            }
-            if (lane == 0) {
-              a.n_accepted[b] = n;
-              a.nseq[b] = n;
-            }
+        if (j < gamma) tok = a.tokens[(size_t)b * gamma + j];
+      }
+      const int am = key_token(key);
+      const unsigned long long miss = __ballot(lane < nj && (j == gamma || tok != am));
+      if (miss != 0ull) {
+        const int k = __builtin_ctzll(miss);
+        const int n = p0 + k;
+        const int token = __shfl(am, k, kWave);
+        alive = 0;
+        if (lead) {
+          for (int i = lane; i <= gamma; i += kWave) {
+            if (i < n) out[i] = a.tokens[(size_t)b * gamma + i];
+            else if (i == n) out[i] = token;
+            else out[i] = -1;
+          }
+          if (lane == 0) {
+            a.n_accepted[b] = n;
+            a.nseq[b] = n;
           }
         }
       }
