@@ -398,3 +398,45 @@ def test_nucleus_edge_cases(name, w):
         _check(PT.compare(w, seed, g), f"nucleus edge {name} seed {seed}")
     if name == "p-equals-q":
         assert np.all(g.n_accepted == w.gamma)
+
+
+# ---------------------------------------------------------------------------
+# Extreme shapes and temperatures, every path
+# ---------------------------------------------------------------------------
+def _extreme_workloads():
+    rng = np.random.default_rng(4242)
+    out = []
+    # many sequences, tiny vocabulary (grids far larger than the chip)
+    t = rng.normal(0, 2, (65536, 3, 16)).astype(np.float32)
+    d = (t[:, :2] + rng.normal(0, 1, (65536, 2, 16))).astype(np.float32)
+    tok = I.sample_rows(d.reshape(-1, 16), 1.0, 0, rng).reshape(65536, 2)
+    out.append(("B65536-V16", I.from_arrays(t, d, tok)))
+    out.append(("B65536-V16-topk3", I.from_arrays(t, d, I.sample_rows(d.reshape(-1, 16), 1.0, 3, rng).reshape(65536, 2),
+                                                  top_k=3)))
+    out.append(("B65536-V16-argmax", I.from_arrays(t, d, np.argmax(d, axis=2).astype(np.int32), temperature=0.0)))
+    # a million-entry vocabulary (4 MB rows; every thread walks many vectors)
+    V = 1 << 20
+    t = rng.normal(0, 3, (2, 3, V)).astype(np.float32)
+    d = (t[:, :2] + rng.normal(0, 1, (2, 2, V))).astype(np.float32)
+    out.append(("V1M", I.from_arrays(t, d, I.sample_rows(d.reshape(-1, V), 1.0, 0, rng).reshape(2, 2))))
+    tb, db = I.f32_to_bf16_bits(t), I.f32_to_bf16_bits(d)
+    out.append(("V1M-bf16-topk40", I.from_arrays(tb, db, I.sample_rows(I.bf16_bits_to_f32(db).reshape(-1, V), 1.0, 40,
+                                                                        rng).reshape(2, 2), top_k=40)))
+    out.append(("V1M-argmax", I.from_arrays(t, d, np.argmax(d, axis=2).astype(np.int32), temperature=0.0)))
+    # temperatures far from 1
+    t = rng.normal(0, 2, (16, 4, 3000)).astype(np.float32)
+    d = (t[:, :3] + rng.normal(0, 0.5, (16, 3, 3000))).astype(np.float32)
+    for T in (0.02, 50.0):
+        out.append((f"T{T}", I.from_arrays(t, d, I.sample_rows(d.reshape(-1, 3000), T, 0, rng).reshape(16, 3),
+                                           temperature=T)))
+    return out
+
+
+EXTREME = _extreme_workloads()
+
+
+@pytest.mark.parametrize("name,w", EXTREME, ids=[e[0] for e in EXTREME])
+def test_extreme_shapes(name, w):
+    _say(f"case extreme {name} B={w.B} gamma={w.gamma} V={w.V} T={w.temperature} K={w.top_k}")
+    g = PT.run_gpu(w, 21, debug=w.B <= 4096)
+    _check(PT.compare(w, 21, g, check_probs=w.B <= 4096), f"extreme {name}")
