@@ -219,6 +219,7 @@ struct Selected {
   unsigned long long thr;
   bool in_lds;
   unsigned int ncand;
+  bool one_wave;  // K <= ncand <= 64 candidates in LDS: thr not computed, one wave finishes the row
 };
 
 template <class Src>
@@ -267,6 +268,8 @@ __device__ __forceinline__ Selected select_threshold(TopkShared &sh, const Src &
   __syncthreads();
   const unsigned int ncand = sh.ncand;
   const bool in_lds = ncand <= (unsigned int)kCap;
+  // a wave can sort this few candidates in registers (topk_row finishes)
+  if (in_lds && ncand <= (unsigned int)kWave && (int)ncand >= K) return Selected{0ull, true, ncand, true};
 
   // Phase D: threshold among the candidates.
   unsigned long long thr;
@@ -287,7 +290,7 @@ __device__ __forceinline__ Selected select_threshold(TopkShared &sh, const Src &
   kmin = sh.red_u[0];
   for (int i = 1; i < kTopkThreads / kWave; ++i) kmin = sh.red_u[i] < kmin ? sh.red_u[i] : kmin;
   __syncthreads();
-  return Selected{kmin, in_lds, ncand};
+  return Selected{kmin, in_lds, ncand, false};
 }
 
 // Base-2 softmax statistics over the kept entries (keys >= thr) of a key set;
@@ -449,6 +452,59 @@ __device__ __forceinline__ void nucleus_cut(TopkShared &sh, const Keys &keys, fl
   __syncthreads();
 }
 
+// Rows whose candidates fit one wave (K <= ncand <= 64): wave 0 sorts them
+// in registers (bitonic network by shuffles, descending); the K-th key is the
+// exact threshold, R comes from the first (largest) logit, S is the sum of
+// the first K weights, the first K entries go to the list, and the nucleus
+// cut, when on, is a prefix sum over the same lanes.  No block barrier but
+// the final broadcast.
+__device__ __forceinline__ TopkRow topk_one_wave(TopkShared &sh, unsigned int ncand, int K, float c, float top_p,
+                                                 int2 *list) {
+  const int tid = threadIdx.x, lane = tid % kWave;
+  if (tid < kWave) {
+    unsigned long long x = lane < (int)ncand ? sh.cand[lane] : 0ull;  // 0 is below every real key
+#pragma unroll
+    for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        const unsigned long long y = __shfl_xor(x, stride, kWave);
+        const bool desc = (lane & size) == 0, lower = (lane & stride) == 0;
+        x = (lower == desc) ? (x > y ? x : y) : (x < y ? x : y);
+      }
+    }
+    const float z = from_orderable((uint32_t)(x >> 32));
+    const float zmax = __shfl(z, 0, kWave);
+    const float R = (zmax == -INFINITY) ? -INFINITY : ceilf(zmax * c);
+    const bool kept = lane < K;
+    const float e = (kept && z != -INFINITY) ? __builtin_amdgcn_exp2f(fmaf(z, c, -R)) : 0.0f;
+    if (list && kept) list[lane] = make_int2((int)(0xFFFFFFFFu - (uint32_t)(x & 0xFFFFFFFFull)), (int)__float_as_uint(z));
+    // prefix sums of the kept weights in the sorted order
+    float s = e;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const float y = __shfl_up(s, off, kWave);
+      if (lane >= off) s += y;
+    }
+    int m = K - 1;
+    if (top_p > 0.0f && top_p < 1.0f) {
+      const float total = __shfl(s, K - 1, kWave);
+      const unsigned long long hit = __ballot(kept && s >= top_p * total);
+      if (hit != 0ull) m = __builtin_ctzll(hit);
+    }
+    const unsigned long long thr = __shfl(x, m, kWave);
+    const float S = __shfl(s, m, kWave);
+    if (lane == 0) {
+      sh.srt[0] = thr;
+      sh.cut_sum = S;
+      sh.red_f[0] = R;
+    }
+  }
+  __syncthreads();
+  const TopkRow r{sh.srt[0], sh.red_f[0], sh.cut_sum, true, ncand};
+  __syncthreads();
+  return r;
+}
+
 // Top-K of a row: exact threshold, statistics over the kept entries, and the
 // kept list when given; then the nucleus cut when 0 < top_p < 1 (the caller
 // guarantees K <= kTopkThreads then).
@@ -456,6 +512,7 @@ template <class Src>
 __device__ __forceinline__ TopkRow topk_row(TopkShared &sh, const Src &src, int K, float c, float top_p,
                                             int2 *list) {
   const Selected sel = select_threshold(sh, src, K);
+  if (sel.one_wave) return topk_one_wave(sh, sel.ncand, K, c, top_p, list);
   TopkRow r = sel.in_lds ? kept_stats(sh, LdsKeys<kTopkThreads>{sh.cand, sel.ncand}, sel.thr, c, list, K)
                          : kept_stats(sh, SrcKeys<Src>{src}, sel.thr, c, list, K);
   r.in_lds = sel.in_lds;
