@@ -306,9 +306,49 @@ def cpu_baseline(w, seed: int, budget_s: float = 12.0) -> dict:
                  top_p=w.top_p)
     t = time.perf_counter() - t0
     return {"value": reps * n * w.gamma / t, "unit": "verified draft positions/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"first {n} of {B} sequences of {w.spec.name}, {reps} verify seeds from {seed}, "
                       f"{t:.1f} s on {cores} threads"}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_one_thread(name: str = "c2", n: int = 4, seed: int = 3000) -> dict:
+    """The oracle on one host thread, the first n sequences of a workload: a
+    per-core figure beside the all-core baseline."""
+    from oracle import oracle as O
+    from rejection_sampling_verify_17_amd import inputs as I
+    w = I.make(name, B=n)
+    t0 = time.perf_counter()
+    O.verify(w.target, w.draft, w.tokens, w.temperature, w.top_k, seed=seed, nthreads=1, top_p=w.top_p)
+    t = time.perf_counter() - t0
+    return {"workload": name, "sequences": n, "seconds": t, "positions_per_s": n * w.gamma / t, "threads": 1}
+
+
+def stream_read_GBps(gib: int = 1) -> float:
+    """Context only: HBM read rate of a plain reduction (torch.sum) over
+    `gib` GiB of float32, averaged over 10 calls."""
+    import torch
+    x = torch.ones((gib << 30) // 4, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        x.sum()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(10):
+        x.sum()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 10
+    del x
+    torch.cuda.empty_cache()
+    return (gib << 30) / dt / 1e9
 
 
 # ---------------------------------------------------------------------------
@@ -466,6 +506,8 @@ def main():
                 "algorithmic_bytes_per_launch": head["dominant_bytes_per_launch"], "avg_launch_us": dom_us,
                 "launches_per_step": head["dominant_launches"]}
     cpu = None if args.no_cpu else cpu_baseline(w, 3000)
+    if cpu is not None:
+        cpu["one_thread"] = cpu_one_thread()
     sweep = []
     if not args.no_sweep:
         for name in SWEEP:
@@ -492,6 +534,7 @@ def main():
         "GBps_step": head["GBps_step"], "frac_peak_step": head["frac_peak_step"],
         "kernels": head["kernels"], "mean_accepted": head["mean_accepted"],
         "roofline": roofline, "cpu_baseline": cpu, "sweep": sweep, "draft_sampling": draft,
+        "context": {"stream_read_GBps_torch_sum_1GiB": None if args.no_sweep else stream_read_GBps()},
         "source_digest": source_digest(),
     }
     print(json.dumps(line))
