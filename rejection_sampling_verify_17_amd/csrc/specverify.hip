@@ -132,6 +132,17 @@ size_t workspace_total(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32
                   make_plan(B, gamma, V, top_k, dtype, true).total);
 }
 
+// End of the top-k window that starts at position w0 < gamma: windows [0, 1),
+// [1, 3), [3, 7), [7, 15), ... (each twice the last); a window that would
+// leave one position over runs to gamma.  With low acceptance few sequences
+// reach the later windows, and a launch over few rows costs about the same as
+// one over many (one block per row), so fewer launches win.
+int topk_window_end(int gamma, int w0) {
+  if (w0 == 0) return 1;
+  const int w1 = 2 * w0 + 1;
+  return gamma - w1 <= 1 ? gamma : w1;
+}
+
 template <int DT>
 struct Launches {
   // Dense: k_rows for the first window, k_rows that judges it in every block
@@ -204,13 +215,11 @@ struct Launches {
         w0 = w1;
       }
     } else {
-      // windows [0, 1), [1, 2), [2, 4), [4, 8), ...: with low acceptance few
-      // sequences reach the wide windows, and a launch over few rows costs
-      // about the same as one over many (one block per row)
+      // one launch per window, then one that judges the last window
       const int G = a.gamma;
-      int launch = 0, p0 = 0, w0 = 0, size = 1;
+      int launch = 0, p0 = 0, w0 = 0;
       while (true) {
-        const int w1 = std::min(G, w0 + size);
+        const int w1 = w0 < G ? topk_window_end(G, w0) : G;
         const int per_seq = w1 > w0 ? 2 * (w1 - w0) : 1;
         before();
         hipLaunchKernelGGL(k_topk_step<DT>, dim3(a.B * per_seq), dim3(kTopkThreads), 0, stream, a, launch++, p0, w0,
@@ -219,7 +228,6 @@ struct Launches {
         if (w0 == G) break;
         p0 = w0;
         w0 = w1;
-        if (p0 > 0) size *= 2;
       }
     }
     if (n_launches) *n_launches = li;
@@ -343,12 +351,8 @@ const char *sv_launch_name(int32_t B, int32_t gamma, int32_t V, int32_t dtype, i
   if (i < 0) return nullptr;
   if (p.greedy) return i <= p.nwin ? "k_greedy_step" : nullptr;
   if (p.topk) {
-    int launches = 1;  // windows [0,1), [1,2), [2,4), ... then the judgement
-    for (int w0 = 0, size = 1; w0 < gamma; ++launches) {
-      const int w1 = std::min(gamma, w0 + size);
-      if (w0 > 0) size *= 2;
-      w0 = w1;
-    }
+    int launches = 1;  // one per window, then the judgement
+    for (int w0 = 0; w0 < gamma; ++launches) w0 = topk_window_end(gamma, w0);
     return i < launches ? "k_topk_step" : nullptr;
   }
   // k_rows for the first window, k_judge unless that window holds every

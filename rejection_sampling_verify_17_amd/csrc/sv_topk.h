@@ -7,8 +7,9 @@
 // largest keys, i.e. all keys >= the K-th largest ("threshold").
 //
 // The drafts are judged left to right; positions are walked in windows
-// [0, 1), [1, 2), [2, 4), [4, 8), ... and k_topk_step(window) runs one block
-// per row of the window (draft and target rows of every position):
+// [0, 1), [1, 3), [3, 7), [7, 15), ... (a window that would leave a single
+// position over runs to gamma) and k_topk_step(window) runs one block per row
+// of the window (draft and target rows of every position):
 //   first window   each block selects its row: threshold by an LDS radix
 //                  select, base-2 softmax statistics (R, S) over the kept
 //                  entries and, for small K, the kept list.

@@ -67,11 +67,16 @@ def test_launch_names(L):
     # large inputs: statistics of position 0 and its judgement, then one launch
     # per further position (each judges its position in place) and one to sample
     assert S.launch_names(1024, 4, 50257, 0, 0) == ["k_rows", "k_judge"] + ["k_rows"] * 4
-    # the top-k path: windows [0,1), [1,2), [2,4), [4,8) of the sequences still
-    # alive, then the judgement of the last window and the draw
-    assert S.launch_names(256, 8, 152064, 1, 50) == ["k_topk_step"] * 5
-    assert S.launch_names(16, 1, 152064, 1, 50) == ["k_topk_step"] * 2
-    assert S.launch_names(4, 3, 152064, 1, 300) == ["k_topk_step"] * 4
+    # the top-k path: windows [0,1), [1,3), [3,7), ... of the sequences still
+    # alive (one that would leave a single position over runs to gamma), then
+    # the judgement of the last window and the draw
+    assert S.launch_names(256, 8, 152064, 1, 50) == ["k_topk_step"] * 4   # [0,1) [1,3) [3,8)
+    assert S.launch_names(16, 1, 152064, 1, 50) == ["k_topk_step"] * 2   # [0,1)
+    assert S.launch_names(4, 3, 152064, 1, 300) == ["k_topk_step"] * 3   # [0,1) [1,3)
+    assert S.launch_names(4, 4, 152064, 1, 300) == ["k_topk_step"] * 3   # [0,1) [1,4)
+    assert S.launch_names(4, 5, 152064, 1, 300) == ["k_topk_step"] * 4   # [0,1) [1,3) [3,5)
+    # [0,1) [1,3) [3,7) [7,15) [15,31) [31,64)
+    assert S.launch_names(2, 64, 2048, 0, 16) == ["k_topk_step"] * 7
     # the arg-max mode (T = 0): windows [0,1), [1,2), [2,4), [4,5) of target
     # rows 0..gamma, then the judgement of the last window; top-k changes nothing
     assert S.launch_names(1024, 4, 50257, 0, 0, 0.0) == ["k_greedy_step"] * 5
