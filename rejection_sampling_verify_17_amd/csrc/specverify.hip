@@ -44,7 +44,7 @@ int compute_units() {
   return n;
 }
 
-constexpr int kMaxWindows = 9;  // windows [0,1), [1,2), [2,4), ... over at most 65 rows
+constexpr int kMaxWindows = 9;  // windows [0,1), [1,3), [3,7), ... over at most 65 rows
 
 struct Plan {
   bool topk, greedy;
@@ -64,6 +64,17 @@ bool shape_ok(int32_t B, int32_t gamma, int32_t V, int32_t dtype) {
 
 // `resident`: k_rows blocks resident at once (the grid of a launch).
 // `greedy`: the arg-max mode (temperature 0), where top-k changes nothing.
+// End of the window that starts at w0 < n when positions 0..n-1 are walked
+// in windows [0, 1), [1, 3), [3, 7), [7, 15), ... (each twice the last); a
+// window that would leave one position over runs to n.  With low acceptance
+// few sequences reach the later windows, and a launch over few rows costs
+// about the same as one over many, so fewer launches win.
+int window_end(int n, int w0) {
+  if (w0 == 0) return 1;
+  const int w1 = 2 * w0 + 1;
+  return n - w1 <= 1 ? n : w1;
+}
+
 Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype, bool greedy,
                int resident = 2048) {
   Plan p{};
@@ -77,13 +88,12 @@ Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype
     // every thread keeps at least kGreedyU vectors; a launch gets about one
     // block per resident slot (dead sequences' blocks return at once)
     p.gstride = std::max(1, p.nvec / (kGreedyThreads * kGreedyU));
-    for (int w0 = 0, size = 1; w0 <= gamma; ++p.nwin) {
-      const int w1 = std::min(gamma + 1, w0 + size);
+    for (int w0 = 0; w0 <= gamma; ++p.nwin) {
+      const int w1 = window_end(gamma + 1, w0);
       const long long rows = (long long)B * (w1 - w0);
       p.gw0[p.nwin] = w0;
       p.gw1[p.nwin] = w1;
       p.gnch[p.nwin] = (int)std::max(1LL, std::min<long long>(p.gstride, (resident + rows - 1) / rows));
-      if (w0 > 0) size *= 2;
       w0 = w1;
     }
   } else if (!p.topk) {
@@ -132,16 +142,6 @@ size_t workspace_total(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32
                   make_plan(B, gamma, V, top_k, dtype, true).total);
 }
 
-// End of the top-k window that starts at position w0 < gamma: windows [0, 1),
-// [1, 3), [3, 7), [7, 15), ... (each twice the last); a window that would
-// leave one position over runs to gamma.  With low acceptance few sequences
-// reach the later windows, and a launch over few rows costs about the same as
-// one over many (one block per row), so fewer launches win.
-int topk_window_end(int gamma, int w0) {
-  if (w0 == 0) return 1;
-  const int w1 = 2 * w0 + 1;
-  return gamma - w1 <= 1 ? gamma : w1;
-}
 
 template <int DT>
 struct Launches {
@@ -219,7 +219,7 @@ struct Launches {
       const int G = a.gamma;
       int launch = 0, p0 = 0, w0 = 0;
       while (true) {
-        const int w1 = w0 < G ? topk_window_end(G, w0) : G;
+        const int w1 = w0 < G ? window_end(G, w0) : G;
         const int per_seq = w1 > w0 ? 2 * (w1 - w0) : 1;
         before();
         hipLaunchKernelGGL(k_topk_step<DT>, dim3(a.B * per_seq), dim3(kTopkThreads), 0, stream, a, launch++, p0, w0,
@@ -352,7 +352,7 @@ const char *sv_launch_name(int32_t B, int32_t gamma, int32_t V, int32_t dtype, i
   if (p.greedy) return i <= p.nwin ? "k_greedy_step" : nullptr;
   if (p.topk) {
     int launches = 1;  // one per window, then the judgement
-    for (int w0 = 0; w0 < gamma; ++launches) w0 = topk_window_end(gamma, w0);
+    for (int w0 = 0; w0 < gamma; ++launches) w0 = window_end(gamma, w0);
     return i < launches ? "k_topk_step" : nullptr;
   }
   // k_rows for the first window, k_judge unless that window holds every

@@ -13,8 +13,9 @@
 // So the token after the kept prefix is always the arg-max of the target row
 // at that position, and every target row is read at most once.
 //
-// Target rows 0..gamma are walked in windows [0, 1), [1, 2), [2, 4), [4, 8),
-// ... (the last one ends at row gamma, the bonus row); k_greedy_step(window)
+// Target rows 0..gamma are walked in windows [0, 1), [1, 3), [3, 7), [7, 15),
+// ... (a window that would leave one row over runs to row gamma, the bonus
+// row, and the last window always ends there); k_greedy_step(window)
 // runs nch blocks per row of the window for every sequence.  Each block first
 // judges the previous window of its sequence (wave 0, lane l: row p0 + l's
 // arg-max merged from the chunk keys of the previous launch, compared with the
@@ -22,9 +23,9 @@
 // mismatch).  If the sequence is still alive, the block writes the packed
 // arg-max key of its chunk; the lead block writes the per-sequence state and,
 // when the sequence ended, its outputs.  A last launch without rows only
-// judges.  Rows after a sequence's first rejection are never read.  The first
-// launch has nothing to judge: it reads row 0 of every sequence at once and
-// checks the drafted tokens afterwards.
+// judges.  Windows after the one that holds a sequence's first mismatch are
+// never read for it.  The first launch has nothing to judge: it reads row 0
+// of every sequence at once and checks the drafted tokens afterwards.
 //
 // Key of entry v: (orderable(z) << 32) | (2^32 - 1 - v), so the u64 maximum is
 // the largest logit with the smallest index among equals; -0 counts as +0, as

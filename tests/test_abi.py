@@ -77,11 +77,13 @@ def test_launch_names(L):
     assert S.launch_names(4, 5, 152064, 1, 300) == ["k_topk_step"] * 4   # [0,1) [1,3) [3,5)
     # [0,1) [1,3) [3,7) [7,15) [15,31) [31,64)
     assert S.launch_names(2, 64, 2048, 0, 16) == ["k_topk_step"] * 7
-    # the arg-max mode (T = 0): windows [0,1), [1,2), [2,4), [4,5) of target
-    # rows 0..gamma, then the judgement of the last window; top-k changes nothing
-    assert S.launch_names(1024, 4, 50257, 0, 0, 0.0) == ["k_greedy_step"] * 5
-    assert S.launch_names(1024, 4, 50257, 0, 50, 0.0) == ["k_greedy_step"] * 5
-    assert S.launch_names(3, 64, 100, 1, 0, 0.0) == ["k_greedy_step"] * 9
+    # the arg-max mode (T = 0): the same windows over target rows 0..gamma
+    # ([0,1), [1,3), [3,5) at gamma = 4), then the judgement of the last
+    # window; top-k changes nothing
+    assert S.launch_names(1024, 4, 50257, 0, 0, 0.0) == ["k_greedy_step"] * 4
+    assert S.launch_names(1024, 4, 50257, 0, 50, 0.0) == ["k_greedy_step"] * 4
+    # [0,1) [1,3) [3,7) [7,15) [15,31) [31,63) [63,65)
+    assert S.launch_names(3, 64, 100, 1, 0, 0.0) == ["k_greedy_step"] * 8
     assert S.launch_names(3, 1, 100, 1, 0, 0.0) == ["k_greedy_step"] * 3
 
 
