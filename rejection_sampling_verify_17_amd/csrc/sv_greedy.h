@@ -36,7 +36,7 @@
 
 namespace sv {
 
-constexpr int kGreedyThreads = 256;
+constexpr int kGreedyThreads = 512;
 constexpr int kGreedyU = 4;  // 16-byte vectors in flight per thread
 
 // Arg-max key of target row j of sequence b over vectors [v0, v1).  Each
