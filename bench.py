@@ -118,7 +118,7 @@ def algorithmic_bytes(w, n_accepted: np.ndarray) -> dict:
 def run_workload(name: str, steps: int, warmup: int, hip: Hip, seed: int = 3000) -> dict:
     import torch
     import rejection_sampling_verify_17_amd as S
-    from rejection_sampling_verify_17_amd import inputs as I
+    from workloads import synth as I
 
     t0 = time.time()
     w = I.make(name)
@@ -226,7 +226,7 @@ def run_draft(name: str, steps: int, warmup: int, hip: Hip, seed: int = 3000) ->
     one Philox word and two logarithms per entry (no top-k)."""
     import torch
     import rejection_sampling_verify_17_amd as S
-    from rejection_sampling_verify_17_amd import inputs as I
+    from workloads import synth as I
     w = I.make(name)
     dev = torch.device("cuda:0")
     copies = max(2, min(8, int(np.ceil((1 << 30) / w.draft.nbytes))))
@@ -325,7 +325,7 @@ def cpu_one_thread(name: str = "c2", n: int = 4, seed: int = 3000) -> dict:
     """The oracle on one host thread, the first n sequences of a workload: a
     per-core figure beside the all-core baseline."""
     from oracle import oracle as O
-    from rejection_sampling_verify_17_amd import inputs as I
+    from workloads import synth as I
     w = I.make(name, B=n)
     t0 = time.perf_counter()
     O.verify(w.target, w.draft, w.tokens, w.temperature, w.top_k, seed=seed, nthreads=1, top_p=w.top_p)

@@ -53,8 +53,15 @@
  *     is empty) or argmax q_gamma.  Draft logits are not read, no random
  *     number is drawn, top_k changes nothing, and token_probs / accept_ur of
  *     sv_verify_debug are all NaN.
- *   Results are a pure function of (inputs, temperature, top_k, seed,
- *   seq_offset): independent of launch geometry and repeatable bit for bit.
+ *   Results are repeatable bit for bit: the same arguments on the same
+ *   device give the same outputs.  The random numbers depend only on (seed,
+ *   seq_offset + b, position, v), so a sub-batch called with the matching
+ *   seq_offset draws exactly what the full batch draws.  The softmax sums are
+ *   fp32, and without top-k a row's sum is split into chunks whose number
+ *   follows the batch size and the device's compute-unit count; a different
+ *   batch size can therefore round p(t), q(t) differently in the last bits,
+ *   which changes a decision only where the acceptance uniform lies within
+ *   that rounding of q(t)/p(t) or two Gumbel keys are that close.
  *
  * Layouts: row-major, contiguous.
  *   target_logits [B][gamma+1][V], draft_logits [B][gamma][V], both of dtype
@@ -117,10 +124,14 @@ SV_API sv_status sv_verify(const void *target_logits, const void *draft_logits,
 
 /* sv_verify plus per-position diagnostics for tests (device outputs, either
  * may be NULL):
- *   token_probs [B][gamma][2] float: p_j(t_j), q_j(t_j) for every j < gamma
- *     (computed for all positions, judged or not);
+ *   token_probs [B][gamma][2] float: p_j(t_j), q_j(t_j) for every judged
+ *     position j (0 .. n_accepted, below gamma);
  *   accept_ur [B][gamma][2] float: the acceptance uniform u_j and the ratio
- *     q_j(t_j)/p_j(t_j) (+inf when p_j(t_j) = 0) for every j < gamma. */
+ *     q_j(t_j)/p_j(t_j) (+inf when p_j(t_j) = 0, 0 when q_j(t_j) = 0) for
+ *     every judged position j.
+ *   Positions after the first rejection are not judged (their rows need not
+ *   be read) and hold NaN in both arrays; so does every position of an
+ *   invalid sequence and, in the arg-max mode, every position. */
 SV_API sv_status sv_verify_debug(const void *target_logits, const void *draft_logits,
                           const int32_t *draft_tokens,
                           int32_t B, int32_t gamma, int32_t V, int32_t dtype,

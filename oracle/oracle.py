@@ -198,7 +198,7 @@ class OracleResult:
     ratio: np.ndarray        # [B, gamma] q(t)/p(t)            (NaN after the first rejection)
     gap: np.ndarray          # [B] best - second-best key of the sampled row
     flags: np.ndarray        # [B] bit 0: empty residual, q sampled instead
-    margin: np.ndarray       # [B] smallest nucleus-cut margin over the rows used (+inf without top-p)
+    margin: np.ndarray       # [B, gamma+1] nucleus-cut margin of each position used (+inf elsewhere / without top-p)
 
 
 def verify(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray, temperature: float,
@@ -219,7 +219,7 @@ def verify(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray, temperatur
     ratio = np.zeros((B, gamma), dtype=np.float64)
     gap = np.zeros(B, dtype=np.float64)
     flags = np.zeros(B, dtype=np.int32)
-    margin = np.zeros(B, dtype=np.float64)
+    margin = np.zeros((B, gamma + 1), dtype=np.float64)
     rc = lib().svo_verify(_ptr(target), _ptr(draft), _ptr(tokens), B, gamma, V,
                           _dtype_code(target), temperature, top_k, top_p, seed, seq_offset, nthreads,
                           _ptr(out), _ptr(n), _ptr(u), _ptr(ratio), _ptr(gap), _ptr(flags), _ptr(margin))

@@ -325,7 +325,10 @@ void svo_gumbel_sample_many(const double *w, int V, uint64_t seed, uint64_t seq0
 /*   diag_u, diag_ratio [B][gamma]: u and q(t)/p(t) of every judged draft,   */
 /*     NaN where not judged (after the first rejection);                     */
 /*   diag_gap [B]: best minus second-best key of the sampled row;            */
-/*   diag_flags [B]: bit 0 = residual was empty and q was sampled (R6).      */
+/*   diag_flags [B]: bit 0 = residual was empty and q was sampled (R6);      */
+/*   diag_margin [B][gamma+1]: nucleus-cut margin of position j, the smaller  */
+/*     of its two rows' margins (row gamma: the bonus row), for the positions */
+/*     the step used; +inf elsewhere and without top-p.                      */
 /* Returns 0, or -1 on arguments the rule is not defined for.                */
 /* ------------------------------------------------------------------------ */
 int svo_verify(const void *target, const void *draft, const int32_t *tokens,
@@ -361,12 +364,13 @@ int svo_verify(const void *target, const void *draft, const int32_t *tokens,
             if (diag_ratio) for (int j = 0; j < gamma; ++j) diag_ratio[(size_t)b * gamma + j] = NAN;
             if (diag_gap) diag_gap[b] = NAN;
             if (diag_flags) diag_flags[b] = 0;
-            double margin = INFINITY, mg;
+            double *margin = diag_margin ? diag_margin + (size_t)b * (gamma + 1) : NULL;
+            double mg;
 
             int valid = 1;
             for (int j = 0; j < gamma; ++j)
                 if (tok[j] < 0 || tok[j] >= V) valid = 0;
-            if (diag_margin) diag_margin[b] = INFINITY;
+            if (margin) for (int j = 0; j <= gamma; ++j) margin[j] = INFINITY;
             if (!valid) {                                   /* R8 */
                 n_accepted[b] = -1;
                 for (int i = 0; i <= gamma; ++i) out[i] = -1;
@@ -379,9 +383,9 @@ int svo_verify(const void *target, const void *draft, const int32_t *tokens,
                 const char *qrow = (const char *)target + ((size_t)b * (gamma + 1) + j) * V * esz;
                 const char *prow = (const char *)draft + ((size_t)b * gamma + j) * V * esz;
                 svo_row_probs_p(qrow, dtype, V, temperature, top_k, top_p, q, keep, &mg);
-                margin = fmin(margin, mg);
+                if (margin) margin[j] = mg;
                 svo_row_probs_p(prow, dtype, V, temperature, top_k, top_p, p, keep, &mg);
-                margin = fmin(margin, mg);
+                if (margin) margin[j] = fmin(margin[j], mg);
                 const int t = tok[j];
                 const double u = svo_uniform_accept(svo_word(seed, seq, (uint32_t)j, 0u, SVO_ACCEPT));
                 const double ratio = p[t] > 0.0 ? q[t] / p[t] : INFINITY;
@@ -401,7 +405,7 @@ int svo_verify(const void *target, const void *draft, const int32_t *tokens,
                 /* All gamma kept: one more token from target row gamma. */
                 const char *qrow = (const char *)target + ((size_t)b * (gamma + 1) + gamma) * V * esz;
                 svo_row_probs_p(qrow, dtype, V, temperature, top_k, top_p, q, keep, &mg);
-                margin = fmin(margin, mg);
+                if (margin) margin[gamma] = mg;
                 sampled = svo_gumbel_sample(q, V, seed, seq, (uint32_t)gamma, &gap);
             }
 
@@ -411,7 +415,6 @@ int svo_verify(const void *target, const void *draft, const int32_t *tokens,
             for (int i = n + 1; i <= gamma; ++i) out[i] = -1;
             n_accepted[b] = n;
             if (diag_gap) diag_gap[b] = gap;
-            if (diag_margin) diag_margin[b] = margin;
         }
         free(q); free(p); free(r); free(keep);
     }

@@ -3,7 +3,8 @@
 The C ABI (include/specverify.h) is implemented by libspecverify.so, built
 from csrc/ with hipcc for gfx950; this package is its thin torch binding
 (`verify`, `verify_debug`, `verify_timed`, `draft_sample`,
-`accept_histogram`) plus seeded synthetic inputs (`inputs`).
+`accept_histogram`).  Seeded synthetic workloads for tests and the benchmark
+live outside the package, in `workloads/synth.py`.
 """
 from ._binding import (SV_BF16, SV_EHIP, SV_EINVAL, SV_F32, SV_OK, SpecVerifyError, accept_histogram,
                        draft_sample, launch_names, lib, status_string, verify, verify_debug, verify_timed, version,

@@ -235,6 +235,16 @@ struct Launches {
   }
 };
 
+// Every workspace pointer the kernels of the chosen path dereference is set
+// (a pointer left null for one path would otherwise fault on the GPU).
+bool pointers_set(const Args &a, const Plan &p) {
+  if (!a.nseq) return false;
+  if (p.greedy) return a.state && a.gpart && a.gstride >= 1;
+  if (p.topk) return a.state && a.rowinfo && (p.klist == 0 || a.lists);
+  return a.part && a.ztok && a.slist && a.sst && a.tlist && a.lcnt && a.icnt && a.pcnt && a.pbest && a.nch >= 1 &&
+         a.nch_max >= a.nch && a.cs_max >= 1;
+}
+
 sv_status verify_impl(const void *target, const void *draft, const int32_t *tokens, int32_t B, int32_t gamma,
                       int32_t V, int32_t dtype, float temperature, int32_t top_k, float top_p, uint64_t seed,
                       uint64_t seq_offset, int32_t *out_tokens, int32_t *n_accepted, void *workspace,
@@ -256,8 +266,10 @@ sv_status verify_impl(const void *target, const void *draft, const int32_t *toke
   if ((uintptr_t)workspace % kAlign) return SV_EINVAL;
   const Plan p = make_plan(B, gamma, V, top_k, dtype, greedy, kSlotsPerCU * compute_units());
   if (workspace_bytes < p.total) return SV_EINVAL;
-  // overflow guard for the arg-max grid (B * rows * chunks blocks)
+  // overflow guards for grids that scale with B: the arg-max grid (B * rows
+  // * chunks blocks) and the top-k grid (B * 2 * window blocks, window <= gamma)
   if (greedy && (long long)B * (gamma + 1) * p.gstride > 0x7FFFFFFFLL) return SV_EINVAL;
+  if (p.topk && (long long)B * 2 * gamma > 0x7FFFFFFFLL) return SV_EINVAL;
   if (events && n_events < 0) return SV_EINVAL;
 
   char *ws = (char *)workspace;
@@ -299,6 +311,8 @@ sv_status verify_impl(const void *target, const void *draft, const int32_t *toke
   a.klist = p.klist;
   a.gpart = p.greedy ? (unsigned long long *)(ws + p.off_gpart) : nullptr;
   a.gstride = p.gstride;
+
+  if (!pointers_set(a, p)) return SV_EINVAL;
 
   (void)hipGetLastError();  // start from a clean error state
   hipStream_t s = (hipStream_t)stream;

@@ -208,13 +208,20 @@ __device__ __forceinline__ float4 load_coherent(const float4 *p) {
   return make_float4(load_coherent(f), load_coherent(f + 1), load_coherent(f + 2), load_coherent(f + 3));
 }
 
-// Called by one thread after its coherent stores: waits until they are
-// performed, then counts one more finished item.  True for the caller whose
-// item completes `target`; that caller may then read every other item's
-// stores with coherent loads.
-__device__ __forceinline__ bool count_finished(int32_t *ctr, int target) {
+// Waits until every memory operation this wave issued is performed (vmcnt,
+// expcnt and lgkmcnt all zero).  Results published with agent-scope atomic
+// stores are then visible to every block of the agent, and a counter bumped
+// after this wait can announce them: the agent-scope release sequence of the
+// LLVM AMDGPU memory model for gfx942/gfx950 is an L2 write-back followed by
+// this same wait before the releasing operation; the write-back is not
+// needed here because everything published was itself stored with the
+// agent-coherent bit.  The empty asm statements keep the compiler from
+// moving memory accesses across the wait (the builtin itself is not a
+// memory barrier to the compiler).
+__device__ __forceinline__ void wait_performed() {
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0);
-  return __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == target - 1;
+  asm volatile("" ::: "memory");
 }
 
 // ---------------------------------------------------------------------------
@@ -318,6 +325,17 @@ __device__ float4 chunk_stats(const Args &a, int b, int j, int v0, int v1) {
   return make_float4(Rp, Sp, Rq, Sq);
 }
 
+// Residual weight q_v - p_v from the two unnormalised weights and the rows'
+// reciprocal sums.  Both products are rounded before the subtraction: fused
+// into one FMA, identical rows would leave the rounding error of q_v instead
+// of the exact zero of max(0, q - p), and an empty residual would look full.
+__device__ __forceinline__ float residual_weight(float eq, float invSq, float ep, float invSp) {
+#pragma clang fp contract(off)
+  const float qv = eq * invSq;
+  const float pv = ep * invSp;
+  return qv - pv;
+}
+
 // Gumbel-max winner over group blocks [g0, g1) of row `pos`: the residual
 // weights max(0, q - p) (statistics st of that row pair) when RESID, else the
 // bonus row (weights q).  Residual key r / E2 (the exponential race, monotone
@@ -360,9 +378,8 @@ __device__ unsigned long long chunk_winner(const Args &a, int b, int pos, float4
           const float E2 = exp2_variate(blk.w[e]);
           bool take;
           if (RESID) {
-            const float qv = __builtin_amdgcn_exp2f(fmaf(zq[u][g * 4 + e], c, -st.z)) * invSq;
-            const float pv = __builtin_amdgcn_exp2f(fmaf(zp[u][g * 4 + e], c, -st.x)) * invSp;
-            const float r = qv - pv;
+            const float r = residual_weight(__builtin_amdgcn_exp2f(fmaf(zq[u][g * 4 + e], c, -st.z)), invSq,
+                                            __builtin_amdgcn_exp2f(fmaf(zp[u][g * 4 + e], c, -st.x)), invSp);
             take = idx < lim && r * bestE > bestr * E2;  // r / E2 > bestr / bestE (and r > 0)
             bestr = take ? r : bestr;
             bestE = take ? E2 : bestE;
@@ -717,7 +734,7 @@ __global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int launch, int w0
     const int t = threadIdx.x;
     if (t < nq && q_row[t] >= 0)
       __hip_atomic_fetch_max(a.pbest + q_b[t], q_w[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);  // every wave: its coherent stores and maxima are performed
+    wait_performed();  // every wave: its coherent stores and maxima are performed
     __syncthreads();
     if (t < nq) {
       const int b = q_b[t];

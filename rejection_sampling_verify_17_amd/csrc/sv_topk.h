@@ -62,8 +62,11 @@ struct TopkShared {
   float cut_sum;
 };
 
+// -0 is keyed as +0: equal logits, so the smaller index ranks first, as in an
+// ordinary floating-point comparison.
 __device__ __forceinline__ unsigned long long entry_key(float z, uint32_t v) {
-  return ((unsigned long long)orderable(z) << 32) | (unsigned long long)(0xFFFFFFFFu - v);
+  const float zc = z == 0.0f ? 0.0f : z;
+  return ((unsigned long long)orderable(zc) << 32) | (unsigned long long)(0xFFFFFFFFu - v);
 }
 
 // Radix select, most significant byte first: the K-th largest (1-based, with
@@ -240,9 +243,13 @@ __device__ __forceinline__ Selected select_threshold(TopkShared &sh, const Src &
 
   // Phase B: lower bound L = K-th largest per-thread maximum: K threads own an
   // entry >= L each, so the K-th largest logit of the row is >= L.
+  // The select may clear low bits of L (still a lower bound as an integer).
+  // Every bound at or below orderable(-inf), including 0 (fewer than K
+  // threads hold entries), admits every entry: cleared bits there would not
+  // decode to a float.
   unsigned int L = 0u;
   if (K <= kTopkThreads) L = (unsigned int)(radix_select<kTopkThreads>(sh, LdsMax32<kTopkThreads>{sh.tmax}, (unsigned)K, 64, 32) >> 32);
-  const bool take_all = L == 0u;
+  const bool take_all = L <= orderable(-INFINITY);
   const float Lf = take_all ? -INFINITY : from_orderable(L);
 
   // Phase C (a second pass): gather every entry with logit >= L into LDS as
@@ -268,7 +275,9 @@ __device__ __forceinline__ Selected select_threshold(TopkShared &sh, const Src &
   }
   __syncthreads();
   const unsigned int ncand = sh.ncand;
-  const bool in_lds = ncand <= (unsigned int)kCap;
+  // fewer than K candidates cannot happen with a true lower bound; should it,
+  // the select runs over the row itself rather than over too few keys
+  const bool in_lds = ncand <= (unsigned int)kCap && ncand >= (unsigned int)K;
   // a wave can sort this few candidates in registers (topk_row finishes)
   if (in_lds && ncand <= (unsigned int)kWave && (int)ncand >= K) return Selected{0ull, true, ncand, true};
 
@@ -295,8 +304,13 @@ __device__ __forceinline__ Selected select_threshold(TopkShared &sh, const Src &
 }
 
 // Base-2 softmax statistics over the kept entries (keys >= thr) of a key set;
-// writes the kept entries to `list` when given.
-template <class Keys>
+// writes the kept entries to `list` when given.  FIXED: the keys sit in LDS in
+// the order the gather's atomics handed out slots, which varies from run to
+// run, so S is summed in 64-bit fixed point (every weight 2^(z c - R) is in
+// (0, 1] and at most kCap of them are kept: scale 2^40, truncation below
+// 2^-29 of S >= 1/2 in all) and the sum does not depend on that order.  A row
+// scan visits its entries in a fixed order and sums in fp32.
+template <bool FIXED, class Keys>
 __device__ __forceinline__ TopkRow kept_stats(TopkShared &sh, const Keys &keys, unsigned long long thr, float c,
                                               int2 *list, int K) {
   const int tid = threadIdx.x;
@@ -313,10 +327,15 @@ __device__ __forceinline__ TopkRow kept_stats(TopkShared &sh, const Keys &keys, 
   __syncthreads();
   const float R = (zmax == -INFINITY) ? -INFINITY : ceilf(zmax * c);
   float S = 0.0f;
+  unsigned long long Sfix = 0ull;
   keys.for_each([&](unsigned long long key) {
     if (key >= thr) {
       const float z = from_orderable((uint32_t)(key >> 32));
-      if (z != -INFINITY) S += __builtin_amdgcn_exp2f(fmaf(z, c, -R));
+      if (z != -INFINITY) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(z, c, -R));
+        if (FIXED) Sfix += (unsigned long long)(e * 0x1p40f);
+        else S += e;
+      }
       if (list) {
         const unsigned int slot = atomicAdd(&sh.nkept, 1u);  // exactly K kept entries
         if (slot < (unsigned int)K)
@@ -324,11 +343,21 @@ __device__ __forceinline__ TopkRow kept_stats(TopkShared &sh, const Keys &keys, 
       }
     }
   });
-  S = wave_sum_f(S);
-  if ((tid % kWave) == 0) sh.red_f[tid / kWave] = S;
-  __syncthreads();
-  S = 0.0f;
-  for (int i = 0; i < kTopkThreads / kWave; ++i) S += sh.red_f[i];
+  if (FIXED) {
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) Sfix += __shfl_xor(Sfix, off, kWave);
+    if ((tid % kWave) == 0) sh.red_u[tid / kWave] = Sfix;
+    __syncthreads();
+    Sfix = 0ull;
+    for (int i = 0; i < kTopkThreads / kWave; ++i) Sfix += sh.red_u[i];
+    S = (float)Sfix * 0x1p-40f;
+  } else {
+    S = wave_sum_f(S);
+    if ((tid % kWave) == 0) sh.red_f[tid / kWave] = S;
+    __syncthreads();
+    S = 0.0f;
+    for (int i = 0; i < kTopkThreads / kWave; ++i) S += sh.red_f[i];
+  }
   __syncthreads();
   return TopkRow{thr, R, S, false, 0u};
 }
@@ -514,8 +543,8 @@ __device__ __forceinline__ TopkRow topk_row(TopkShared &sh, const Src &src, int 
                                             int2 *list) {
   const Selected sel = select_threshold(sh, src, K);
   if (sel.one_wave) return topk_one_wave(sh, sel.ncand, K, c, top_p, list);
-  TopkRow r = sel.in_lds ? kept_stats(sh, LdsKeys<kTopkThreads>{sh.cand, sel.ncand}, sel.thr, c, list, K)
-                         : kept_stats(sh, SrcKeys<Src>{src}, sel.thr, c, list, K);
+  TopkRow r = sel.in_lds ? kept_stats<true>(sh, LdsKeys<kTopkThreads>{sh.cand, sel.ncand}, sel.thr, c, list, K)
+                         : kept_stats<false>(sh, SrcKeys<Src>{src}, sel.thr, c, list, K);
   r.in_lds = sel.in_lds;
   r.ncand = sel.ncand;
   if (top_p > 0.0f && top_p < 1.0f) {

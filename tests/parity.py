@@ -11,9 +11,9 @@ same Philox streams):
       - the sampled token when the oracle's two best Gumbel keys are within
         1e-5 (a knife-edge arg-max);
   * the rate of non-exempt mismatches is <= 1e-4;
-  * with top-p, a sequence is exempt when one of the oracle's rows it used
-    has its nucleus cut within 1e-5 of flipping (the kept set is decided by
-    an fp32 prefix sum on the GPU);
+  * with top-p, from the first position whose oracle rows have their nucleus
+    cut within 1e-5 of flipping onward (the kept set is decided by an fp32
+    sum on the GPU; the positions before it are still exact);
   * p_j(t_j), q_j(t_j) within 1e-5 relative of the oracle where the oracle's
     value is >= 1e-30, and the acceptance uniforms equal exactly, at every
     position both sides judged; positions the GPU did not judge (after its
@@ -129,8 +129,7 @@ def compare(w, seed: int, g: GpuResult, seq_offset: int = 0, rows=None, nthreads
         for i in range(hi - lo):
             b = lo + i
             rep.sequences += 1
-            if res.margin[i] < KNIFE:
-                rep.exempt_nucleus += 1
+            if _nucleus_edge(rep, w, b, i, res, g):
                 continue
             _compare_seq(rep, w, b, i, res, g)
             if w.temperature == 0.0:
@@ -144,6 +143,26 @@ def compare(w, seed: int, g: GpuResult, seq_offset: int = 0, rows=None, nthreads
                     _compare_probs(rep, w, seed, seq_offset, b, pt[i], qt[i], g, min(n_o, n_g, w.gamma - 1) + 1,
                                    min(n_g + 1, w.gamma))
     return rep
+
+
+def _nucleus_edge(rep: Report, w, b: int, i: int, res, g: GpuResult) -> bool:
+    """A position whose nucleus cut lies within KNIFE of flipping decides that
+    position's acceptance and sample: the sequence is compared exactly up to
+    it and exempt from there (True when exempt)."""
+    n_o = int(res.n_accepted[i])
+    if n_o < 0:
+        return False
+    used = res.margin[i, :n_o + 1]
+    edge = np.flatnonzero(used < KNIFE)
+    if edge.size == 0:
+        return False
+    j0 = int(edge[0])
+    rep.exempt_nucleus += 1
+    n_g = int(g.n_accepted[b])
+    if min(n_g, n_o) < j0 or not np.array_equal(res.out_tokens[i, :j0], g.out_tokens[b, :j0]):
+        rep.mismatches += 1
+        rep.mismatch_examples.append(("prefix-before-nucleus-edge", b, j0, n_o, n_g))
+    return True
 
 
 def _compare_seq(rep: Report, w, b: int, i: int, res, g: GpuResult):

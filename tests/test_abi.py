@@ -105,6 +105,9 @@ def _call(L, **over):
     dict(wsb=16), dict(target=0x100002), dict(dtype=1, draft=0x200001), dict(tokens=0x300002),
     dict(ws=0x600010), dict(P=float("nan")), dict(P=0.9), dict(P=0.9, K=2000), dict(P=0.5, K=1000),
     dict(P=0.9, K=50, ws=None),
+    # grids that would not fit 32 bits: top-k (B * 2 gamma blocks), arg-max
+    # (B * (gamma + 1) * chunks); the workspace size is made to pass
+    dict(B=1 << 25, gamma=64, K=50, wsb=1 << 62), dict(B=1 << 25, gamma=64, T=0.0, wsb=1 << 62),
 ], ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
 def test_invalid_arguments_rejected_before_launch(L, over):
     assert _call(L, **over) == 1  # SV_EINVAL

@@ -11,7 +11,7 @@ import pytest
 
 import parity as PT
 from oracle import oracle as O
-from rejection_sampling_verify_17_amd import inputs as I
+from workloads import synth as I
 
 pytestmark = pytest.mark.gpu
 

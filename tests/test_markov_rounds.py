@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import markov_rounds as M
-from rejection_sampling_verify_17_amd import inputs as I
+from workloads import synth as I
 
 
 def _tv_and_noise(counts: np.ndarray, probs: np.ndarray, seed: int = 3, runs: int = 100):

@@ -8,7 +8,7 @@ import pytest
 
 import oracle_checks as C
 from oracle import oracle as O
-from rejection_sampling_verify_17_amd import inputs as I
+from workloads import synth as I
 
 # (name, text in sv_oracle.c, replacement, checks expected to catch it)
 MUTANTS = [
@@ -35,8 +35,14 @@ MUTANTS = [
      "svo_gumbel_draw(p, V, seed, seq_offset + (uint64_t)b, (uint32_t)j, SVO_DRAFT, &g)",
      "svo_gumbel_draw(p, V, seed, seq_offset + (uint64_t)b, (uint32_t)j, SVO_SAMPLE, &g)", ["draft"]),
     ("draft row without temperature",
-     "svo_row_probs_p(prow, dtype, V, temperature, top_k, top_p, p, keep, &mg);\n                if (margin)",
-     "svo_row_probs_p(prow, dtype, V, 1.0f, top_k, top_p, p, keep, &mg);\n                if (margin)", ["draft"]),
+     "svo_row_probs_p(prow, dtype, V, temperature, top_k, top_p, p, keep, &mg);\n                if (margin) margin[(size_t)b",
+     "svo_row_probs_p(prow, dtype, V, 1.0f, top_k, top_p, p, keep, &mg);\n                if (margin) margin[(size_t)b", ["draft"]),
+    ("token probabilities of p and q swapped",
+     "svo_row_probs_p(qrow, dtype, V, temperature, top_k, top_p, row, keep, NULL);",
+     "svo_row_probs_p(prow, dtype, V, temperature, top_k, top_p, row, keep, NULL);", ["token_probs"]),
+    ("token probabilities without top-k",
+     "svo_row_probs_p(prow, dtype, V, temperature, top_k, top_p, row, keep, NULL);",
+     "svo_row_probs_p(prow, dtype, V, temperature, 0, top_p, row, keep, NULL);", ["token_probs"]),
     ("nucleus drops the entry that reaches P", "if (cum >= P) { m = i; break; }",
      "if (cum >= P) { m = i - 1; cum = before; break; }", ["nucleus", "golden_adjusted"]),
     ("arg-max ties keep the larger index",
@@ -68,6 +74,8 @@ def _run(check):
         C.check_golden_adjusted()
     elif check == "nucleus":
         C.check_nucleus()
+    elif check == "token_probs":
+        C.check_golden_token_probs()
     elif check == "greedy":
         C.check_greedy()
     elif check == "philox":

@@ -7,7 +7,7 @@ import pytest
 
 import oracle_checks as C
 from oracle import oracle as O
-from rejection_sampling_verify_17_amd import inputs as I
+from workloads import synth as I
 
 
 def test_philox_matches_rocrand_engine():
@@ -36,6 +36,11 @@ def test_golden_worked_examples():
 def test_golden_adjusted_distributions():
     """Hand-worked top-k, nucleus and arg-max rows (tests/golden)."""
     C.check_golden_adjusted()
+
+
+def test_golden_token_probs():
+    """Hand-worked p_j(t_j), q_j(t_j) per position (tests/golden)."""
+    C.check_golden_token_probs()
 
 
 def test_enumeration_v4_output_equals_q():
