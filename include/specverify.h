@@ -44,6 +44,10 @@
  *     otherwise); top_p <= 0 or >= 1 turns it off.  The cut is computed in
  *     fp32: where the mass of a prefix lies within rounding of top_p, the
  *     kept set can differ from an exact computation.
+ *   - the residual max(0, q_n - p_n) is formed from fp32 probabilities; a
+ *     difference at or below 2^-16 of q_n(v) is taken as zero (it is within
+ *     the rounding of the two rows' softmax sums), so identical rows give an
+ *     empty residual and the draw falls back to q_n.
  *   - temperature 0 is the arg-max mode (page ai-trend.me, "어떻게 작동하나":
  *     arg-max decoding is sampling from an adjusted distribution): every
  *     distribution is the point mass on its row's largest logit, the smaller

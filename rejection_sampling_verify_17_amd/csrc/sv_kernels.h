@@ -325,15 +325,24 @@ __device__ float4 chunk_stats(const Args &a, int b, int j, int v0, int v1) {
   return make_float4(Rp, Sp, Rq, Sq);
 }
 
-// Residual weight q_v - p_v from the two unnormalised weights and the rows'
-// reciprocal sums.  Both products are rounded before the subtraction: fused
-// into one FMA, identical rows would leave the rounding error of q_v instead
-// of the exact zero of max(0, q - p), and an empty residual would look full.
+// Residual weight max(0, q_v - p_v) as the GPU can resolve it.  q_v and p_v
+// come from fp32 softmax sums whose rounding depends on how a row's entries
+// fall into 16-byte vectors (its address), so two identical rows can differ
+// in the last bits; a difference at or below 2^-16 of q_v (under the 1e-5
+// resolution the results are held to) is rounding, not residual mass, and
+// counts as zero.  An all-zero residual then falls back to q, as it does in
+// exact arithmetic.  The products are rounded before the subtraction (no
+// FMA contraction), so identical statistics give exactly zero.
+__device__ __forceinline__ float residual_weight(float qv, float pv) {
+#pragma clang fp contract(off)
+  const float r = qv - pv;
+  return r > qv * 0x1p-16f ? r : 0.0f;
+}
 __device__ __forceinline__ float residual_weight(float eq, float invSq, float ep, float invSp) {
 #pragma clang fp contract(off)
   const float qv = eq * invSq;
   const float pv = ep * invSp;
-  return qv - pv;
+  return residual_weight(qv, pv);
 }
 
 // Gumbel-max winner over group blocks [g0, g1) of row `pos`: the residual

@@ -630,7 +630,7 @@ __device__ __forceinline__ unsigned long long gumbel_residual_topk(TopkShared &s
     const float qv = kept_prob(qr, zq, v, c);
     if (qv <= 0.0f) return;
     const float pv = kept_prob(pr, P.load_one((int)v), v, c);
-    const float r = qv - pv;
+    const float r = residual_weight(qv, pv);
     if (!(r > 0.0f)) return;
     const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)n, v >> 2, PURPOSE_SAMPLE);
     const unsigned long long k = pack_key(r * __builtin_amdgcn_rcpf(exp2_variate(word_of(blk, v & 3u))), v);
