@@ -78,7 +78,8 @@
  *
  * Ownership: the caller allocates every buffer (device memory of the current
  * HIP device, or memory the device can address).  The library allocates
- * nothing and keeps no state between calls beyond the workspace contents.
+ * nothing and keeps no state between calls beyond the workspace contents
+ * (sv_verify_noalloc's workspace is a fixed buffer inside the library).
  *
  * Workspace: sv_workspace_bytes() bytes of device memory, 256-byte aligned.
  * Its contents before a call do not matter (each call first clears the part
@@ -125,6 +126,29 @@ SV_API sv_status sv_verify(const void *target_logits, const void *draft_logits,
                     uint64_t seed, uint64_t seq_offset,
                     int32_t *out_tokens, int32_t *n_accepted,
                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* sv_verify without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  The workspace is a buffer inside the library,
+ * SV_NOALLOC_WORKSPACE_BYTES of device memory on each GPU the library runs on,
+ * held until the process ends; its address is looked up once per device on
+ * the first call made with that device current.  Same arguments (minus the
+ * workspace), kernels and results as sv_verify.  SV_EINVAL, before anything
+ * is enqueued, when sv_workspace_bytes() of the shape exceeds
+ * SV_NOALLOC_WORKSPACE_BYTES (for example top_k = 1024 at B = 256, gamma = 8),
+ * and for every argument error of sv_verify; SV_EHIP when the buffer's
+ * address cannot be obtained or a launch fails.  Nothing is allocated.  Every
+ * call on one GPU uses that GPU's single buffer: calls that overlap on one
+ * GPU (different streams, or host threads enqueueing at once) race; calls
+ * enqueued one after another on one stream do not.  Each call clears what it
+ * counts in before use, so the buffer's earlier contents do not matter. */
+#define SV_NOALLOC_WORKSPACE_BYTES ((size_t)32 << 20)
+SV_API sv_status sv_verify_noalloc(const void *target_logits, const void *draft_logits,
+                            const int32_t *draft_tokens,
+                            int32_t B, int32_t gamma, int32_t V, int32_t dtype,
+                            float temperature, int32_t top_k, float top_p,
+                            uint64_t seed, uint64_t seq_offset,
+                            int32_t *out_tokens, int32_t *n_accepted, void *stream);
 
 /* sv_verify plus per-position diagnostics for tests (device outputs, either
  * may be NULL):

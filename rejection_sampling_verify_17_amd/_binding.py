@@ -19,6 +19,7 @@ SV_BF16 = 1
 SV_OK = 0
 SV_EINVAL = 1
 SV_EHIP = 2
+NOALLOC_WORKSPACE_BYTES = 32 << 20   # SV_NOALLOC_WORKSPACE_BYTES of include/specverify.h
 
 
 class SpecVerifyError(RuntimeError):
@@ -48,6 +49,8 @@ def lib() -> ctypes.CDLL:
                 L.sv_workspace_bytes.restype = sz
                 L.sv_verify.argtypes = common
                 L.sv_verify.restype = i32
+                L.sv_verify_noalloc.argtypes = [vp, vp, vp, i32, i32, i32, i32, flt, i32, flt, u64, u64, vp, vp, vp]
+                L.sv_verify_noalloc.restype = i32
                 L.sv_verify_debug.argtypes = common + [vp, vp]
                 L.sv_verify_debug.restype = i32
                 L.sv_verify_timed.argtypes = common + [vp, i32, vp]
@@ -191,6 +194,31 @@ def verify(target, draft, tokens, temperature: float, top_k: int = 0, seed: int 
     enqueued on the current stream (no synchronisation)."""
     return _run("sv_verify", target, draft, tokens, temperature, top_k, seed, seq_offset, out_tokens,
                 n_accepted, workspace, stream, (), top_p)
+
+
+def verify_noalloc(target, draft, tokens, temperature: float, top_k: int = 0, seed: int = 0, seq_offset: int = 0,
+                   out_tokens=None, n_accepted=None, stream=None, top_p: float = 1.0):
+    """sv_verify_noalloc: sv_verify on the library's own fixed workspace (no
+    workspace argument; the library allocates nothing).  Pass out_tokens
+    [B, gamma+1] and n_accepted [B] (int32, on the logits' device) to allocate
+    nothing here either.  Calls that overlap on one GPU race (one buffer per
+    GPU)."""
+    torch = _torch()
+    tokens, B, gamma, V = _check(target, draft, tokens)
+    dev = target.device
+    if out_tokens is None:
+        out_tokens = torch.empty((B, gamma + 1), dtype=torch.int32, device=dev)
+    if n_accepted is None:
+        n_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        st = lib().sv_verify_noalloc(
+            target.data_ptr(), draft.data_ptr(), tokens.data_ptr(), B, gamma, V, _dtype_code(target),
+            float(temperature), int(top_k), float(top_p), int(seed) & 0xFFFFFFFFFFFFFFFF,
+            int(seq_offset) & 0xFFFFFFFFFFFFFFFF, out_tokens.data_ptr(), n_accepted.data_ptr(),
+            _stream_ptr(dev, stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_verify_noalloc")
+    return out_tokens, n_accepted
 
 
 def verify_debug(target, draft, tokens, temperature: float, top_k: int = 0, seed: int = 0,

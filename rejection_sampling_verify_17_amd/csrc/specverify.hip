@@ -24,12 +24,18 @@ constexpr int kListMax = 1024;          // top-k lists kept up to this K
 constexpr double kSmallRows = 256e6;    // bytes of all rows below which one launch reads them all
 constexpr int kSlotsPerCU = 8;          // resident k_rows blocks per compute unit
 constexpr size_t kAlign = 256;
+constexpr int kMaxDevices = 64;
+// Workspace of sv_verify_noalloc: a buffer inside the library, one per GPU the
+// library runs on (each device holds its own copy of this array).  Host code
+// never uses the array's name as an address: the device address comes from
+// hipGetSymbolAddress, per device.
+constexpr size_t kStaticWorkspace = SV_NOALLOC_WORKSPACE_BYTES;
+__device__ __align__(256) unsigned char scratch[kStaticWorkspace];
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Compute units of the current device (queried once per device).
 int compute_units() {
-  constexpr int kMaxDevices = 64;
   static std::atomic<int> cached[kMaxDevices];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
@@ -320,6 +326,19 @@ sv_status verify_impl(const void *target, const void *draft, const int32_t *toke
   return Launches<DT_F32>::run(a, p, s, events, n_events, n_launches);
 }
 
+// Device address of `scratch` on the current device: looked up on the first
+// call on that device (with it current) and kept per device; null on failure.
+void *noalloc_workspace() {
+  static std::atomic<void *> addr[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void *p = addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  addr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -336,6 +355,20 @@ sv_status sv_verify(const void *target_logits, const void *draft_logits, const i
   return verify_impl(target_logits, draft_logits, draft_tokens, B, gamma, V, dtype, temperature, top_k, top_p, seed,
                      seq_offset, out_tokens, n_accepted, workspace, workspace_bytes, stream, nullptr, nullptr,
                      nullptr, 0, nullptr);
+}
+
+sv_status sv_verify_noalloc(const void *target_logits, const void *draft_logits, const int32_t *draft_tokens,
+                            int32_t B, int32_t gamma, int32_t V, int32_t dtype, float temperature, int32_t top_k,
+                            float top_p, uint64_t seed, uint64_t seq_offset, int32_t *out_tokens,
+                            int32_t *n_accepted, void *stream) {
+  // shape and size first, so an oversized shape is refused before any HIP call
+  if (!shape_ok(B, gamma, V, dtype)) return SV_EINVAL;
+  if (workspace_total(B, gamma, V, top_k, dtype) > kStaticWorkspace) return SV_EINVAL;
+  void *ws = noalloc_workspace();
+  if (!ws) return SV_EHIP;
+  return verify_impl(target_logits, draft_logits, draft_tokens, B, gamma, V, dtype, temperature, top_k, top_p, seed,
+                     seq_offset, out_tokens, n_accepted, ws, kStaticWorkspace, stream, nullptr, nullptr, nullptr, 0,
+                     nullptr);
 }
 
 sv_status sv_verify_debug(const void *target_logits, const void *draft_logits, const int32_t *draft_tokens,
