@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 HEADLINE = "c4b"
-SWEEP = ["c2", "c3", "c3p", "c4a", "c4c", "c1", "g4b", "g2"]
+SWEEP = ["c2", "c3", "c3p", "c2p", "c4a", "c4c", "c1", "g4b", "g2"]
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "rejection_sampling_verify_17_amd", "csrc")
 
@@ -140,7 +140,7 @@ def run_workload(name: str, steps: int, warmup: int, hip: Hip, seed: int = 3000)
     nacc = torch.empty((w.B,), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = int(stream.cuda_stream)
-    names = S.launch_names(w.B, w.gamma, w.V, dt, w.top_k, w.temperature)
+    names = S.launch_names(w.B, w.gamma, w.V, dt, w.top_k, w.temperature, w.top_p)
     nl = len(names)
 
     def step(i, events=None):
@@ -194,6 +194,7 @@ def run_workload(name: str, steps: int, warmup: int, hip: Hip, seed: int = 3000)
         hip.destroy(e)
 
     n_acc = nacc.cpu().numpy()
+    out_np = out.cpu().numpy()
     ab = algorithmic_bytes(w, n_acc)
     positions = w.B * w.gamma
     dominant = names[0]  # the per-position kernel: every byte of the rows goes through it
@@ -215,7 +216,7 @@ def run_workload(name: str, steps: int, warmup: int, hip: Hip, seed: int = 3000)
     }
     del tgts, drfs
     torch.cuda.empty_cache()
-    return res, w
+    return res, w, (out_np, n_acc)
 
 
 # ---------------------------------------------------------------------------
@@ -281,34 +282,52 @@ def read_traffic(kernel: str, workload: str) -> float | None:
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle, as it stands, on a bounded sample
 # ---------------------------------------------------------------------------
-def cpu_baseline(w, seed: int, budget_s: float = 12.0) -> dict:
-    """The oracle on this host's cores: the first n sequences of the workload
-    (all of them if they fit the budget), repeated until about budget_s of
-    CPU work, reported in verified positions per second."""
+def cpu_baseline(w, seed: int, budget_s: float = 12.0, gpu_out=None) -> dict:
+    """The oracle as it stands on this host's cores, on a bounded sample: the
+    first n sequences of the workload (n sized so one run takes about
+    budget_s / 3; all B if they fit), one warm-up run, then the median of 3
+    timed runs, in verified positions per second.  Its outputs (verify seed
+    `seed`, the seed the timed GPU steps used) are compared with the GPU's
+    outputs for the same sequences (`gpu_out` = (out_tokens, n_accepted) of
+    the last timed step) under the parity bar of tests/parity.py."""
     from oracle import oracle as O
     cores = len(os.sched_getaffinity(0))
     B = w.B
+    target_s = budget_s / 3.0
     n = min(B, max(cores, 8))
     t0 = time.perf_counter()
     O.verify(w.target[:n], w.draft[:n], w.tokens[:n], w.temperature, w.top_k, seed=seed, nthreads=cores,
              top_p=w.top_p)
     t1 = time.perf_counter() - t0
-    if t1 < budget_s / 4 and n < B:
-        n = int(min(B, max(n + 1, n * (budget_s / 2 / max(t1, 1e-3)))))
+    if t1 < target_s / 2 and n < B:
+        n = int(min(B, max(n + 1, n * (target_s / max(t1, 1e-3)))))
+    O.verify(w.target[:n], w.draft[:n], w.tokens[:n], w.temperature, w.top_k, seed=seed, nthreads=cores,
+             top_p=w.top_p)  # warm-up at the final size
+    times = []
+    for r in range(3):
         t0 = time.perf_counter()
-        O.verify(w.target[:n], w.draft[:n], w.tokens[:n], w.temperature, w.top_k, seed=seed, nthreads=cores,
-             top_p=w.top_p)
-        t1 = time.perf_counter() - t0
-    reps = max(1, int(budget_s / max(t1, 1e-3)))
-    t0 = time.perf_counter()
-    for r in range(reps):
         O.verify(w.target[:n], w.draft[:n], w.tokens[:n], w.temperature, w.top_k, seed=seed + r, nthreads=cores,
                  top_p=w.top_p)
-    t = time.perf_counter() - t0
-    return {"value": reps * n * w.gamma / t, "unit": "verified draft positions/s", "cores": cores,
-            "kind": "oracle", "cpu_model": cpu_model(),
-            "sample": f"first {n} of {B} sequences of {w.spec.name}, {reps} verify seeds from {seed}, "
-                      f"{t:.1f} s on {cores} threads"}
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    res = {"value": n * w.gamma / t, "unit": "verified draft positions/s", "cores": cores,
+           "kind": "oracle", "cpu_model": cpu_model(),
+           "sample": f"first {n} of {B} sequences of {w.spec.name}, verify seeds {seed}..{seed + 2}, "
+                     f"median of 3 runs ({', '.join(f'{x:.2f}' for x in times)} s) on {cores} threads"}
+    if gpu_out is not None:
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        try:
+            import parity as PT
+        finally:
+            sys.path.pop(0)
+        from workloads import synth as I
+        ws = I.from_arrays(w.target[:n], w.draft[:n], w.tokens[:n], w.temperature, w.top_k, top_p=w.top_p)
+        g = PT.GpuResult(gpu_out[0][:n], gpu_out[1][:n])
+        rep = PT.compare(ws, seed, g, nthreads=cores, check_probs=False)
+        sm = rep.summary()
+        res["parity_of_timed_outputs"] = {k: sm[k] for k in ("sequences", "mismatches", "exempt_accept",
+                                                             "exempt_token", "exempt_nucleus")}
+    return res
 
 
 def cpu_model() -> str:
@@ -333,22 +352,42 @@ def cpu_one_thread(name: str = "c2", n: int = 4, seed: int = 3000) -> dict:
     return {"workload": name, "sequences": n, "seconds": t, "positions_per_s": n * w.gamma / t, "threads": 1}
 
 
-def stream_read_GBps(gib: int = 1) -> float:
-    """Context only: HBM read rate of a plain reduction (torch.sum) over
-    `gib` GiB of float32, averaged over 10 calls."""
+def stream_read_GBps(hip: Hip, gib: int = 1) -> dict:
+    """Context only: the read rate of a plain streaming kernel of the library
+    (sv_probe_read: contiguous slabs, four 16-byte loads in flight per
+    thread) over `gib` GiB, per grid size, mean of 10 launches timed by HIP
+    events on the launch stream; and, for comparison, torch.sum over the same
+    buffer."""
     import torch
-    x = torch.ones((gib << 30) // 4, dtype=torch.float32, device="cuda")
-    for _ in range(3):
-        x.sum()
+    import rejection_sampling_verify_17_amd as S
+    nbytes = gib << 30
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    out = torch.empty(65536, dtype=torch.float32, device="cuda")
+    sp = int(torch.cuda.current_stream().cuda_stream)
+    e0, e1 = hip.event(), hip.event()
+    rates = {}
+    for grid in (1024, 2048, 4096, 8192, 16384):
+        for _ in range(3):
+            assert S.lib().sv_probe_read(x.data_ptr(), nbytes, out.data_ptr(), grid, sp) == 0
+        hip.record(e0, sp)
+        for _ in range(10):
+            S.lib().sv_probe_read(x.data_ptr(), nbytes, out.data_ptr(), grid, sp)
+        hip.record(e1, sp)
+        hip.sync(e1)
+        rates[str(grid)] = nbytes * 10 / (hip.ms(e0, e1) * 1e-3) / 1e9
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    hip.record(e0, sp)
     for _ in range(10):
         x.sum()
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / 10
-    del x
+    hip.record(e1, sp)
+    hip.sync(e1)
+    torch_sum = nbytes * 10 / (hip.ms(e0, e1) * 1e-3) / 1e9
+    hip.destroy(e0)
+    hip.destroy(e1)
+    del x, out
     torch.cuda.empty_cache()
-    return (gib << 30) / dt / 1e9
+    return {"probe_read_GBps_by_grid": rates, "probe_read_GBps_best": max(rates.values()),
+            "torch_sum_GBps": torch_sum, "bytes": nbytes}
 
 
 # ---------------------------------------------------------------------------
@@ -496,7 +535,7 @@ def main():
         print(json.dumps(run_draft(args.workload, args.steps, args.warmup, hip)))
         return
     print(f"# bench {args.workload}: steps {args.steps} warmup {args.warmup}", file=sys.stderr, flush=True)
-    head, w = run_workload(args.workload, args.steps, args.warmup, hip)
+    head, w, head_out = run_workload(args.workload, args.steps, args.warmup, hip)
     print(f"# {args.workload}: {head['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
     dom = head["dominant"]
     dom_us = head["kernels"][dom]["avg_us"]
@@ -505,19 +544,32 @@ def main():
                 "unit": "GB/s", "frac": head["dominant_GBps"] / HBM_PEAK_GBS, "traffic": traffic,
                 "algorithmic_bytes_per_launch": head["dominant_bytes_per_launch"], "avg_launch_us": dom_us,
                 "launches_per_step": head["dominant_launches"]}
-    cpu = None if args.no_cpu else cpu_baseline(w, 3000)
+    cpu = None if args.no_cpu else cpu_baseline(w, 3000, budget_s=15.0, gpu_out=head_out)
     if cpu is not None:
         cpu["one_thread"] = cpu_one_thread()
+        print(f"# cpu baseline {args.workload}: {cpu['value']:.0f} positions/s; timed-output parity "
+              f"{cpu.get('parity_of_timed_outputs')}", file=sys.stderr, flush=True)
     sweep = []
     if not args.no_sweep:
         for name in SWEEP:
             if name == args.workload:
                 continue
-            r, _ = run_workload(name, max(10, args.steps // 2), max(3, args.warmup // 2), hip)
+            r, wr, rout = run_workload(name, max(10, args.steps // 2), max(3, args.warmup // 2), hip)
             print(f"# {name}: {r['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
-            sweep.append({k: r[k] for k in ("workload", "ms_per_step", "positions_per_s", "GBps_step",
-                                            "frac_peak_step", "dominant", "dominant_GBps", "kernels",
-                                            "mean_accepted", "input_copies")})
+            entry = {k: r[k] for k in ("workload", "ms_per_step", "positions_per_s", "GBps_step",
+                                       "frac_peak_step", "dominant", "dominant_GBps", "kernels",
+                                       "mean_accepted", "input_copies")}
+            entry["roofline"] = {"bound": "hbm", "kernel": r["dominant"], "achieved": r["dominant_GBps"],
+                                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": r["dominant_GBps"] / HBM_PEAK_GBS,
+                                 "traffic": read_traffic(r["dominant"], name),
+                                 "algorithmic_bytes_per_launch": r["dominant_bytes_per_launch"],
+                                 "avg_launch_us": r["kernels"][r["dominant"]]["avg_us"],
+                                 "launches_per_step": r["dominant_launches"]}
+            if not args.no_cpu:
+                entry["cpu_baseline"] = cpu_baseline(wr, 3000, budget_s=3.0, gpu_out=rout)
+                print(f"# cpu baseline {name}: {entry['cpu_baseline']['value']:.0f} positions/s; parity "
+                      f"{entry['cpu_baseline'].get('parity_of_timed_outputs')}", file=sys.stderr, flush=True)
+            sweep.append(entry)
     draft = None
     if not args.no_sweep:
         draft = run_draft(HEADLINE, max(10, args.steps // 2), max(3, args.warmup // 2), hip)
@@ -534,7 +586,7 @@ def main():
         "GBps_step": head["GBps_step"], "frac_peak_step": head["frac_peak_step"],
         "kernels": head["kernels"], "mean_accepted": head["mean_accepted"],
         "roofline": roofline, "cpu_baseline": cpu, "sweep": sweep, "draft_sampling": draft,
-        "context": {"stream_read_GBps_torch_sum_1GiB": None if args.no_sweep else stream_read_GBps()},
+        "context": {"read_stream": None if args.no_sweep else stream_read_GBps(hip)},
         "source_digest": source_digest(),
     }
     print(json.dumps(line))

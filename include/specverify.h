@@ -37,13 +37,14 @@
  *     (seed mod 2^32, seed >> 32), counter (v >> 2, pos, seq mod 2^32,
  *     purpose); the word is output (v mod 4).  seq = seq_offset + b.
  *   - top_p in (0, 1) is nucleus sampling (page ai-trend.me, "어떻게 작동하나"):
- *     after temperature and top-k, a row keeps its entries in the top-k order
- *     (larger logit, then smaller index) until their probability mass
- *     reaches top_p (the entry that reaches it is kept), renormalised; both
- *     p and q.  It needs 0 < top_k <= 1024 and top_k < V (SV_EINVAL
- *     otherwise); top_p <= 0 or >= 1 turns it off.  The cut is computed in
- *     fp32: where the mass of a prefix lies within rounding of top_p, the
- *     kept set can differ from an exact computation.
+ *     after temperature and top-k (if on), a row keeps its entries in the
+ *     top-k order (larger logit, then smaller index) until their probability
+ *     mass reaches top_p (the entry that reaches it is kept), renormalised;
+ *     both p and q, with or without top-k.  top_p <= 0 or >= 1 turns it off.
+ *     The cut is computed in finite precision (fp32 prefix sums for kept
+ *     sets of up to 1024 entries, 64-bit fixed-point masses otherwise):
+ *     where the mass of a prefix lies within rounding of top_p, the kept set
+ *     can differ from an exact computation.
  *   - the residual max(0, q_n - p_n) is formed from fp32 probabilities; a
  *     difference at or below 2^-16 of q_n(v) is taken as zero (it is within
  *     the rounding of the two rows' softmax sums), so identical rows give an
@@ -89,9 +90,9 @@
  *
  * Errors: argument errors return SV_EINVAL before anything is enqueued
  * (null pointer, B < 1, gamma not in [1, 64], V < 2 or V > 2^28, temperature
- * not finite or < 0, top_p NaN, top_p in (0, 1) without 0 < top_k <= 1024 <
- * V, unknown dtype, a logits pointer not aligned to its
- * element size, workspace too small or misaligned).  A failed launch returns
+ * not finite or < 0, top_p NaN, unknown dtype, a logits pointer not aligned
+ * to its element size, workspace too small or misaligned, a grid that would
+ * not fit 32 bits).  A failed launch returns
  * SV_EHIP.  Calls never synchronise.
  */
 #ifndef SPECVERIFY_H
@@ -186,12 +187,11 @@ SV_API sv_status sv_verify_timed(const void *target_logits, const void *draft_lo
 /* Name of kernel launch i of a call with these arguments (for matching event
  * timings to profiler rows); NULL past the last launch. */
 SV_API const char *sv_launch_name(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
-                           int32_t top_k, float temperature, int32_t i);
+                           int32_t top_k, float top_p, float temperature, int32_t i);
 
 /* Draft tokens for a verification step: token j of sequence b drawn on the
  * GPU from the draft row's adjusted distribution p_j = softmax(topk(z) / T)
- * (the same temperature, top-k, top-p and arg-max conventions as sv_verify,
- * top-p again only with 0 < top_k <= 1024 < V), the
+ * (the same temperature, top-k, top-p and arg-max conventions as sv_verify), the
  * step the small model takes before the large one verifies (page ai-trend.me,
  * section "어떻게 작동하나").  The draw is Gumbel-max: the arg-max over the kept
  * entries of ln p_v - ln E_v, E_v = -ln U_v, U_v = (2 * (w >> 9) + 1) * 2^-24,
@@ -201,8 +201,8 @@ SV_API const char *sv_launch_name(int32_t B, int32_t gamma, int32_t V, int32_t d
  *   draft_logits [B][gamma][V] of dtype `dtype` (device); draft_tokens
  *   [B][gamma] int32 (device, caller-owned).  No workspace; nothing is
  *   allocated.  Errors: SV_EINVAL for null pointers, a bad shape or dtype,
- *   temperature not finite or < 0, top_p NaN or on without a top-k it can
- *   cut, misaligned pointers; SV_EHIP for a failed launch.  Enqueued on
+ *   temperature not finite or < 0, top_p NaN, misaligned pointers; SV_EHIP
+ *   for a failed launch.  Enqueued on
  *   `stream`, never synchronises. */
 SV_API sv_status sv_draft_sample(const void *draft_logits, int32_t B, int32_t gamma, int32_t V, int32_t dtype,
                           float temperature, int32_t top_k, float top_p, uint64_t seed, uint64_t seq_offset,
@@ -216,6 +216,29 @@ SV_API sv_status sv_draft_sample(const void *draft_logits, int32_t B, int32_t ga
  * pointers, B < 1 or gamma not in [1, 64]; SV_EHIP for a failed launch. */
 SV_API sv_status sv_accept_histogram(const int32_t *n_accepted, int32_t B, int32_t gamma, int32_t *hist,
                               void *stream);
+
+/* Measurement aids (not part of a verification step).
+ *
+ * sv_probe_read: reads `bytes` (a multiple of 16 is read; the rest ignored)
+ * of device memory at x (16-byte aligned) once, `grid` blocks of 256 threads
+ * each streaming a contiguous slab with four 16-byte loads in flight per
+ * thread, and writes one float per block to out [grid] (device).  Timing it
+ * gives the read rate a plain kernel reaches on this GPU, the context the
+ * verification kernels' rates are read against.
+ *
+ * sv_probe_variates: out[i] (device, n floats) = the exponential variate in
+ * base 2 that the samplers derive from Philox word w = (first + i) << 9, i.e.
+ * -log2(U) for U = (2 (first + i) + 1) 2^-24, computed by the same device
+ * code; first + n <= 2^23 covers every possible U.
+ *
+ * sv_probe_math: out[i] = the native exp2 (op 0) or log2 (op 1) the kernels
+ * use, of x[i] (device arrays of n floats).
+ *
+ * All three: SV_EINVAL for null or misaligned pointers and out-of-range
+ * sizes, SV_EHIP for a failed launch; enqueued on `stream`. */
+SV_API sv_status sv_probe_read(const void *x, size_t bytes, float *out, int32_t grid, void *stream);
+SV_API sv_status sv_probe_variates(uint32_t first, int32_t n, float *out, void *stream);
+SV_API sv_status sv_probe_math(const float *x, int32_t n, int32_t op, float *out, void *stream);
 
 /* Human-readable status. */
 SV_API const char *sv_status_string(sv_status s);

@@ -55,12 +55,18 @@ def lib() -> ctypes.CDLL:
                 L.sv_verify_debug.restype = i32
                 L.sv_verify_timed.argtypes = common + [vp, i32, vp]
                 L.sv_verify_timed.restype = i32
-                L.sv_launch_name.argtypes = [i32, i32, i32, i32, i32, flt, i32]
+                L.sv_launch_name.argtypes = [i32, i32, i32, i32, i32, flt, flt, i32]
                 L.sv_launch_name.restype = ctypes.c_char_p
                 L.sv_draft_sample.argtypes = [vp, i32, i32, i32, i32, flt, i32, flt, u64, u64, vp, vp]
                 L.sv_draft_sample.restype = i32
                 L.sv_accept_histogram.argtypes = [vp, i32, i32, vp, vp]
                 L.sv_accept_histogram.restype = i32
+                L.sv_probe_read.argtypes = [vp, sz, vp, i32, vp]
+                L.sv_probe_read.restype = i32
+                L.sv_probe_variates.argtypes = [ctypes.c_uint32, i32, vp, vp]
+                L.sv_probe_variates.restype = i32
+                L.sv_probe_math.argtypes = [vp, i32, i32, vp, vp]
+                L.sv_probe_math.restype = i32
                 L.sv_status_string.argtypes = [i32]
                 L.sv_status_string.restype = ctypes.c_char_p
                 L.sv_version.argtypes = []
@@ -81,10 +87,11 @@ def workspace_bytes(B: int, gamma: int, V: int, top_k: int, dtype: int) -> int:
     return int(lib().sv_workspace_bytes(B, gamma, V, top_k, dtype))
 
 
-def launch_names(B: int, gamma: int, V: int, dtype: int, top_k: int, temperature: float = 1.0) -> list[str]:
+def launch_names(B: int, gamma: int, V: int, dtype: int, top_k: int, temperature: float = 1.0,
+                 top_p: float = 1.0) -> list[str]:
     out, i = [], 0
     while True:
-        n = lib().sv_launch_name(B, gamma, V, dtype, top_k, float(temperature), i)
+        n = lib().sv_launch_name(B, gamma, V, dtype, top_k, float(top_p), float(temperature), i)
         if n is None:
             return out
         out.append(n.decode())

@@ -3,6 +3,7 @@
 // include/specverify.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -54,6 +55,7 @@ constexpr int kMaxWindows = 9;  // windows [0,1), [1,3), [3,7), ... over at most
 
 struct Plan {
   bool topk, greedy;
+  bool radix;  // top-k path with the mass-weighted nucleus cut (no top-k, or K > kListMax)
   int window;  // positions whose statistics one launch computes (dense path)
   int nch, nch_max, nvec, ngb, cs_max, klist;
   // arg-max mode: windows [gw0, gw1) of target rows with gnch chunks per row
@@ -81,15 +83,19 @@ int window_end(int n, int w0) {
   return n - w1 <= 1 ? n : w1;
 }
 
-Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype, bool greedy,
+// `nucleus`: top-p on (0 < top_p < 1, temperature > 0): the kept sets are cut
+// per row, so the rows go through the top-k path even without top-k.
+Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype, bool greedy, bool nucleus = false,
                int resident = 2048) {
   Plan p{};
   const int ne = dtype == SV_BF16 ? 8 : 4;
   p.nvec = (V + 2 * ne - 2) / ne;  // vectors covering a row at any 16-byte offset
   p.ngb = (V + ne - 1) / ne;       // group blocks of ne entries
   p.greedy = greedy;
-  p.topk = !greedy && top_k > 0 && top_k < V;
-  p.klist = (p.topk && top_k <= kListMax) ? top_k : 0;
+  const bool has_k = top_k > 0 && top_k < V;
+  p.topk = !greedy && (has_k || nucleus);
+  p.klist = (p.topk && has_k && top_k <= kListMax) ? top_k : 0;
+  p.radix = p.topk && nucleus && !(has_k && top_k <= kListMax);
   if (greedy) {
     // every thread keeps at least kGreedyU vectors; a launch gets about one
     // block per resident slot (dead sequences' blocks return at once)
@@ -142,10 +148,11 @@ Plan make_plan(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype
   return p;
 }
 
-// One workspace size serves every temperature.
+// One workspace size serves every temperature and top-p.
 size_t workspace_total(int32_t B, int32_t gamma, int32_t V, int32_t top_k, int32_t dtype) {
-  return std::max(make_plan(B, gamma, V, top_k, dtype, false).total,
-                  make_plan(B, gamma, V, top_k, dtype, true).total);
+  return std::max({make_plan(B, gamma, V, top_k, dtype, false).total,
+                   make_plan(B, gamma, V, top_k, dtype, true).total,
+                   make_plan(B, gamma, V, top_k, dtype, false, true).total});
 }
 
 
@@ -228,8 +235,13 @@ struct Launches {
         const int w1 = w0 < G ? window_end(G, w0) : G;
         const int per_seq = w1 > w0 ? 2 * (w1 - w0) : 1;
         before();
-        hipLaunchKernelGGL(k_topk_step<DT>, dim3(a.B * per_seq), dim3(kTopkThreads), 0, stream, a, launch++, p0, w0,
-                           w1);
+        if (p.radix)
+          hipLaunchKernelGGL((k_topk_step<DT, true>), dim3(a.B * per_seq), dim3(kTopkThreads), 0, stream, a, launch,
+                             p0, w0, w1);
+        else
+          hipLaunchKernelGGL((k_topk_step<DT, false>), dim3(a.B * per_seq), dim3(kTopkThreads), 0, stream, a, launch,
+                             p0, w0, w1);
+        ++launch;
         ok = ok && after();
         if (w0 == G) break;
         p0 = w0;
@@ -261,16 +273,15 @@ sv_status verify_impl(const void *target, const void *draft, const int32_t *toke
   if (!shape_ok(B, gamma, V, dtype)) return SV_EINVAL;
   if (!std::isfinite(temperature) || !(temperature >= 0.0f)) return SV_EINVAL;  // 0: arg-max mode
   const bool greedy = temperature == 0.0f;
-  // nucleus: 0 < top_p < 1 (else off); it cuts the top-k path's kept lists, so
-  // it needs 0 < top_k <= 1024 and top_k < V (the arg-max mode ignores both)
+  // nucleus: 0 < top_p < 1 (else off), with or without top-k (the arg-max
+  // mode ignores both)
   if (std::isnan(top_p)) return SV_EINVAL;
   const bool nucleus = !greedy && top_p > 0.0f && top_p < 1.0f;
-  if (nucleus && !(top_k > 0 && top_k <= kListMax && top_k < V)) return SV_EINVAL;
   const uintptr_t elem = dtype == SV_BF16 ? 2 : 4;
   if (((uintptr_t)target % elem) || ((uintptr_t)draft % elem)) return SV_EINVAL;
   if (((uintptr_t)tokens % 4) || ((uintptr_t)out_tokens % 4) || ((uintptr_t)n_accepted % 4)) return SV_EINVAL;
   if ((uintptr_t)workspace % kAlign) return SV_EINVAL;
-  const Plan p = make_plan(B, gamma, V, top_k, dtype, greedy, kSlotsPerCU * compute_units());
+  const Plan p = make_plan(B, gamma, V, top_k, dtype, greedy, nucleus, kSlotsPerCU * compute_units());
   if (workspace_bytes < p.total) return SV_EINVAL;
   // overflow guards for grids that scale with B: the arg-max grid (B * rows
   // * chunks blocks) and the top-k grid (B * 2 * window blocks, window <= gamma)
@@ -286,7 +297,7 @@ sv_status verify_impl(const void *target, const void *draft, const int32_t *toke
   a.B = B;
   a.gamma = gamma;
   a.V = V;
-  a.top_k = p.topk ? top_k : 0;
+  a.top_k = (p.topk && top_k > 0 && top_k < V) ? top_k : 0;  // 0 on the top-k path: every entry, then the cut
   a.top_p = nucleus ? top_p : 1.0f;
   a.c = greedy ? 0.0f : (float)(1.4426950408889634 / (double)temperature);
   a.key0 = (uint32_t)seed;
@@ -391,10 +402,11 @@ sv_status sv_verify_timed(const void *target_logits, const void *draft_logits, c
                      events, n_events, n_launches);
 }
 
-const char *sv_launch_name(int32_t B, int32_t gamma, int32_t V, int32_t dtype, int32_t top_k, float temperature,
-                           int32_t i) {
+const char *sv_launch_name(int32_t B, int32_t gamma, int32_t V, int32_t dtype, int32_t top_k, float top_p,
+                           float temperature, int32_t i) {
   if (!shape_ok(B, gamma, V, dtype)) return nullptr;
-  const Plan p = make_plan(B, gamma, V, top_k, dtype, temperature == 0.0f);
+  const bool greedy = temperature == 0.0f;
+  const Plan p = make_plan(B, gamma, V, top_k, dtype, greedy, !greedy && top_p > 0.0f && top_p < 1.0f);
   if (i < 0) return nullptr;
   if (p.greedy) return i <= p.nwin ? "k_greedy_step" : nullptr;
   if (p.topk) {
@@ -419,7 +431,6 @@ sv_status sv_draft_sample(const void *draft_logits, int32_t B, int32_t gamma, in
   if (!std::isfinite(temperature) || !(temperature >= 0.0f)) return SV_EINVAL;
   if (std::isnan(top_p)) return SV_EINVAL;
   const bool nucleus = temperature != 0.0f && top_p > 0.0f && top_p < 1.0f;
-  if (nucleus && !(top_k > 0 && top_k <= kListMax && top_k < V)) return SV_EINVAL;
   const uintptr_t elem = dtype == SV_BF16 ? 2 : 4;
   if (((uintptr_t)draft_logits % elem) || ((uintptr_t)draft_tokens % 4)) return SV_EINVAL;
   if ((long long)B * gamma > 0x7FFFFFFFLL) return SV_EINVAL;
@@ -441,8 +452,14 @@ sv_status sv_draft_sample(const void *draft_logits, int32_t B, int32_t gamma, in
   (void)hipGetLastError();
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid((unsigned)(B * gamma));
-  if (dtype == SV_BF16) hipLaunchKernelGGL(k_draft_sample<DT_BF16>, grid, dim3(kTopkThreads), 0, s, a);
-  else hipLaunchKernelGGL(k_draft_sample<DT_F32>, grid, dim3(kTopkThreads), 0, s, a);
+  const bool radix = nucleus && !(a.top_k > 0 && a.top_k <= kListMax);
+  if (dtype == SV_BF16) {
+    if (radix) hipLaunchKernelGGL((k_draft_sample<DT_BF16, true>), grid, dim3(kTopkThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_draft_sample<DT_BF16, false>), grid, dim3(kTopkThreads), 0, s, a);
+  } else {
+    if (radix) hipLaunchKernelGGL((k_draft_sample<DT_F32, true>), grid, dim3(kTopkThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_draft_sample<DT_F32, false>), grid, dim3(kTopkThreads), 0, s, a);
+  }
   return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }
 

@@ -24,36 +24,9 @@
 
 namespace sv {
 
-// Gumbel-max over group blocks [g0, g1) of a row (every entry kept): key
-// z c - log2 E2 with words of `ps`.  Each thread walks its entries in
-// increasing index with a strict comparison (smaller index among equal keys).
-template <int DT, int NT>
-__device__ __forceinline__ unsigned long long gumbel_dense_row(const Row<DT> &R, int V, float c,
-                                                             const PhiloxStream &ps, int g0, int g1) {
-  constexpr int NE = Elem<DT>::kVec;
-  float bestk = -INFINITY;
-  uint32_t besti = 0xFFFFFFFFu;  // none
-  for (int gb = g0 + (int)threadIdx.x; gb < g1; gb += NT) {
-    float z[NE];
-    R.load_block(gb, z);  // entries NE gb .. NE gb + NE - 1; past the row: masked below
-#pragma unroll
-    for (int g = 0; g < NE / 4; ++g) {
-      const uint32_t group = (uint32_t)(gb * (NE / 4) + g);
-      const Philox4 blk = ps.block(group);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t idx = group * 4u + (uint32_t)e;
-        const float key = fmaf(z[g * 4 + e], c, -__builtin_amdgcn_logf(exp2_variate(blk.w[e])));
-        const bool take = idx < (uint32_t)V && key > bestk;
-        bestk = take ? key : bestk;
-        besti = take ? idx : besti;
-      }
-    }
-  }
-  return besti == 0xFFFFFFFFu ? 0ull : pack_key(bestk, besti);
-}
-
-template <int DT>
+// RADIX: the nucleus without top-k or over more than kTopkThreads kept
+// entries (see topk_row).
+template <int DT, bool RADIX>
 __global__ __launch_bounds__(kTopkThreads) void k_draft_sample(Args a) {
   __shared__ TopkShared sh;
   const int row = blockIdx.x;  // b * gamma + j
@@ -69,9 +42,10 @@ __global__ __launch_bounds__(kTopkThreads) void k_draft_sample(Args a) {
       const unsigned long long k = entry_key(z == 0.0f ? 0.0f : z, (uint32_t)v);  // -0 counts as +0
       best = k > best ? k : best;
     });
-  } else if (a.top_k > 0) {
-    // kept set: the exact top-K threshold, raised by the nucleus cut when on
-    const TopkRow sel = topk_row(sh, src, a.top_k, a.c, a.top_p, nullptr);
+  } else if (a.top_k > 0 || a.top_p < 1.0f) {
+    // kept set: the exact top-K threshold (every entry without top-k), raised
+    // by the nucleus cut when on
+    const TopkRow sel = topk_row<RADIX>(sh, src, a.top_k, a.c, a.top_p, nullptr, a.V);
     auto consider = [&](float z, uint32_t v) {
       if (z == -INFINITY || entry_key(z, v) < sel.thr) return;
       const Philox4 blk = stream_block(a.key0, a.key1, seq, (uint32_t)j, v >> 2, PURPOSE_DRAFT);
@@ -85,7 +59,10 @@ __global__ __launch_bounds__(kTopkThreads) void k_draft_sample(Args a) {
         consider(from_orderable((uint32_t)(key >> 32)), 0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
       }
     } else {
-      src.for_each([&](float z, int v) { consider(z, (uint32_t)v); });
+      // a kept set too large for LDS: the dense Gumbel pass over the row,
+      // one Philox block per four entries, entries outside the set skipped
+      const PhiloxStream ps(a.key0, a.key1, seq, (uint32_t)j, PURPOSE_DRAFT);
+      best = gumbel_dense_row<DT, kTopkThreads, true>(P, a.V, a.c, ps, 0, a.ngb, sel.thr);
     }
   } else {
     const PhiloxStream ps(a.key0, a.key1, seq, (uint32_t)j, PURPOSE_DRAFT);

@@ -535,20 +535,196 @@ __device__ __forceinline__ TopkRow topk_one_wave(TopkShared &sh, unsigned int nc
   return r;
 }
 
-// Top-K of a row: exact threshold, statistics over the kept entries, and the
-// kept list when given; then the nucleus cut when 0 < top_p < 1 (the caller
-// guarantees K <= kTopkThreads then).
+// ---------------------------------------------------------------------------
+// Nucleus cut over a large kept set (no top-k, or K > kTopkThreads): the kept
+// entries are not sorted; the cut is found by a radix select weighted by
+// mass.  Masses are 64-bit fixed point, 2^(z c - R) 2^fb with fb = 62 - (bits
+// of V), so the total of at most V weights <= 1 stays below 2^62 and sums do
+// not depend on the order atomics arrive in.  Three passes over the row fix
+// the 32-bit logit key of the entry whose cumulative mass (in the top-k order:
+// larger logit first) first reaches P of the total: each histograms the
+// masses of the kept entries that share the digits fixed so far by the next
+// 11, 11, 10 bits and keeps the digit where the cumulative mass from the top
+// crosses the target.  Among the entries with that logit (equal weights w),
+// the first k by index are kept, k = ceil((target - mass above) / w): a
+// radix select over their indices gives the exact threshold key.
+// ---------------------------------------------------------------------------
+constexpr int kMassBins = kCap;  // the candidate buffer holds the mass histogram
+
+__device__ __forceinline__ unsigned long long mass_fix(float z, float c, float R, float scale) {
+  if (z == -INFINITY) return 0ull;
+  return (unsigned long long)(__builtin_amdgcn_exp2f(fmaf(z, c, -R)) * scale);
+}
+
+// Keys of a source's entries whose logit key (high word) is hw and whose key
+// is at least thr: the ties at the nucleus cut.
+template <class Src> struct TieKeys {
+  const Src &src;
+  uint32_t hw;
+  unsigned long long thr;
+  template <class F> __device__ __forceinline__ void for_each(F f) const {
+    src.for_each([&](float z, int v) {
+      const unsigned long long k = entry_key(z, (uint32_t)v);
+      if ((uint32_t)(k >> 32) == hw && k >= thr) f(k);
+    });
+  }
+};
+
+// Exact K-th largest key of a key set whose bits >= hi agree (K <= its size).
+template <class Keys>
+__device__ __forceinline__ unsigned long long exact_kth(TopkShared &sh, const Keys &keys, unsigned int K, int hi,
+                                                        unsigned long long high) {
+  const unsigned long long t = high | radix_select<kTopkThreads>(sh, keys, K, hi, 0);
+  unsigned long long kmin = ~0ull;
+  keys.for_each([&](unsigned long long key) {
+    if (key >= t) kmin = key < kmin ? key : kmin;
+  });
+  kmin = ~wave_max_u64(~kmin);
+  if ((threadIdx.x % kWave) == 0) sh.red_u[threadIdx.x / kWave] = kmin;
+  __syncthreads();
+  kmin = sh.red_u[0];
+  for (int i = 1; i < kTopkThreads / kWave; ++i) kmin = sh.red_u[i] < kmin ? sh.red_u[i] : kmin;
+  __syncthreads();
+  return kmin;
+}
+
+// R of a row with every entry kept: the reference ceil(max z c).
 template <class Src>
+__device__ __forceinline__ float row_reference(TopkShared &sh, const Src &src, float c) {
+  float zmax = -INFINITY;
+  src.for_each([&](float z, int) { zmax = fmaxf(zmax, z); });
+  zmax = wave_max_f(zmax);
+  if ((threadIdx.x % kWave) == 0) sh.red_f[threadIdx.x / kWave] = zmax;
+  __syncthreads();
+  zmax = sh.red_f[0];
+  for (int i = 1; i < kTopkThreads / kWave; ++i) zmax = fmaxf(zmax, sh.red_f[i]);
+  __syncthreads();
+  return zmax == -INFINITY ? -INFINITY : ceilf(zmax * c);
+}
+
+template <class Src>
+__device__ void nucleus_cut_radix(TopkShared &sh, const Src &src, int V, float c, float P, TopkRow &r) {
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int fb = 62 - (32 - __builtin_clz((unsigned)V));
+  const float scale = ldexpf(1.0f, fb);
+  const unsigned long long thr0 = r.thr;
+  const float R = r.R;
+  unsigned long long *mass = sh.cand;
+  unsigned long long prefix = 0ull, pmask = 0ull;  // key bits fixed so far
+  unsigned long long above = 0ull;                 // mass of kept keys above them
+  unsigned long long target = 0ull;                // P of the total mass, rounded up
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    // digits of the key's high word: bits [53, 64), [42, 53), [32, 42)
+    const int shift = pass == 0 ? 53 : (pass == 1 ? 42 : 32);
+    const int nb = pass < 2 ? 2048 : 1024;
+    const unsigned long long dmask = (unsigned long long)(nb - 1);
+    for (int i = tid; i < kMassBins; i += kTopkThreads) mass[i] = 0ull;
+    __syncthreads();
+    src.for_each([&](float z, int v) {
+      const unsigned long long key = entry_key(z, (uint32_t)v);
+      if (key >= thr0 && (key & pmask) == prefix) {
+        const unsigned long long w = mass_fix(z, c, R, scale);
+        if (w) atomicAdd(&mass[(unsigned)((key >> shift) & dmask)], w);
+      }
+    });
+    __syncthreads();
+    // thread t owns digits nb-1-2t and nb-2-2t (descending); inclusive scan
+    const int dh = nb - 1 - 2 * tid, dl = dh - 1;
+    const unsigned long long mh = dh >= 0 ? mass[dh] : 0ull, ml = dl >= 0 ? mass[dl] : 0ull;
+    unsigned long long incl = mh + ml;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const unsigned long long y = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += y;
+    }
+    if (lane == kWave - 1) sh.red_u[wave] = incl;
+    if (tid == 0) sh.bcast_n = -1;
+    __syncthreads();
+    unsigned long long before = 0ull, total = 0ull;
+    for (int w = 0; w < kTopkThreads / kWave; ++w) {
+      if (w < wave) before += sh.red_u[w];
+      total += sh.red_u[w];
+    }
+    if (pass == 0) {
+      // the cumulative mass must reach P of the total: an integer target; the
+      // row stays valid (uncut) should no crossing be found below
+      unsigned long long t = (unsigned long long)ceil((double)P * (double)total);
+      target = t < 1ull ? 1ull : (t > total ? total : t);
+      r.S = (float)total * ldexpf(1.0f, -fb);
+    }
+    const unsigned long long a0 = above + before + incl - (mh + ml);  // mass of the digits above dh
+    if (dh >= 0 && a0 < target && a0 + mh >= target) {
+      sh.bcast_n = dh;
+      sh.sel_prefix = a0;
+    } else if (dl >= 0 && a0 + mh < target && a0 + mh + ml >= target) {
+      sh.bcast_n = dl;
+      sh.sel_prefix = a0 + mh;
+    }
+    __syncthreads();
+    const int d = sh.bcast_n;
+    const unsigned long long ab = sh.sel_prefix;
+    __syncthreads();
+    if (d < 0) return;  // no crossing (cannot happen: the target lies within the kept mass); keep the row as is
+    prefix |= (unsigned long long)d << shift;
+    pmask |= dmask << shift;
+    above = ab;
+  }
+  // every kept entry with logit key hw weighs w; the first k by index are kept
+  const uint32_t hw = (uint32_t)(prefix >> 32);
+  const unsigned long long w = mass_fix(from_orderable(hw), c, R, scale);
+  if (w == 0ull) return;
+  const unsigned long long need = target - above;
+  unsigned long long k = (need + w - 1ull) / w;
+  if (tid == 0) sh.ncand = 0u;
+  __syncthreads();
+  const TieKeys<Src> ties{src, hw, thr0};
+  ties.for_each([&](unsigned long long key) {
+    const unsigned int slot = atomicAdd(&sh.ncand, 1u);
+    if (slot < (unsigned int)kCap) sh.cand[slot] = key;
+  });
+  __syncthreads();
+  const unsigned int n = sh.ncand;
+  __syncthreads();
+  if (n == 0u) return;
+  if (k > n) k = n;
+  const unsigned long long high = (unsigned long long)hw << 32;
+  const unsigned long long thr = n <= (unsigned int)kCap
+      ? exact_kth(sh, LdsKeys<kTopkThreads>{sh.cand, n}, (unsigned int)k, 32, high)
+      : exact_kth(sh, ties, (unsigned int)k, 32, high);
+  r.thr = thr;
+  r.S = (float)(above + k * w) * ldexpf(1.0f, -fb);
+  r.in_lds = false;
+}
+
+// Kept set of a row: the top-K (0 < K < V; K <= 0: every entry), then the
+// nucleus cut when 0 < top_p < 1.  Exact threshold, statistics over the kept
+// entries, and the top-K list when given (K <= kTopkThreads).  RADIX compiles
+// in the mass-weighted cut that sets without top-k (K <= 0) or larger than
+// kTopkThreads need; it takes many registers, so kernels without it keep two
+// 1024-thread blocks per compute unit.  Without RADIX the caller guarantees
+// 0 < K and, with the nucleus on, K <= kTopkThreads.
+template <bool RADIX, class Src>
 __device__ __forceinline__ TopkRow topk_row(TopkShared &sh, const Src &src, int K, float c, float top_p,
-                                            int2 *list) {
+                                            int2 *list, int V) {
+  const bool nucleus = top_p > 0.0f && top_p < 1.0f;
+  if (RADIX && K <= 0) {
+    // no top-k: every entry is kept before the cut (callers come here only
+    // with the nucleus on; without it the statistics are those of the row)
+    TopkRow r{0ull, row_reference(sh, src, c), 0.0f, false, 0u};
+    if (nucleus) nucleus_cut_radix(sh, src, V, c, top_p, r);
+    return r;
+  }
   const Selected sel = select_threshold(sh, src, K);
   if (sel.one_wave) return topk_one_wave(sh, sel.ncand, K, c, top_p, list);
   TopkRow r = sel.in_lds ? kept_stats<true>(sh, LdsKeys<kTopkThreads>{sh.cand, sel.ncand}, sel.thr, c, list, K)
                          : kept_stats<false>(sh, SrcKeys<Src>{src}, sel.thr, c, list, K);
   r.in_lds = sel.in_lds;
   r.ncand = sel.ncand;
-  if (top_p > 0.0f && top_p < 1.0f) {
-    if (sel.in_lds) nucleus_cut(sh, LdsKeys<kTopkThreads>{sh.cand, sel.ncand}, c, top_p, r);
+  if (nucleus) {
+    if (K > kTopkThreads) {
+      if constexpr (RADIX) nucleus_cut_radix(sh, src, V, c, top_p, r);
+    } else if (sel.in_lds) nucleus_cut(sh, LdsKeys<kTopkThreads>{sh.cand, sel.ncand}, c, top_p, r);
     else nucleus_cut(sh, SrcKeys<Src>{src}, c, top_p, r);
   }
   return r;
@@ -578,6 +754,38 @@ __device__ __forceinline__ unsigned long long block_max_u64_sh(unsigned long lon
   for (int i = 1; i < NT / kWave; ++i) x = red[i] > x ? red[i] : x;
   __syncthreads();
   return x;
+}
+
+// Gumbel-max over group blocks [g0, g1) of a row, over every entry or
+// (MASKED) the entries whose key is at least thr: key z c - log2 E2 with
+// words of `ps`, one Philox block per four entries.  Each thread walks its entries in
+// increasing index with a strict comparison (smaller index among equal keys).
+template <int DT, int NT, bool MASKED = false>
+__device__ __forceinline__ unsigned long long gumbel_dense_row(const Row<DT> &R, int V, float c,
+                                                             const PhiloxStream &ps, int g0, int g1,
+                                                             unsigned long long thr = 0ull) {
+  constexpr int NE = Elem<DT>::kVec;
+  float bestk = -INFINITY;
+  uint32_t besti = 0xFFFFFFFFu;  // none
+  for (int gb = g0 + (int)threadIdx.x; gb < g1; gb += NT) {
+    float z[NE];
+    R.load_block(gb, z);  // entries NE gb .. NE gb + NE - 1; past the row: masked below
+#pragma unroll
+    for (int g = 0; g < NE / 4; ++g) {
+      const uint32_t group = (uint32_t)(gb * (NE / 4) + g);
+      const Philox4 blk = ps.block(group);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t idx = group * 4u + (uint32_t)e;
+        const float key = fmaf(z[g * 4 + e], c, -__builtin_amdgcn_logf(exp2_variate(blk.w[e])));
+        const bool kept = !MASKED || entry_key(z[g * 4 + e], idx) >= thr;
+        const bool take = idx < (uint32_t)V && kept && key > bestk;
+        bestk = take ? key : bestk;
+        besti = take ? idx : besti;
+      }
+    }
+  }
+  return besti == 0xFFFFFFFFu ? 0ull : pack_key(bestk, besti);
 }
 
 // Bonus key of kept entry (z, v) at position pos: z c - log2 E2_v, monotone in
@@ -653,11 +861,11 @@ __device__ __forceinline__ size_t slot_of(const Args &a, int b, int s) {
 // Judge position j of sequence b against its selected rows (every lane of
 // wave 0 computes the same result).
 // Top-k of one global row.
-template <int DT>
+template <int DT, bool RADIX>
 __device__ __forceinline__ TopkRow select_row(TopkShared &sh, const Row<DT> &row, int V, int K, float c, float top_p,
                                               int2 *list) {
   const StreamRow<DT> src(row, V);
-  return topk_row(sh, src, K, c, top_p, list);
+  return topk_row<RADIX>(sh, src, K, c, top_p, list, V);
 }
 
 template <int DT>
@@ -679,8 +887,10 @@ __device__ __forceinline__ Judged judge_topk(const Args &a, int b, int j) {
 // block 0 leads (writes the outputs, draws the token).  Every block first
 // judges the previous window [p0, w0) of its sequence (wave 0, lane l:
 // position p0 + l; a ballot finds the first rejection).
-template <int DT>
-// Two blocks per compute unit (eight waves per SIMD) keep enough rows in flight.
+// Two blocks per compute unit (eight waves per SIMD) keep enough rows in
+// flight; RADIX: the nucleus without top-k or over more than kTopkThreads
+// kept entries (see topk_row).
+template <int DT, bool RADIX>
 __global__ __launch_bounds__(kTopkThreads, 8) void k_topk_step(Args a, int launch, int p0, int w0, int w1) {
   __shared__ TopkShared sh;
   const int dw = w1 - w0;
@@ -753,7 +963,7 @@ __global__ __launch_bounds__(kTopkThreads, 8) void k_topk_step(Args a, int launc
     const void *ptr = r == 0 ? draft_row<DT>(a, b, j) : target_row<DT>(a, b, j);
     const Row<DT> row(ptr, a.V);
     int2 *list = a.lists ? a.lists + slot_of(a, b, slot) * (size_t)a.klist : nullptr;
-    const TopkRow tr = select_row<DT>(sh, row, a.V, a.top_k, a.c, a.top_p, list);
+    const TopkRow tr = select_row<DT, RADIX>(sh, row, a.V, a.top_k, a.c, a.top_p, list);
     if (threadIdx.x == 0) a.rowinfo[slot_of(a, b, slot)] = pack_rowinfo(tr);
   } else if (mode == 1) {
     const TopkRow pr = unpack_rowinfo(a.rowinfo[slot_of(a, b, n)]);
@@ -765,10 +975,19 @@ __global__ __launch_bounds__(kTopkThreads, 8) void k_topk_step(Args a, int launc
     if (k == 0ull) k = gumbel_over_kept_q<DT>(sh, a, b, n, qr, qlist, Q);
     if (threadIdx.x == 0) out[n] = (int32_t)packed_index(k);
   } else {
-    // every draft kept: top-k of target row gamma, then the bonus draw
+    // every draft kept: top-k of target row gamma, then the bonus draw (a
+    // nucleus kept set from the mass-weighted cut: the dense Gumbel pass over
+    // the row, entries outside the set skipped)
     const Row<DT> Q(target_row<DT>(a, b, gamma), a.V);
-    const TopkRow qr = select_row<DT>(sh, Q, a.V, a.top_k, a.c, a.top_p, nullptr);
-    const unsigned long long k = gumbel_over_kept_q<DT>(sh, a, b, gamma, qr, nullptr, Q);
+    const TopkRow qr = select_row<DT, RADIX>(sh, Q, a.V, a.top_k, a.c, a.top_p, nullptr);
+    unsigned long long k;
+    if (!RADIX || qr.in_lds) {
+      k = gumbel_over_kept_q<DT>(sh, a, b, gamma, qr, nullptr, Q);
+    } else {
+      const PhiloxStream ps(a.key0, a.key1, seq_of(a, b), (uint32_t)gamma, PURPOSE_SAMPLE);
+      k = block_max_u64_sh<kTopkThreads>(gumbel_dense_row<DT, kTopkThreads, true>(Q, a.V, a.c, ps, 0, a.ngb, qr.thr),
+                                         sh.red_u);
+    }
     if (threadIdx.x == 0) out[gamma] = (int32_t)packed_index(k);
   }
 }

@@ -61,6 +61,12 @@ def test_workspace_bytes(L):
 
 def test_launch_names(L):
     import rejection_sampling_verify_17_amd as S
+    # top-p without top-k (or K > 1024) cuts every row by mass: the rows go
+    # through the top-k path's windows
+    assert S.launch_names(64, 5, 128256, 1, 0, 0.7, 0.9) == ["k_topk_step"] * 4    # [0,1) [1,3) [3,5)
+    assert S.launch_names(64, 5, 128256, 1, 3000, 0.7, 0.9) == ["k_topk_step"] * 4
+    assert S.launch_names(64, 5, 128256, 1, 0, 0.0, 0.9) == ["k_greedy_step"] * 4  # arg-max ignores top-p
+    assert S.launch_names(64, 5, 128256, 1, 0, 0.7, 1.0) == ["k_rows", "k_rows"]
     # small inputs: statistics of every row, then the judgement (in every
     # block) and the sampling
     assert S.launch_names(64, 5, 128256, 1, 0) == ["k_rows", "k_rows"]
@@ -103,7 +109,7 @@ def _call(L, **over):
     dict(B=0), dict(B=-3), dict(gamma=0), dict(gamma=65), dict(V=1), dict(V=(1 << 28) + 1),
     dict(dtype=2), dict(T=-1e-30), dict(T=-1.0), dict(T=float("nan")), dict(T=float("inf")),
     dict(wsb=16), dict(target=0x100002), dict(dtype=1, draft=0x200001), dict(tokens=0x300002),
-    dict(ws=0x600010), dict(P=float("nan")), dict(P=0.9), dict(P=0.9, K=2000), dict(P=0.5, K=1000),
+    dict(ws=0x600010), dict(P=float("nan")),
     dict(P=0.9, K=50, ws=None),
     # grids that would not fit 32 bits: top-k (B * 2 gamma blocks), arg-max
     # (B * (gamma + 1) * chunks); the workspace size is made to pass
@@ -127,7 +133,7 @@ def test_product_path_does_not_touch_the_oracle():
 @pytest.mark.parametrize("over", [
     dict(draft=None), dict(out=None), dict(B=0), dict(gamma=0), dict(gamma=65), dict(V=1), dict(dtype=3),
     dict(T=-1.0), dict(T=float("nan")), dict(T=float("inf")), dict(draft=0x200002), dict(out=0x400002),
-    dict(dtype=1, draft=0x200001), dict(P=float("nan")), dict(P=0.9), dict(P=0.9, K=1000),
+    dict(dtype=1, draft=0x200001), dict(P=float("nan")),
 ], ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
 def test_draft_sample_invalid_arguments(L, over):
     args = dict(draft=0x200000, B=4, gamma=3, V=1000, dtype=0, T=1.0, K=0, P=1.0, seed=1, off=0, out=0x400000,

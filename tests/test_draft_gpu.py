@@ -46,7 +46,7 @@ def _compare_draft(w, seed, got, seq_offset=0):
     return want
 
 
-CASES = [("c4b", 64), ("c4b", None), ("c2", 4), ("c3", 8), ("c3p", 8), ("g4b", 32), ("c1", None)]
+CASES = [("c4b", 64), ("c4b", None), ("c2", 4), ("c3", 8), ("c3p", 8), ("c2p", 8), ("g4b", 32), ("c1", None)]
 
 
 @pytest.mark.parametrize("name,B", CASES, ids=[f"{n}-B{b or 'full'}" for n, b in CASES])
@@ -79,6 +79,11 @@ def _edge_drafts():
     zt = rng.integers(-3, 4, (6, 3, 500)).astype(np.float32)
     out.append(("ties-K20-P0.6", I.from_arrays(np.zeros((6, 4, 500), np.float32), zt, np.zeros((6, 3), np.int32),
                                                top_k=20, top_p=0.6)))
+    out.append(("ties-noK-P0.6", I.from_arrays(np.zeros((6, 4, 500), np.float32), zt, np.zeros((6, 3), np.int32),
+                                               top_p=0.6)))
+    zf = rng.normal(0, 1, (3, 2, 9000)).astype(np.float32)
+    out.append(("flat-K2000-P0.8", I.from_arrays(np.zeros((3, 3, 9000), np.float32), zf, np.zeros((3, 2), np.int32),
+                                                 top_k=2000, top_p=0.8)))
     zi = rng.normal(0, 2, (4, 2, 3000)).astype(np.float32)
     zi[:, :, 100:2900] = -np.inf
     out.append(("neg-inf", I.from_arrays(np.zeros((4, 3, 3000), np.float32), zi, np.zeros((4, 2), np.int32))))

@@ -350,14 +350,17 @@ def test_greedy_invalid_tokens_and_workspace_reuse():
 # ---------------------------------------------------------------------------
 # Nucleus (top-p after top-k)
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("B", [8, None], ids=["B8", "Bfull"])
-def test_nucleus_parity(B):
-    w = I.make("c3p", B=B)
-    _say(f"case nucleus c3p B={w.B} gamma={w.gamma} V={w.V} T={w.temperature} K={w.top_k} P={w.top_p}")
+NUCLEUS = [("c3p", 8), ("c3p", None), ("c2p", 8), ("c2p", None)]
+
+
+@pytest.mark.parametrize("name,B", NUCLEUS, ids=[f"{n}-B{b or 'full'}" for n, b in NUCLEUS])
+def test_nucleus_parity(name, B):
+    w = I.make(name, B=B)
+    _say(f"case nucleus {name} B={w.B} gamma={w.gamma} V={w.V} T={w.temperature} K={w.top_k} P={w.top_p}")
     tensors = PT.to_device(w)
     for seed in ((3301, 3302) if B else (3303,)):
         g = PT.run_gpu(w, seed, tensors=tensors)
-        _check(PT.compare(w, seed, g), f"c3p seed {seed}")
+        _check(PT.compare(w, seed, g), f"{name} seed {seed}")
 
 
 def _nucleus_edges():
@@ -384,6 +387,28 @@ def _nucleus_edges():
     t = rng.normal(0, 2, (16, 4, 3000)).astype(np.float32)               # p == q: all kept, bonus under top-p
     out.append(("p-equals-q", I.from_arrays(t, t[:, :3].copy(), drafted(t[:, :3], 1.0, 30, 0.7), top_k=30,
                                             top_p=0.7)))
+    # no top-k: the cut by mass over the whole row (and K above the 1024 the
+    # lists hold), ties at the cut, tiny and large P, both dtypes
+    for P in (0.6, 1e-6, 0.999):
+        t = rng.integers(-4, 5, (6, 3, 700)).astype(np.float32)
+        d = rng.integers(-4, 5, (6, 2, 700)).astype(np.float32)
+        tok = drafted(d, 1.0, 0, P)
+        out.append((f"noK-ties-P{P}", I.from_arrays(t, d, tok, top_p=P)))
+        out.append((f"noK-ties-P{P}-bf16", I.from_arrays(I.f32_to_bf16_bits(t), I.f32_to_bf16_bits(d), tok,
+                                                          top_p=P)))
+    t = rng.normal(0, 1, (4, 3, 9000)).astype(np.float32)                 # flat rows: thousands kept
+    d = (t[:, :2] + rng.normal(0, 0.3, (4, 2, 9000))).astype(np.float32)
+    out.append(("noK-flat-P0.9", I.from_arrays(t, d, drafted(d, 1.0, 0, 0.9), top_p=0.9)))
+    out.append(("K2000-P0.8", I.from_arrays(t, d, drafted(d, 1.0, 2000, 0.8), top_k=2000, top_p=0.8)))
+    tb = I.f32_to_bf16_bits(rng.normal(0, 3, (5, 3, 4099)).astype(np.float32))  # every 2-byte row offset
+    db = I.f32_to_bf16_bits((I.bf16_bits_to_f32(tb[:, :2]) + rng.normal(0, 1, (5, 2, 4099))).astype(np.float32))
+    out.append(("noK-bf16-oddV", I.from_arrays(tb, db, drafted(db, 0.9, 0, 0.8), temperature=0.9, top_p=0.8)))
+    t = rng.normal(0, 2, (16, 4, 3000)).astype(np.float32)               # p == q without top-k
+    out.append(("noK-p-equals-q", I.from_arrays(t, t[:, :3].copy(), drafted(t[:, :3], 1.0, 0, 0.7), top_p=0.7)))
+    t = rng.normal(0, 2, (8, 4, 2000)).astype(np.float32)                # -inf entries inside the row
+    t[:, :, 100:900] = -np.inf
+    d = (t[:, :3] + rng.normal(0, 0.5, (8, 3, 2000))).astype(np.float32)
+    out.append(("noK-neg-inf", I.from_arrays(t, d, drafted(d, 1.0, 0, 0.95), top_p=0.95)))
     return out
 
 
@@ -396,7 +421,7 @@ def test_nucleus_edge_cases(name, w):
     for seed in (13, 14):
         g = PT.run_gpu(w, seed)
         _check(PT.compare(w, seed, g), f"nucleus edge {name} seed {seed}")
-    if name == "p-equals-q":
+    if name in ("p-equals-q", "noK-p-equals-q"):
         assert np.all(g.n_accepted == w.gamma)
 
 

@@ -14,6 +14,7 @@ Workloads (B sequences, gamma drafts, vocabulary V):
   c4a/b/c B=1024, gamma=4, V=50257, fp32, target N(0, 3^2), draft = target + N(0, s^2),
        s = 0.25 / 1 / 4, T=1
   c3p  c3 with top-p 0.9 after the top-k 50 (nucleus)
+  c2p  c2 with top-p 0.9 and no top-k (nucleus over the whole vocabulary)
   g2   c2's logits at T=0 (arg-max mode)
   g4b  c4b's logits at T=0 (arg-max mode)
 
@@ -64,6 +65,7 @@ SPECS = {
     "c4b": Spec("c4b", 1024, 4, 50257, "f32", 1.0, 0, 3.0, 1.0, 1.0, False, 1041, 2041),
     "c4c": Spec("c4c", 1024, 4, 50257, "f32", 1.0, 0, 3.0, 1.0, 4.0, False, 1042, 2042),
     "c3p": Spec("c3p", 256, 8, 152064, "bf16", 0.8, 50, 3.0, 1.0, 2.0, True, 1003, 2003, 0.9),
+    "c2p": Spec("c2p", 64, 5, 128256, "bf16", 0.7, 0, 3.0, 1.0, 1.0, True, 1002, 2002, 0.9),
     "g2": Spec("g2", 64, 5, 128256, "bf16", 0.0, 0, 3.0, 1.0, 1.0, True, 1002, 2002),
     "g4b": Spec("g4b", 1024, 4, 50257, "f32", 0.0, 0, 3.0, 1.0, 1.0, False, 1041, 2041),
 }
