@@ -197,7 +197,8 @@ def run_workload(name: str, steps: int, warmup: int, hip: Hip, seed: int = 3000)
     out_np = out.cpu().numpy()
     ab = algorithmic_bytes(w, n_acc)
     positions = w.B * w.gamma
-    dominant = names[0]  # the per-position kernel: every byte of the rows goes through it
+    # the kernel that takes most of the step (every byte of the rows goes through it)
+    dominant = max(per_kernel, key=lambda k: per_kernel[k]["us_per_step"])
     dom_launches = per_kernel[dominant]["launches_per_step"]
     dom_bytes = ab["stats"] + ab["sample"] + 4 * w.B * w.gamma
     dom_us = per_kernel[dominant]["avg_us"]

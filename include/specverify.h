@@ -240,6 +240,11 @@ SV_API sv_status sv_probe_read(const void *x, size_t bytes, float *out, int32_t 
 SV_API sv_status sv_probe_variates(uint32_t first, int32_t n, float *out, void *stream);
 SV_API sv_status sv_probe_math(const float *x, int32_t n, int32_t op, float *out, void *stream);
 
+/* The hipError_t behind the last SV_EHIP that sv_verify (any variant),
+ * sv_draft_sample or sv_accept_histogram returned on the calling host thread
+ * (hipSuccess if none). */
+SV_API int32_t sv_last_hip_error(void);
+
 /* Human-readable status. */
 SV_API const char *sv_status_string(sv_status s);
 

@@ -25,7 +25,11 @@ NOALLOC_WORKSPACE_BYTES = 32 << 20   # SV_NOALLOC_WORKSPACE_BYTES of include/spe
 class SpecVerifyError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        detail = ""
+        if status == SV_EHIP:
+            self.hip_error = int(lib().sv_last_hip_error())
+            detail = f", hipError_t {self.hip_error}"
+        super().__init__(f"{where}: {status_string(status)} (status {status}{detail})")
 
 
 _lib = None
@@ -41,6 +45,14 @@ def lib() -> ctypes.CDLL:
                 if not os.path.exists(LIB_PATH):
                     raise ImportError(
                         f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+                # torch ships its own HIP runtime under the same soname as the
+                # system's; loading this library first would make torch bind to
+                # the system copy, and launches then fail (hipErrorNoDevice).
+                # Importing torch first keeps one runtime in the process: torch's.
+                try:
+                    import torch  # noqa: F401
+                except ImportError:
+                    pass
                 L = ctypes.CDLL(LIB_PATH)
                 vp, i32, u64, flt, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_float,
                                          ctypes.c_size_t)
@@ -67,6 +79,8 @@ def lib() -> ctypes.CDLL:
                 L.sv_probe_variates.restype = i32
                 L.sv_probe_math.argtypes = [vp, i32, i32, vp, vp]
                 L.sv_probe_math.restype = i32
+                L.sv_last_hip_error.argtypes = []
+                L.sv_last_hip_error.restype = i32
                 L.sv_status_string.argtypes = [i32]
                 L.sv_status_string.restype = ctypes.c_char_p
                 L.sv_version.argtypes = []

@@ -35,6 +35,14 @@ __device__ __align__(256) unsigned char scratch[kStaticWorkspace];
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// The HIP error behind the last SV_EHIP this host thread received.
+thread_local hipError_t g_last_hip_error = hipSuccess;
+bool launch_ok() {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) g_last_hip_error = e;
+  return e == hipSuccess;
+}
+
 // Compute units of the current device (queried once per device).
 int compute_units() {
   static std::atomic<int> cached[kMaxDevices];
@@ -171,7 +179,7 @@ struct Launches {
     auto after = [&]() -> bool {
       if (events && 2 * li + 1 < n_events) (void)hipEventRecord((hipEvent_t)events[2 * li + 1], stream);
       ++li;
-      return hipGetLastError() == hipSuccess;
+      return launch_ok();
     };
     bool ok = true;
     if (p.greedy) {
@@ -345,7 +353,11 @@ void *noalloc_workspace() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
   void *p = addr[dev].load(std::memory_order_acquire);
   if (p) return p;
-  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) {
+    g_last_hip_error = e != hipSuccess ? e : hipErrorInvalidSymbol;
+    return nullptr;
+  }
   addr[dev].store(p, std::memory_order_release);
   return p;
 }
@@ -460,7 +472,7 @@ sv_status sv_draft_sample(const void *draft_logits, int32_t B, int32_t gamma, in
     if (radix) hipLaunchKernelGGL((k_draft_sample<DT_F32, true>), grid, dim3(kTopkThreads), 0, s, a);
     else hipLaunchKernelGGL((k_draft_sample<DT_F32, false>), grid, dim3(kTopkThreads), 0, s, a);
   }
-  return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+  return launch_ok() ? SV_OK : SV_EHIP;
 }
 
 sv_status sv_accept_histogram(const int32_t *n_accepted, int32_t B, int32_t gamma, int32_t *hist, void *stream) {
@@ -468,7 +480,7 @@ sv_status sv_accept_histogram(const int32_t *n_accepted, int32_t B, int32_t gamm
   if (((uintptr_t)n_accepted % 4) || ((uintptr_t)hist % 4)) return SV_EINVAL;
   (void)hipGetLastError();
   hipLaunchKernelGGL(k_accept_hist, dim3(1), dim3(256), 0, (hipStream_t)stream, n_accepted, B, gamma, hist);
-  return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+  return launch_ok() ? SV_OK : SV_EHIP;
 }
 
 const char *sv_status_string(sv_status s) {
@@ -479,6 +491,8 @@ const char *sv_status_string(sv_status s) {
   }
   return "unknown status";
 }
+
+int32_t sv_last_hip_error(void) { return (int32_t)g_last_hip_error; }
 
 const char *sv_version(void) { return "specverify 0.1 (gfx950)"; }
 

@@ -112,6 +112,30 @@ def test_deterministic_and_geometry_independent():
     assert np.array_equal(c.out_tokens, a.out_tokens[5:9])
 
 
+def test_large_batch_invalid_tokens_and_sub_batches():
+    """Large inputs (one position per launch): drafted tokens outside [0, V)
+    flag their sequence; a sub-batch with the matching seq_offset draws the
+    same random numbers, so it matches the oracle on the same sequences; every
+    sequence equals the oracle."""
+    import rejection_sampling_verify_17_amd as S
+    w = I.make("c4b", B=512)
+    assert S.launch_names(w.B, w.gamma, w.V, S.SV_F32, 0)[:2] == ["k_rows", "k_judge"]
+    tok = w.tokens.copy()
+    tok[3, 0] = w.V
+    tok[100, 3] = -2
+    w2 = I.from_arrays(w.target, w.draft, tok, w.temperature, w.top_k)
+    _say(f"case large batch B={w2.B} gamma={w2.gamma} V={w2.V}, two invalid sequences")
+    g = PT.run_gpu(w2, 3004)
+    assert g.n_accepted[3] == -1 and np.all(g.out_tokens[3] == -1)
+    assert g.n_accepted[100] == -1 and np.all(g.out_tokens[100] == -1)
+    _check(PT.compare(w2, 3004, g), "large batch")
+    sub = I.from_arrays(w2.target[160:480], w2.draft[160:480], tok[160:480], w2.temperature, w2.top_k)
+    gs = PT.run_gpu(sub, 3004, seq_offset=160)
+    _check(PT.compare(sub, 3004, gs, seq_offset=160), "large sub-batch")
+    same = np.mean(np.all(gs.out_tokens == g.out_tokens[160:480], axis=1))
+    _say(f"sub-batch rows equal to the full batch's: {same:.4f}")
+
+
 def test_invalid_tokens_flagged():
     w = I.make("c1")
     tok = w.tokens.copy()
