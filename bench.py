@@ -327,7 +327,7 @@ def cpu_baseline(w, seed: int, budget_s: float = 12.0, gpu_out=None) -> dict:
         rep = PT.compare(ws, seed, g, nthreads=cores, check_probs=False)
         sm = rep.summary()
         res["parity_of_timed_outputs"] = {k: sm[k] for k in ("sequences", "mismatches", "exempt_accept",
-                                                             "exempt_token", "exempt_nucleus")}
+                                                             "exempt_token", "exempt_nucleus", "exempt_equal")}
     return res
 
 

@@ -111,3 +111,32 @@ def exact_first_two(pair, x0_token: int, temperature: float = 1.0) -> np.ndarray
     q = np.exp(z)
     q /= q.sum(axis=1, keepdims=True)
     return q[x0_token][:, None] * q
+
+
+def exact_all_accepted(pair, x0_token: int, gamma_max: int, temperature: float = 1.0) -> np.ndarray:
+    """A_i = P(the first i drafts of a round are all accepted), i = 1..gamma_max,
+    starting from token x0 (fp64, written out here apart from the oracle).
+
+    From state x the draft proposes t with probability p(t|x) and keeps it with
+    probability min(1, q(t|x)/p(t|x)), so a step is accepted with next state t
+    with probability M[x, t] = min(p(t|x), q(t|x)), and A_i = e_x0' M^i 1."""
+    def probs(table):
+        z = table.astype(np.float64) / float(np.float32(temperature))
+        z = z - z.max(axis=1, keepdims=True)
+        e = np.exp(z)
+        return e / e.sum(axis=1, keepdims=True)
+    M = np.minimum(probs(pair.draft), probs(pair.target))
+    v = np.zeros(pair.V)
+    v[x0_token] = 1.0
+    out = []
+    for _ in range(gamma_max):
+        v = v @ M
+        out.append(v.sum())
+    return np.array(out)
+
+
+def acceptance_by_draft_length(run, pair, x0: np.ndarray, gammas) -> dict:
+    """One round per draft length gamma with the same seeds: {gamma: n per
+    sequence}.  The draft and verification streams do not depend on gamma,
+    so position i is decided alike in every run that reaches it."""
+    return {g: run(pair, x0, gamma=g, rounds=1).n_per_round[0].astype(np.int64) for g in gammas}

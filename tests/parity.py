@@ -14,6 +14,8 @@ same Philox streams):
   * with top-p, from the first position whose oracle rows have their nucleus
     cut within 1e-5 of flipping onward (the kept set is decided by an fp32
     sum on the GPU; the positions before it are still exact);
+  * exempt sequences whose outputs equal the oracle's all the same are
+    counted (exempt_equal), so a report shows how many edges really flipped;
   * p_j(t_j), q_j(t_j) within 1e-5 relative of the oracle where the oracle's
     value is >= 1e-30, and the acceptance uniforms equal exactly, at every
     position both sides judged; positions the GPU did not judge (after its
@@ -46,6 +48,7 @@ class Report:
     exempt_accept: int = 0
     exempt_token: int = 0
     exempt_nucleus: int = 0
+    exempt_equal: int = 0   # sequences exempt at a knife edge whose outputs equal the oracle's all the same
     mismatches: int = 0
     mismatch_examples: list = field(default_factory=list)
     prob_checked: int = 0
@@ -58,6 +61,7 @@ class Report:
         self.exempt_accept += o.exempt_accept
         self.exempt_token += o.exempt_token
         self.exempt_nucleus += o.exempt_nucleus
+        self.exempt_equal += o.exempt_equal
         self.mismatches += o.mismatches
         self.mismatch_examples += o.mismatch_examples[: max(0, 10 - len(self.mismatch_examples))]
         self.prob_checked += o.prob_checked
@@ -77,6 +81,7 @@ class Report:
         return {"sequences": self.sequences, "mismatches": self.mismatches,
                 "mismatch_rate": self.mismatch_rate, "exempt_accept": self.exempt_accept,
                 "exempt_token": self.exempt_token, "exempt_nucleus": self.exempt_nucleus,
+                "exempt_equal": self.exempt_equal,
                 "prob_checked": self.prob_checked,
                 "prob_max_rel": self.prob_max_rel, "prob_failures": self.prob_failures,
                 "u_failures": self.u_failures, "examples": self.mismatch_examples[:5]}
@@ -162,7 +167,13 @@ def _nucleus_edge(rep: Report, w, b: int, i: int, res, g: GpuResult) -> bool:
     if min(n_g, n_o) < j0 or not np.array_equal(res.out_tokens[i, :j0], g.out_tokens[b, :j0]):
         rep.mismatches += 1
         rep.mismatch_examples.append(("prefix-before-nucleus-edge", b, j0, n_o, n_g))
+    elif _same_outputs(res, i, g, b):
+        rep.exempt_equal += 1
     return True
+
+
+def _same_outputs(res, i: int, g: GpuResult, b: int) -> bool:
+    return int(res.n_accepted[i]) == int(g.n_accepted[b]) and np.array_equal(res.out_tokens[i], g.out_tokens[b])
 
 
 def _compare_seq(rep: Report, w, b: int, i: int, res, g: GpuResult):
@@ -184,6 +195,8 @@ def _compare_seq(rep: Report, w, b: int, i: int, res, g: GpuResult):
         if not np.array_equal(res.out_tokens[i, :j0], g.out_tokens[b, :j0]) or min(n_g, n_o) < j0:
             rep.mismatches += 1
             rep.mismatch_examples.append(("prefix-before-knife-edge", b, j0, n_o, n_g))
+        elif _same_outputs(res, i, g, b):
+            rep.exempt_equal += 1
         return
     if n_o != n_g:
         rep.mismatches += 1

@@ -96,7 +96,43 @@ def test_60k_total_variation_on_gpu():
     thr = C.direct_tv_threshold(q)
     _say(f"TV(gpu samples, q) = {got:.5f}; direct-sampling p99 = {thr:.5f}")
     assert got <= thr
-    _check(PT.compare(rep_w, 3000, g, check_probs=False), "c0-60k")
+    rep = PT.compare(rep_w, 3000, g, check_probs=False)
+    _POOL["c0-60k"] = rep
+    _check(rep, "c0-60k")
+
+
+# Pooled mismatch rate: every workload at its full size under 20 verify
+# seeds each, pooled with the 60,000-sequence run above.  Exemptions (knife
+# edges, tests/parity.py) are counted and printed per workload and pooled.
+_POOL = {}
+POOLED = ["c0", "c1", "c2", "c2p", "c3", "c3p", "c4a", "c4b", "c4c"]
+POOL_SEEDS = 20
+
+
+@pytest.mark.parametrize("name", POOLED)
+def test_pooled_seeds(name):
+    w = I.make(name)
+    _say(f"case pooled {name} B={w.B} gamma={w.gamma} V={w.V} K={w.top_k} top_p={w.top_p}, {POOL_SEEDS} seeds")
+    tensors = PT.to_device(w)
+    rep = PT.Report()
+    for k in range(POOL_SEEDS):
+        seed = 5000 + 100 * k + POOLED.index(name)
+        g = PT.run_gpu(w, seed, tensors=tensors, debug=False)
+        rep.merge(PT.compare(w, seed, g, check_probs=False))
+    _POOL[name] = rep
+    _check(rep, f"pooled {name}")
+
+
+def test_pooled_total():
+    missing = [n for n in POOLED + ["c0-60k"] if n not in _POOL]
+    if missing:
+        pytest.skip(f"pooled parts not run in this session: {missing}")
+    tot = PT.Report()
+    for n in POOLED + ["c0-60k"]:
+        tot.merge(_POOL[n])
+    _say("pooled over all workloads x 20 seeds and the 60k run:", tot.summary())
+    assert tot.sequences >= 128_000
+    assert tot.mismatches == 0 and tot.ok()
 
 
 def test_deterministic_and_geometry_independent():
