@@ -149,6 +149,7 @@ template <int NT> struct LdsMax32 {  // per-thread maxima as 32-bit keys in the 
 template <int DT> struct StreamRow {
   static constexpr int NE = Elem<DT>::kVec;
   static constexpr int kU = 2;
+  static constexpr int kUCut = 8;  // loads in flight in the passes of the mass-weighted nucleus cut (one block per compute unit there)
   const Row<DT> &row;
   int e0, e1;  // entries [e0, e1) of the row
   __device__ __forceinline__ StreamRow(const Row<DT> &r, int V) : row(r), e0(0), e1(V) {}
@@ -172,14 +173,16 @@ template <int DT> struct StreamRow {
       if (v >= e0 && v < e1) f(z[e], v);
     }
   }
-  template <class F> __device__ __forceinline__ void for_each(F f) const {
+  template <class F> __device__ __forceinline__ void for_each(F f) const { for_each_u<kU>(f); }
+  // The same with U loads in flight per thread.
+  template <int U, class F> __device__ __forceinline__ void for_each_u(F f) const {
     const int iv0 = this->iv0(), iv1 = this->iv1();
-    for (int base = iv0 + (int)threadIdx.x; base < iv1; base += kTopkThreads * kU) {
-      u32x4 d[kU];
+    for (int base = iv0 + (int)threadIdx.x; base < iv1; base += kTopkThreads * U) {
+      u32x4 d[U];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) d[u] = row.raw(base + u * kTopkThreads);
+      for (int u = 0; u < U; ++u) d[u] = row.raw(base + u * kTopkThreads);
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
+      for (int u = 0; u < U; ++u) {
         float z[NE];
         decode<DT>(d[u], z);
         const int ev = (base + u * kTopkThreads) * NE - row.s;
@@ -563,7 +566,7 @@ template <class Src> struct TieKeys {
   uint32_t hw;
   unsigned long long thr;
   template <class F> __device__ __forceinline__ void for_each(F f) const {
-    src.for_each([&](float z, int v) {
+    src.template for_each_u<Src::kUCut>([&](float z, int v) {
       const unsigned long long k = entry_key(z, (uint32_t)v);
       if ((uint32_t)(k >> 32) == hw && k >= thr) f(k);
     });
@@ -592,7 +595,7 @@ __device__ __forceinline__ unsigned long long exact_kth(TopkShared &sh, const Ke
 template <class Src>
 __device__ __forceinline__ float row_reference(TopkShared &sh, const Src &src, float c) {
   float zmax = -INFINITY;
-  src.for_each([&](float z, int) { zmax = fmaxf(zmax, z); });
+  src.template for_each_u<Src::kUCut>([&](float z, int) { zmax = fmaxf(zmax, z); });
   zmax = wave_max_f(zmax);
   if ((threadIdx.x % kWave) == 0) sh.red_f[threadIdx.x / kWave] = zmax;
   __syncthreads();
@@ -613,15 +616,20 @@ __device__ void nucleus_cut_radix(TopkShared &sh, const Src &src, int V, float c
   unsigned long long prefix = 0ull, pmask = 0ull;  // key bits fixed so far
   unsigned long long above = 0ull;                 // mass of kept keys above them
   unsigned long long target = 0ull;                // P of the total mass, rounded up
+  // bf16 logits fill only the top 16 bits of their float: the low 16 bits of
+  // the key's high word are then 0 (z >= 0) or all ones (z < 0, complemented
+  // by orderable), fixed by the sign bit that pass 0 fixes; the last digit is
+  // known without a pass
+  constexpr int kPasses = Src::NE == 8 ? 2 : 3;
 #pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
+  for (int pass = 0; pass < kPasses; ++pass) {
     // digits of the key's high word: bits [53, 64), [42, 53), [32, 42)
     const int shift = pass == 0 ? 53 : (pass == 1 ? 42 : 32);
     const int nb = pass < 2 ? 2048 : 1024;
     const unsigned long long dmask = (unsigned long long)(nb - 1);
     for (int i = tid; i < kMassBins; i += kTopkThreads) mass[i] = 0ull;
     __syncthreads();
-    src.for_each([&](float z, int v) {
+    src.template for_each_u<Src::kUCut>([&](float z, int v) {
       const unsigned long long key = entry_key(z, (uint32_t)v);
       if (key >= thr0 && (key & pmask) == prefix) {
         const unsigned long long w = mass_fix(z, c, R, scale);
@@ -669,6 +677,11 @@ __device__ void nucleus_cut_radix(TopkShared &sh, const Src &src, int V, float c
     prefix |= (unsigned long long)d << shift;
     pmask |= dmask << shift;
     above = ab;
+  }
+  if (kPasses == 2) {
+    const unsigned long long low = (prefix >> 63) ? 0ull : 0x3FFull;  // key bit 63 set: z >= 0
+    prefix |= low << 32;
+    pmask |= 0x3FFull << 32;
   }
   // every kept entry with logit key hw weighs w; the first k by index are kept
   const uint32_t hw = (uint32_t)(prefix >> 32);
@@ -891,7 +904,7 @@ __device__ __forceinline__ Judged judge_topk(const Args &a, int b, int j) {
 // flight; RADIX: the nucleus without top-k or over more than kTopkThreads
 // kept entries (see topk_row).
 template <int DT, bool RADIX>
-__global__ __launch_bounds__(kTopkThreads, 8) void k_topk_step(Args a, int launch, int p0, int w0, int w1) {
+__global__ __launch_bounds__(kTopkThreads, RADIX ? 4 : 8) void k_topk_step(Args a, int launch, int p0, int w0, int w1) {
   __shared__ TopkShared sh;
   const int dw = w1 - w0;
   const int per_seq = dw > 0 ? 2 * dw : 1;

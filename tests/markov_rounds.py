@@ -140,3 +140,36 @@ def acceptance_by_draft_length(run, pair, x0: np.ndarray, gammas) -> dict:
     sequence}.  The draft and verification streams do not depend on gamma,
     so position i is decided alike in every run that reaches it."""
     return {g: run(pair, x0, gamma=g, rounds=1).n_per_round[0].astype(np.int64) for g in gammas}
+
+
+def draft_length_table(n: dict, exact: np.ndarray, label: str):
+    """Mean accepted E_g and all-accepted rate A_g per draft length g (the
+    shape of the table in page "스펙큘러티브 디코딩 — 작은 모델이 먼저 쓰고 큰 모델이
+    검사한다" §2), with the chain's exact A_g beside them.  Checks, for every
+    g: n_g = sum over i <= g of [n_i = i] for every sequence (so E_g equals the
+    sum of A_i exactly), and A_g within 4.5 binomial standard deviations of the
+    exact value."""
+    B = len(next(iter(n.values())))
+    gs = sorted(n)
+    print(f"{label}: B = {B}")
+    print(" gamma | mean accepted E | all accepted A | exact A | sum_{i<=gamma} A_i")
+    for g in gs:
+        allacc = {i: (n[i] == i) for i in gs if i <= g}
+        assert sorted(allacc) == list(range(1, g + 1))
+        assert np.array_equal(n[g], sum(allacc[i].astype(np.int64) for i in range(1, g + 1))), f"gamma {g}"
+        A = float(np.mean(n[g] == g))
+        sd = np.sqrt(exact[g - 1] * (1 - exact[g - 1]) / B)
+        assert abs(A - exact[g - 1]) <= 4.5 * sd + 1e-12, (g, A, exact[g - 1])
+        if g in (1, 2, 3, 4, 6, 8):
+            print(f" {g:5d} | {n[g].mean():15.4f} | {A:14.4f} | {exact[g - 1]:7.4f} | "
+                  f"{sum(np.mean(n[i] == i) for i in range(1, g + 1)):.4f}")
+
+
+
+def check_acceptance_by_draft_length(run, B: int = 30_000):
+    """The table for a fixed pair (V = 32) from x0 = 7, against the exact rates."""
+    from workloads import synth as I
+    pair = I.markov_pair(V=32, seed=41)
+    x0 = np.full(B, 7, np.int32)
+    n = acceptance_by_draft_length(run, pair, x0, range(1, 9))
+    draft_length_table(n, exact_all_accepted(pair, 7, 8), "oracle" if run is run_oracle else "gpu")

@@ -62,36 +62,12 @@ def test_gpu_rounds_follow_the_target_chain():
     assert got <= thr
 
 
-def _draft_length_table(n: dict, exact: np.ndarray, label: str):
-    """Mean accepted E_g and all-accepted rate A_g per draft length g (the
-    shape of the table in page "스펙큘러티브 디코딩 — 작은 모델이 먼저 쓰고 큰 모델이
-    검사한다" §2), with the chain's exact A_g beside them.  Checks, for every
-    g: n_g = sum over i <= g of [n_i = i] for every sequence (so E_g equals the
-    sum of A_i exactly), and A_g within 4.5 binomial standard deviations of the
-    exact value."""
-    B = len(next(iter(n.values())))
-    gs = sorted(n)
-    print(f"{label}: B = {B}")
-    print(" gamma | mean accepted E | all accepted A | exact A | sum_{i<=gamma} A_i")
-    for g in gs:
-        allacc = {i: (n[i] == i) for i in gs if i <= g}
-        assert sorted(allacc) == list(range(1, g + 1))
-        assert np.array_equal(n[g], sum(allacc[i].astype(np.int64) for i in range(1, g + 1))), f"gamma {g}"
-        A = float(np.mean(n[g] == g))
-        sd = np.sqrt(exact[g - 1] * (1 - exact[g - 1]) / B)
-        assert abs(A - exact[g - 1]) <= 4.5 * sd + 1e-12, (g, A, exact[g - 1])
-        if g in (1, 2, 3, 4, 6, 8):
-            print(f" {g:5d} | {n[g].mean():15.4f} | {A:14.4f} | {exact[g - 1]:7.4f} | "
-                  f"{sum(np.mean(n[i] == i) for i in range(1, g + 1)):.4f}")
-
-
 def test_oracle_acceptance_by_draft_length():
     """The oracle's rounds against the chain's exact all-accepted rates
     (a pin of the acceptance rule through a closed form), and E_g = sum A_i."""
     pair = I.markov_pair(V=32, seed=41)
     x0 = np.full(30_000, 7, np.int32)
-    n = M.acceptance_by_draft_length(M.run_oracle, pair, x0, range(1, 9))
-    _draft_length_table(n, M.exact_all_accepted(pair, 7, 8), "oracle")
+    M.check_acceptance_by_draft_length(M.run_oracle, B=30_000)
 
 
 @pytest.mark.gpu
@@ -102,7 +78,7 @@ def test_gpu_acceptance_by_draft_length():
     x0 = np.full(60_000, 9, np.int32)
     gs = range(1, 9)
     n = M.acceptance_by_draft_length(M.run_gpu, pair, x0, gs)
-    _draft_length_table(n, M.exact_all_accepted(pair, 9, 8), "gpu")
+    M.draft_length_table(n, M.exact_all_accepted(pair, 9, 8), "gpu")
     o = M.acceptance_by_draft_length(M.run_oracle, pair, x0, gs)
     for g in gs:
         assert np.array_equal(n[g], o[g]), f"gamma {g}: GPU and oracle differ"

@@ -15,7 +15,7 @@ MUTANTS = [
     ("residual sign flipped", "double d = q[v] - p[v];", "double d = p[v] - q[v];",
      ["enumeration", "output_is_q"]),
     ("ratio inverted", "return u < q_t / p_t;", "return u < p_t / q_t;",
-     ["enumeration", "golden"]),
+     ["enumeration", "golden", "draft_length"]),
     ("bonus from row gamma-1",
      "((size_t)b * (gamma + 1) + gamma) * V * esz", "((size_t)b * (gamma + 1) + gamma - 1) * V * esz",
      ["special"]),
@@ -78,6 +78,9 @@ def _run(check):
         C.check_golden_token_probs()
     elif check == "greedy":
         C.check_greedy()
+    elif check == "draft_length":
+        import markov_rounds as M
+        M.check_acceptance_by_draft_length(M.run_oracle, B=20_000)
     elif check == "philox":
         import rocrand_ref
         rr = rocrand_ref.load()
