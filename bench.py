@@ -363,9 +363,9 @@ def cpu_one_thread(name: str = "c2", n: int = 4, seed: int = 3000) -> dict:
 def stream_read_GBps(hip: Hip, gib: int = 1) -> dict:
     """Context only: the read rate of a plain streaming kernel of the library
     (sv_probe_read: contiguous slabs, four 16-byte loads in flight per
-    thread) over `gib` GiB, per grid size, mean of 10 launches timed by HIP
-    events on the launch stream; and, for comparison, torch.sum over the same
-    buffer."""
+    thread; with ordinary and with non-temporal loads) over `gib` GiB, per
+    grid size, mean of 10 launches timed by HIP events on the launch stream;
+    and, for comparison, torch.sum over the same buffer."""
     import torch
     import rejection_sampling_verify_17_amd as S
     nbytes = gib << 30
@@ -373,16 +373,17 @@ def stream_read_GBps(hip: Hip, gib: int = 1) -> dict:
     out = torch.empty(65536, dtype=torch.float32, device="cuda")
     sp = int(torch.cuda.current_stream().cuda_stream)
     e0, e1 = hip.event(), hip.event()
-    rates = {}
-    for grid in (1024, 2048, 4096, 8192, 16384):
-        for _ in range(3):
-            assert S.lib().sv_probe_read(x.data_ptr(), nbytes, out.data_ptr(), grid, sp) == 0
-        hip.record(e0, sp)
-        for _ in range(10):
-            S.lib().sv_probe_read(x.data_ptr(), nbytes, out.data_ptr(), grid, sp)
-        hip.record(e1, sp)
-        hip.sync(e1)
-        rates[str(grid)] = nbytes * 10 / (hip.ms(e0, e1) * 1e-3) / 1e9
+    rates, rates_nt = {}, {}
+    for nt, dst in ((0, rates), (1, rates_nt)):
+        for grid in (1024, 2048, 4096, 8192, 16384):
+            for _ in range(3):
+                assert S.lib().sv_probe_read(x.data_ptr(), nbytes, out.data_ptr(), grid, nt, sp) == 0
+            hip.record(e0, sp)
+            for _ in range(10):
+                S.lib().sv_probe_read(x.data_ptr(), nbytes, out.data_ptr(), grid, nt, sp)
+            hip.record(e1, sp)
+            hip.sync(e1)
+            dst[str(grid)] = nbytes * 10 / (hip.ms(e0, e1) * 1e-3) / 1e9
     for _ in range(3):
         x.sum()  # warm-up: the first call also loads the reduction kernel
     torch.cuda.synchronize()
@@ -397,6 +398,8 @@ def stream_read_GBps(hip: Hip, gib: int = 1) -> dict:
     del x, out
     torch.cuda.empty_cache()
     return {"probe_read_GBps_by_grid": rates, "probe_read_GBps_best": max(rates.values()),
+            "probe_read_nontemporal_GBps_by_grid": rates_nt,
+            "probe_read_nontemporal_GBps_best": max(rates_nt.values()),
             "torch_sum_GBps": torch_sum, "bytes": nbytes}
 
 

@@ -222,9 +222,10 @@ SV_API sv_status sv_accept_histogram(const int32_t *n_accepted, int32_t B, int32
  * sv_probe_read: reads `bytes` (a multiple of 16 is read; the rest ignored)
  * of device memory at x (16-byte aligned) once, `grid` blocks of 256 threads
  * each streaming a contiguous slab with four 16-byte loads in flight per
- * thread, and writes one float per block to out [grid] (device).  Timing it
- * gives the read rate a plain kernel reaches on this GPU, the context the
- * verification kernels' rates are read against.
+ * thread, and writes one float per block to out [grid] (device).  With
+ * nontemporal != 0 the loads carry the non-temporal (streaming) cache hint.
+ * Timing it gives the read rate a plain kernel reaches on this GPU, the
+ * context the verification kernels' rates are read against.
  *
  * sv_probe_variates: out[i] (device, n floats) = the exponential variate in
  * base 2 that the samplers derive from Philox word w = (first + i) << 9, i.e.
@@ -236,7 +237,8 @@ SV_API sv_status sv_accept_histogram(const int32_t *n_accepted, int32_t B, int32
  *
  * All three: SV_EINVAL for null or misaligned pointers and out-of-range
  * sizes, SV_EHIP for a failed launch; enqueued on `stream`. */
-SV_API sv_status sv_probe_read(const void *x, size_t bytes, float *out, int32_t grid, void *stream);
+SV_API sv_status sv_probe_read(const void *x, size_t bytes, float *out, int32_t grid, int32_t nontemporal,
+                               void *stream);
 SV_API sv_status sv_probe_variates(uint32_t first, int32_t n, float *out, void *stream);
 SV_API sv_status sv_probe_math(const float *x, int32_t n, int32_t op, float *out, void *stream);
 

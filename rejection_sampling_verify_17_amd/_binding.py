@@ -73,7 +73,7 @@ def lib() -> ctypes.CDLL:
                 L.sv_draft_sample.restype = i32
                 L.sv_accept_histogram.argtypes = [vp, i32, i32, vp, vp]
                 L.sv_accept_histogram.restype = i32
-                L.sv_probe_read.argtypes = [vp, sz, vp, i32, vp]
+                L.sv_probe_read.argtypes = [vp, sz, vp, i32, i32, vp]
                 L.sv_probe_read.restype = i32
                 L.sv_probe_variates.argtypes = [ctypes.c_uint32, i32, vp, vp]
                 L.sv_probe_variates.restype = i32

@@ -19,7 +19,9 @@ constexpr int kProbeU = 4;  // 16-byte loads in flight per thread
 
 // Each block reads a contiguous slab of the buffer (16-byte vectors, kProbeU
 // in flight per thread) and folds it into one float, written per block so the
-// loads cannot be dropped.  Vectors past the buffer are not read.
+// loads cannot be dropped.  Vectors past the buffer are not read.  NT: loads
+// with the non-temporal hint (no allocation for reuse in the caches).
+template <bool NT>
 __global__ __launch_bounds__(kProbeThreads) void k_probe_read(const u32x4 *x, long long n16, float *out) {
   const long long per = (n16 + gridDim.x - 1) / gridDim.x;
   const long long lo = per * blockIdx.x;
@@ -30,7 +32,8 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_read(const u32x4 *x, lo
 #pragma unroll
     for (int u = 0; u < kProbeU; ++u) {
       const long long k = i + (long long)u * kProbeThreads;
-      a[u] = k < hi ? x[k] : u32x4{0u, 0u, 0u, 0u};
+      if (NT) a[u] = k < hi ? __builtin_nontemporal_load(x + k) : u32x4{0u, 0u, 0u, 0u};
+      else a[u] = k < hi ? x[k] : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < kProbeU; ++u)
@@ -64,11 +67,15 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_math(const float *x, in
 
 extern "C" {
 
-sv_status sv_probe_read(const void *x, size_t bytes, float *out, int32_t grid, void *stream) {
+sv_status sv_probe_read(const void *x, size_t bytes, float *out, int32_t grid, int32_t nontemporal, void *stream) {
   if (!x || !out || grid < 1 || bytes < 16 || ((uintptr_t)x % 16) || ((uintptr_t)out % 4)) return SV_EINVAL;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(k_probe_read, dim3((unsigned)grid), dim3(kProbeThreads), 0, (hipStream_t)stream,
-                     (const u32x4 *)x, (long long)(bytes / 16), out);
+  if (nontemporal)
+    hipLaunchKernelGGL(k_probe_read<true>, dim3((unsigned)grid), dim3(kProbeThreads), 0, (hipStream_t)stream,
+                       (const u32x4 *)x, (long long)(bytes / 16), out);
+  else
+    hipLaunchKernelGGL(k_probe_read<false>, dim3((unsigned)grid), dim3(kProbeThreads), 0, (hipStream_t)stream,
+                       (const u32x4 *)x, (long long)(bytes / 16), out);
   return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }
 
