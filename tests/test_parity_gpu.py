@@ -5,6 +5,7 @@ full-size workloads run in the launch configuration the benchmark times and
 compare against the oracle on every sequence (the oracle is fast enough with
 all host threads).  The bar is documented in tests/parity.py."""
 import sys
+import warnings
 
 import numpy as np
 import pytest
@@ -128,11 +129,23 @@ def test_pooled_total():
     if missing:
         pytest.skip(f"pooled parts not run in this session: {missing}")
     tot = PT.Report()
+    lines = []
+    keys = ("sequences", "mismatches", "exempt_accept", "exempt_token", "exempt_nucleus", "exempt_equal")
     for n in POOLED + ["c0-60k"]:
         tot.merge(_POOL[n])
-    _say("pooled over all workloads x 20 seeds and the 60k run:", tot.summary())
+        sm = _POOL[n].summary()
+        lines.append(f"  {n}: " + ", ".join(f"{k} {sm[k]}" for k in keys))
+    sm = tot.summary()
+    lines.append("  pooled: " + ", ".join(f"{k} {sm[k]}" for k in keys) + f", mismatch_rate {sm['mismatch_rate']:.2e}")
+    _say("pooled over all workloads x 20 seeds and the 60k run:", sm)
+    # shown in the warnings summary of a quiet run, so the counts reach its log
+    warnings.warn(ParityReport("pooled parity, every workload x 20 verify seeds + the 60k run:\n" + "\n".join(lines)))
     assert tot.sequences >= 128_000
     assert tot.mismatches == 0 and tot.ok()
+
+
+class ParityReport(UserWarning):
+    """Counts of a parity run, reported through the warnings summary."""
 
 
 def test_deterministic_and_geometry_independent():
@@ -469,6 +482,17 @@ def _nucleus_edges():
     t[:, :, 100:900] = -np.inf
     d = (t[:, :3] + rng.normal(0, 0.5, (8, 3, 2000))).astype(np.float32)
     out.append(("noK-neg-inf", I.from_arrays(t, d, drafted(d, 1.0, 0, 0.95), top_p=0.95)))
+    tb, db = I.f32_to_bf16_bits(t), I.f32_to_bf16_bits(d)
+    out.append(("noK-neg-inf-bf16", I.from_arrays(tb, db, drafted(db, 1.0, 0, 0.95), top_p=0.95)))
+    # every logit negative, ties at the cut: the cut's key lies below the
+    # sign flip (bf16: its low key bits are all ones)
+    for P in (0.6, 0.97):
+        t = rng.integers(-14, -5, (6, 3, 700)).astype(np.float32)
+        d = (t[:, :2] + rng.integers(-1, 2, (6, 2, 700))).astype(np.float32)
+        tok = drafted(d, 1.0, 0, P)
+        out.append((f"noK-negative-P{P}", I.from_arrays(t, d, tok, top_p=P)))
+        out.append((f"noK-negative-P{P}-bf16", I.from_arrays(I.f32_to_bf16_bits(t), I.f32_to_bf16_bits(d), tok,
+                                                              top_p=P)))
     return out
 
 
