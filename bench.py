@@ -507,6 +507,57 @@ def rocprof_summary(args) -> None:
         print("\n".join(lines))
 
 
+def _kernel_variant(name: str) -> str:
+    """Kernel name with its template arguments (e.g. k_rows<1, 0>), else the short name."""
+    short = _short(name)
+    i = name.find(short + "<")
+    if i >= 0:
+        j = name.find(">", i)
+        if j > 0:
+            return name[i:j + 1]
+    return short
+
+
+def busy_summary(args) -> None:
+    """Summary for profiles/ of one rocprofv3 --pmc run under --rocprof-busy DIR
+    (sub-directory busy/) with VALUBusy, TA_BUSY_avr, SQ_INSTS_VALU,
+    SQ_INSTS_VALU_TRANS_F32 and GRBM_GUI_ACTIVE: per kernel instantiation, the
+    mean over its dispatches of the VALU-busy percentage (rocprofv3's derived
+    VALUBusy), the memory-unit (texture addresser) busy percentage
+    TA_BUSY_avr / GRBM_GUI_ACTIVE, and the VALU and transcendental
+    instructions per dispatch."""
+    d = args.rocprof_busy
+    wl = args.workload
+    acc = {}
+    for path in _find(os.path.join(d, "busy"), "counter_collection.csv"):
+        for r in _csv_rows(path):
+            key = _kernel_variant(r["Kernel_Name"])
+            disp = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            acc.setdefault(key, {}).setdefault(disp, {})
+            c = r["Counter_Name"]
+            acc[key][disp][c] = acc[key][disp].get(c, 0.0) + float(r["Counter_Value"])
+    extra = "--no-cpu --no-sweep"
+    lines = [f"# VALU and memory-unit busy, workload {wl}",
+             f"command: rocprofv3 --pmc VALUBusy TA_BUSY_avr SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 GRBM_GUI_ACTIVE "
+             f"--output-format csv -d <dir>/busy -o run -- python3 bench.py --workload {wl} --steps {args.steps} "
+             f"--warmup {args.warmup} {extra}",
+             f"source_digest: {source_digest()}",
+             "kernel | dispatches | VALU busy % | memory unit busy % | VALU instructions | transcendental instructions"]
+    for k, disps in sorted(acc.items()):
+        if not k.startswith("k_"):
+            continue
+        vb = [v.get("VALUBusy", np.nan) for v in disps.values()]
+        mb = [100.0 * v.get("TA_BUSY_avr", np.nan) / v["GRBM_GUI_ACTIVE"]
+              for v in disps.values() if v.get("GRBM_GUI_ACTIVE")]
+        vi = [v.get("SQ_INSTS_VALU", np.nan) for v in disps.values()]
+        ti = [v.get("SQ_INSTS_VALU_TRANS_F32", np.nan) for v in disps.values()]
+        lines.append(f"{k} | {len(disps)} | {np.nanmean(vb):.1f} | {np.nanmean(mb):.1f} | "
+                     f"{np.nanmean(vi):.4g} | {np.nanmean(ti):.4g}")
+    with open(os.path.join(d, f"busy_{wl}.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -521,13 +572,18 @@ def main():
                     help="only time draft-token sampling on the workload's draft rows and print its JSON")
     ap.add_argument("--rocprof-summary", metavar="DIR", default=None,
                     help="summarise rocprofv3 CSV output under DIR (see rocprof_summary) and exit")
+    ap.add_argument("--rocprof-busy", metavar="DIR", default=None,
+                    help="summarise a rocprofv3 busy-counter run under DIR/busy (see busy_summary) and exit")
     args = ap.parse_args()
+    if args.rocprof_busy:
+        busy_summary(args)
+        return
     if args.rocprof_summary:
         rocprof_summary(args)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        print(json.dumps({"error": "the library is measured on one GPU only; run with --gpus 1"}))
         sys.exit(2)
 
     import torch

@@ -265,24 +265,6 @@ __device__ __forceinline__ void merge_stats(float &R, float &S, float R2, float 
   S = a + b;
 }
 
-// Fold NE logits (already masked: -inf for entries outside the row) into (R, S).
-template <int NE>
-__device__ __forceinline__ void accumulate(float &R, float &S, const float (&z)[NE], float c) {
-  float m = z[0];
-#pragma unroll
-  for (int e = 1; e < NE; ++e) m = fmaxf(m, z[e]);
-  const float mc = m * c;
-  if (mc > R) {
-    const float Rn = ceilf(mc);
-    S = (R == -INFINITY) ? 0.0f : scale_pow2(S, R - Rn);
-    R = Rn;
-  }
-  if (R != -INFINITY) {
-#pragma unroll
-    for (int e = 0; e < NE; ++e) S += __builtin_amdgcn_exp2f(fmaf(z[e], c, -R));
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Reductions
 // ---------------------------------------------------------------------------

@@ -238,22 +238,41 @@ __device__ __forceinline__ void raise_ref(float &R, float &S, float m, float c) 
   }
 }
 
-// Fold vectors [u0, u0 + FU) of one row into (R, S): one maximum and one
-// rescale test, then one fma, exp2 and add per entry.
+// Fold vectors [u0, u0 + FU) of one row into (R, S), S 2^R being the sum of
+// 2^(z c) so far, R an integer that only rises.  R need not bound the
+// largest z c: fp32 keeps its relative precision at any scale, so a fold
+// sums its terms 2^(z c - R) against the R it finds (one fma, exp2 and add
+// per entry, no maximum).  Only when R is still unset, or the fold's terms
+// pass 2^64 (an entry more than 64 above R), is R raised to the fold's
+// ceil(max z c), S rescaled by that exact power of two and the fold summed
+// again.  Every term then stays at most 2^64 and S below 2^82 for rows of up
+// to 2^17 folds per thread; partial sums merge by exact powers of two as
+// before, and readers form 2^(z c - R) / S alike.
 template <int FU, int U, int NE>
 __device__ __forceinline__ void fold_vecs(float &R, float &S, const float (&z)[U][NE], int u0, float c) {
-  float m = z[u0][0];
-#pragma unroll
-  for (int u = u0; u < u0 + FU; ++u)
-#pragma unroll
-    for (int e = 0; e < NE; ++e) m = fmaxf(m, z[u][e]);
-  raise_ref(R, S, m, c);
+  float s = 0.0f;
   if (R != -INFINITY) {
 #pragma unroll
     for (int u = u0; u < u0 + FU; ++u)
 #pragma unroll
-      for (int e = 0; e < NE; ++e) S += __builtin_amdgcn_exp2f(fmaf(z[u][e], c, -R));
+      for (int e = 0; e < NE; ++e) s += __builtin_amdgcn_exp2f(fmaf(z[u][e], c, -R));
   }
+  if (R == -INFINITY || !(s <= 0x1p64f)) {
+    float m = z[u0][0];
+#pragma unroll
+    for (int u = u0; u < u0 + FU; ++u)
+#pragma unroll
+      for (int e = 0; e < NE; ++e) m = fmaxf(m, z[u][e]);
+    raise_ref(R, S, m, c);
+    s = 0.0f;
+    if (R != -INFINITY) {
+#pragma unroll
+      for (int u = u0; u < u0 + FU; ++u)
+#pragma unroll
+        for (int e = 0; e < NE; ++e) s += __builtin_amdgcn_exp2f(fmaf(z[u][e], c, -R));
+    }
+  }
+  S += s;
 }
 
 // Partial statistics of draft row j and target row j over vectors [v0, v1);

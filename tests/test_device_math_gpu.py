@@ -5,8 +5,9 @@
   ties of the Gumbel keys the GPU's winner then differs from the oracle's only
   where the keys lie within rounding, which the parity bar exempts.
 * The native exp2 used for the softmax statistics is within 1 ulp over the
-  range its arguments take (z c - R <= 0 down to the fp32 normal limit) on a
-  dense sample of fp32 inputs, and underflows to [0, 2^-126] below it.
+  range its arguments take (z c - R from the fp32 normal limit up to 64: the
+  reference R may lie up to 64 below a row's largest z c) on a dense sample
+  of fp32 inputs, and underflows to [0, 2^-126] below it.
 * The native log2 the bonus keys apply to those variates stays within 2 ulp
   of the result, or 2^-22 absolute where the result is near 0.
 """
@@ -57,10 +58,13 @@ def test_exponential_variate_every_U():
 def test_native_exp2_on_statistics_range():
     import torch
     import rejection_sampling_verify_17_amd as S
-    # every 64th fp32 bit pattern from -0 down to -150 (the arguments of the
-    # statistics are z c - R <= 0)
+    # every 64th fp32 bit pattern from -0 down to -150 and from +0 up to 64
+    # (the arguments of the statistics are z c - R <= 64)
     lo, hi = np.float32(-0.0).view(np.uint32), np.float32(-150.0).view(np.uint32)
-    bits = np.arange(lo, hi, 64, dtype=np.uint64).astype(np.uint32)
+    neg = np.arange(lo, hi, 64, dtype=np.uint64).astype(np.uint32)
+    pos = np.arange(np.float32(0.0).view(np.uint32), np.float32(64.0).view(np.uint32) + 1, 64,
+                    dtype=np.uint64).astype(np.uint32)
+    bits = np.concatenate([neg, pos])
     x = bits.view(np.float32)
     xt = torch.from_numpy(x).cuda()
     out = torch.empty_like(xt)
@@ -69,7 +73,7 @@ def test_native_exp2_on_statistics_range():
     ref = np.exp2(x.astype(np.float64))
     normal = x >= -126.0
     err = np.abs(got[normal] - ref[normal]) / _ulp(ref[normal])
-    _say(f"exp2 on {normal.sum()} inputs in [-126, 0]: max {err.max():.3f} ulp, mean {err.mean():.3f}")
+    _say(f"exp2 on {normal.sum()} inputs in [-126, 64]: max {err.max():.3f} ulp, mean {err.mean():.3f}")
     assert err.max() <= 1.0
     tail = got[~normal]
     assert np.all(tail >= 0.0) and np.all(tail <= 2.0 ** -126)
