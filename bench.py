@@ -4,9 +4,10 @@
 A step is one sv_verify call over one batch of a synthetic workload (every
 kernel of the hot path: softmax statistics, acceptance ratios, first-rejection
 ballot, residual / bonus Gumbel-max sampling).  Inputs are resident in HBM
-before timing starts; at least two copies (more for workloads under 1 GiB)
-are rotated, so a step never finds rows the previous step left in the 256 MB
-last-level cache.
+before timing starts; at least two copies are rotated, more when the rows a
+step surely reads (position 0) come to less than 1 GiB over two, so a step
+does not find rows an earlier step left in the 256 MB last-level cache
+(workloads whose whole input is far smaller, like c1, still fit it).
 
 Prints ONE JSON line: verified draft positions per second on the headline
 workload (c4b: B=1024, gamma=4, V=50257, fp32, draft noise sigma 1), the
@@ -124,8 +125,11 @@ def run_workload(name: str, steps: int, warmup: int, hip: Hip, seed: int = 3000)
     w = I.make(name)
     gen_s = time.time() - t0
     dev = torch.device("cuda:0")
-    nbytes = w.target.nbytes + w.draft.nbytes
-    copies = max(2, min(8, int(np.ceil((1 << 30) / nbytes))))
+    # copies enough that the rows a step surely reads (position 0: the target
+    # row, and the draft row unless T = 0) add up to 1 GiB over the rotation,
+    # so the 256 MB MALL cannot serve a repeat (capped at 8 copies)
+    first = (1 if w.temperature == 0.0 else 2) * w.B * w.V * (2 if w.is_bf16 else 4)
+    copies = max(2, min(8, int(np.ceil((1 << 30) / first))))
     if w.is_bf16:
         tgt0 = torch.from_numpy(w.target.view(np.int16)).view(torch.bfloat16)
         drf0 = torch.from_numpy(w.draft.view(np.int16)).view(torch.bfloat16)
