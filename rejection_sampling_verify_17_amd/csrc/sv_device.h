@@ -29,8 +29,17 @@ struct Philox4 {
   uint32_t w[4];
 };
 
+// a ^ b ^ c in one instruction (gfx950's three-input bit operation; the
+// table 0x96 is 1 where an odd number of the three inputs are 1).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 // Rounds FIRST .. 9 of Philox4x32-10 from the words and keys of round FIRST.
-template <int FIRST>
+// X3: each round's two three-way XORs as one instruction each (fewer
+// instructions, but the operation takes its operands in vector registers,
+// which costs registers a kernel near its budget may not have).
+template <int FIRST, bool X3 = false>
 __device__ __forceinline__ Philox4 philox_rounds(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                                  uint32_t k0, uint32_t k1) {
 #pragma unroll
@@ -42,8 +51,8 @@ __device__ __forceinline__ Philox4 philox_rounds(uint32_t c0, uint32_t c1, uint3
     asm("v_mad_u64_u32 %0, %1, %2, %3, 0" : "=v"(pB), "=s"(ccB) : "s"(mB), "v"(c2));
     const uint32_t hiA = (uint32_t)(pA >> 32), loA = (uint32_t)pA;
     const uint32_t hiB = (uint32_t)(pB >> 32), loB = (uint32_t)pB;
-    const uint32_t n0 = hiB ^ c1 ^ k0;
-    const uint32_t n2 = hiA ^ c3 ^ k1;
+    const uint32_t n0 = X3 ? xor3(hiB, c1, k0) : hiB ^ c1 ^ k0;
+    const uint32_t n2 = X3 ? xor3(hiA, c3, k1) : hiA ^ c3 ^ k1;
     c0 = n0;
     c1 = loB;
     c2 = n2;
@@ -81,7 +90,7 @@ struct PhiloxStream {
     hi_a1 = (uint32_t)(pa1 >> 32);
     lo_a1 = (uint32_t)pa1;
   }
-  __device__ __forceinline__ Philox4 block(uint32_t group) const {
+  template <bool X3 = false> __device__ __forceinline__ Philox4 block(uint32_t group) const {
     uint64_t pA, pB, cc;
     asm("v_mad_u64_u32 %0, %1, %2, %3, 0" : "=v"(pA), "=s"(cc) : "s"(0xD2511F53u), "v"(group));
     const uint32_t hi_a0 = (uint32_t)(pA >> 32), lo_a0 = (uint32_t)pA;
@@ -90,7 +99,7 @@ struct PhiloxStream {
     const uint32_t n0 = (uint32_t)(pB >> 32) ^ lo_b0 ^ (k0 + 0x9E3779B9u);
     const uint32_t n2 = hi_a1 ^ lo_a0 ^ (k1 + 0xBB67AE85u);
     // second round done: words (n0, lo(pB), n2, lo_a1), keys advanced twice
-    return philox_rounds<2>(n0, (uint32_t)pB, n2, lo_a1, k0 + 2u * 0x9E3779B9u, k1 + 2u * 0xBB67AE85u);
+    return philox_rounds<2, X3>(n0, (uint32_t)pB, n2, lo_a1, k0 + 2u * 0x9E3779B9u, k1 + 2u * 0xBB67AE85u);
   }
 };
 

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_draft_sample(Args a) {
     }
   } else {
     const PhiloxStream ps(a.key0, a.key1, seq, (uint32_t)j, PURPOSE_DRAFT);
-    best = gumbel_dense_row<DT, kTopkThreads>(P, a.V, a.c, ps, 0, a.ngb);
+    best = gumbel_dense_row<DT, kTopkThreads, false, true>(P, a.V, a.c, ps, 0, a.ngb);
   }
   best = block_max_u64_sh<kTopkThreads>(best, sh.red_u);
   if (threadIdx.x == 0) a.drafted[row] = best == 0ull ? 0 : (int32_t)packed_index(best);

@@ -372,7 +372,7 @@ __device__ __forceinline__ float residual_weight(float eq, float invSq, float ep
 // Each thread walks its entries in increasing index, so a strict comparison
 // keeps the smaller index among equal keys; the block reduction does the same
 // on the packed key.  exp2(-inf) = 0 gives masked logits zero weight.
-template <int DT, bool RESID>
+template <int DT, bool RESID, bool X3 = false>
 __device__ unsigned long long chunk_winner(const Args &a, int b, int pos, float4 st, int g0, int g1) {
   constexpr int NE = Elem<DT>::kVec;
   constexpr int U = NE == 4 ? 2 : 1;  // group blocks in flight per thread (8 entries)
@@ -399,7 +399,7 @@ __device__ unsigned long long chunk_winner(const Args &a, int b, int pos, float4
 #pragma unroll
       for (int g = 0; g < NE / 4; ++g) {
         const uint32_t group = (uint32_t)(gb * (NE / 4) + g);
-        const Philox4 blk = ps.block(group);
+        const Philox4 blk = ps.template block<X3>(group);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t idx = group * 4u + (uint32_t)e;
@@ -667,9 +667,10 @@ __global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int launch, int w0
       const int gper = (a.ngb + cs - 1) / cs;
       const int g0 = slot * gper, g1 = min(a.ngb, g0 + gper);
       const float4 st = make_float4(uni(sh_st.x), uni(sh_st.y), uni(sh_st.z), uni(sh_st.w));
+      // (this launch has the registers for the one-instruction XORs)
       const unsigned long long w = mode == 2
-          ? chunk_winner<DT, false>(a, b, row, make_float4(0.f, 1.f, 0.f, 1.f), g0, g1)
-          : chunk_winner<DT, true>(a, b, row, st, g0, g1);
+          ? chunk_winner<DT, false, true>(a, b, row, make_float4(0.f, 1.f, 0.f, 1.f), g0, g1)
+          : chunk_winner<DT, true, true>(a, b, row, st, g0, g1);
       if (threadIdx.x == 0) {
         sh_nq = 1;
         q_b[0] = b;

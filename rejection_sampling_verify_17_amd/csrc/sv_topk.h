@@ -773,7 +773,7 @@ __device__ __forceinline__ unsigned long long block_max_u64_sh(unsigned long lon
 // (MASKED) the entries whose key is at least thr: key z c - log2 E2 with
 // words of `ps`, one Philox block per four entries.  Each thread walks its entries in
 // increasing index with a strict comparison (smaller index among equal keys).
-template <int DT, int NT, bool MASKED = false>
+template <int DT, int NT, bool MASKED = false, bool X3 = false>
 __device__ __forceinline__ unsigned long long gumbel_dense_row(const Row<DT> &R, int V, float c,
                                                              const PhiloxStream &ps, int g0, int g1,
                                                              unsigned long long thr = 0ull) {
@@ -786,7 +786,7 @@ __device__ __forceinline__ unsigned long long gumbel_dense_row(const Row<DT> &R,
 #pragma unroll
     for (int g = 0; g < NE / 4; ++g) {
       const uint32_t group = (uint32_t)(gb * (NE / 4) + g);
-      const Philox4 blk = ps.block(group);
+      const Philox4 blk = ps.template block<X3>(group);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t idx = group * 4u + (uint32_t)e;
