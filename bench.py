@@ -645,7 +645,7 @@ def main():
             sweep.append(entry)
     draft = None
     if not args.no_sweep:
-        draft = run_draft(HEADLINE, max(10, args.steps // 2), max(3, args.warmup // 2), hip)
+        draft = run_draft(HEADLINE, max(30, args.steps // 2), max(40, args.warmup), hip)
         print(f"# draft sampling {HEADLINE}: {draft['us_per_call']:.1f} us/call", file=sys.stderr, flush=True)
     line = {
         "metric": "verified draft positions/sec (and HBM GB/s, fraction of MI355X peak) at 1 GPU",
