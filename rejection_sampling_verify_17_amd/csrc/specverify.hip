@@ -228,8 +228,12 @@ struct Launches {
                              1, w0, w1, cs1, 0, cs1);
         } else {
           const long long items = (long long)a.B * std::max((w1 - w0) * p.nch_max, p.cs_max);
-          hipLaunchKernelGGL((k_rows<DT, 2>), dim3(grid(items)), dim3(kThreads), 0, stream, a, launch, w0, w1, 0, 0,
-                             0);
+          if (w0 == a.gamma)  // sampling only
+            hipLaunchKernelGGL((k_rows<DT, 3>), dim3(grid(items)), dim3(kThreads), 0, stream, a, launch, w0, w1, 0,
+                               0, 0);
+          else
+            hipLaunchKernelGGL((k_rows<DT, 2>), dim3(grid(items)), dim3(kThreads), 0, stream, a, launch, w0, w1, 0,
+                               0, 0);
         }
         ok = ok && after();
         if (w0 == a.gamma) break;

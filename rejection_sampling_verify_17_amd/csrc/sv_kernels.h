@@ -609,7 +609,9 @@ __device__ __forceinline__ float uni(float x) {
 // chunks); kb = cs1 and nch1 = 0 then, though the code also takes statistics
 // chunks of rows [w0, w1) (nch1 per row).  Otherwise k_judge judges the first
 // window and every later launch runs in MODE 2: the lists of set i: sampling
-// items, then statistics items of rows [w0, w1) (none when w0 = w1).  A block takes its items in rounds of
+// items, then statistics items of rows [w0, w1); the last launch (w0 = w1 =
+// gamma: sampling items only) runs as MODE 3, the same code compiled without
+// the statistics and judging parts.  A block takes its items in rounds of
 // up to kQueue; each item's result goes out at once (partial statistics by
 // coherent store, chunk winner kept in LDS), and at the end of a round the
 // block finishes all its items together: winners folded into the row's best
@@ -631,7 +633,10 @@ __global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int launch, int w0
   if (blockIdx.x == 0 && threadIdx.x < (MODE == 0 ? 4 : 2))
     a.lcnt[2 * list_set(launch + (MODE == 0 ? 1 : 2)) + threadIdx.x] = 0;
   if (threadIdx.x == 0) sh_nq = 0;
-  const int dw = w1 - w0;
+  // MODE 3: the last launch, which only samples (no window left to read);
+  // without the statistics and judging code it has the registers for the
+  // one-instruction three-way XORs of Philox
+  const int dw = MODE == 3 ? 0 : w1 - w0;
   int nch, cs, per_stat;
   if (MODE == 1) {
     // one item per block, after the block's own judgement of window [0, w0)
@@ -685,7 +690,7 @@ __global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int launch, int w0
   // all finish about together (sampling chunks are capped: past a few per
   // row, more blocks only add fixed costs).
   int n_samp = 0, n_stat = a.B;
-  if (MODE == 2) {
+  if (MODE >= 2) {
     n_samp = min(max(uni(a.lcnt[2 * li]), 0), a.B);
     n_stat = min(max(uni(a.lcnt[2 * li + 1]), 0), a.B);
     const int G = (int)gridDim.x;
@@ -699,14 +704,14 @@ __global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int launch, int w0
     cs = 1;
     per_stat = dw * nch;
   }
-  const long long s_items = MODE == 2 ? (long long)n_samp * cs : 0;
+  const long long s_items = MODE >= 2 ? (long long)n_samp * cs : 0;
   const long long total = MODE == 1 ? 0 : s_items + (long long)n_stat * per_stat;
   const long long round = (long long)kQueue * gridDim.x;
   // (a MODE 1 block passes once, with no item to take, to finish the one it has)
   for (long long k0 = blockIdx.x; k0 < total || (MODE == 1 && k0 == (long long)blockIdx.x); k0 += round) {
     const long long kend = min(total, k0 + round);
     for (long long k = k0; k < kend; k += gridDim.x) {
-      if (MODE == 2 && k < s_items) {
+      if (MODE >= 2 && k < s_items) {
         const int l = (int)(k / cs);
         const int ch = (int)(k - (long long)l * cs);
         const int2 e = a.slist[(size_t)li * a.B + l];
@@ -716,10 +721,11 @@ __global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int launch, int w0
         const int g0 = ch * gper, g1 = min(a.ngb, g0 + gper);
         unsigned long long w;
         if (ey & kBonusRow) {
-          w = chunk_winner<DT, false>(a, b, row, make_float4(0.f, 1.f, 0.f, 1.f), g0, g1);
+          w = chunk_winner<DT, false, MODE == 3>(a, b, row, make_float4(0.f, 1.f, 0.f, 1.f), g0, g1);
         } else {
           const float4 st = a.sst[(size_t)li * a.B + l];
-          w = chunk_winner<DT, true>(a, b, row, make_float4(uni(st.x), uni(st.y), uni(st.z), uni(st.w)), g0, g1);
+          w = chunk_winner<DT, true, MODE == 3>(a, b, row, make_float4(uni(st.x), uni(st.y), uni(st.z), uni(st.w)),
+                                                g0, g1);
         }
         if (threadIdx.x == 0) {
           const int q = sh_nq++;
@@ -727,7 +733,7 @@ __global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int launch, int w0
           q_row[q] = row;
           q_w[q] = w;
         }
-      } else {
+      } else if (MODE != 3) {
         const long long k2 = k - s_items;
         const int l = (int)(k2 / per_stat);
         const int rc = (int)(k2 - (long long)l * per_stat);
@@ -748,7 +754,7 @@ __global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int launch, int w0
         const float4 pst = chunk_stats<DT>(a, b, j, v0, min(a.nvec, v0 + cv));
         if (threadIdx.x == 0) {
           store_coherent(a.part + ((size_t)b * a.gamma + j) * a.nch_max + ch, pst);
-          if (MODE == 2) {
+          if (MODE >= 2) {
             const int q = sh_nq++;
             q_b[q] = b;
             q_row[q] = -1;
@@ -781,7 +787,7 @@ __global__ __launch_bounds__(kThreads, 8) void k_rows(Args a, int launch, int w0
     }
     __syncthreads();
     // judgements of completed windows, one wave each
-    for (int q = threadIdx.x / kWave; q < nq; q += kThreads / kWave) {
+    for (int q = threadIdx.x / kWave; MODE != 3 && q < nq; q += kThreads / kWave) {
       if (!q_fin[q] || q_row[q] >= 0) continue;
       const int b = q_b[q];
       int mode, row;
