@@ -56,6 +56,7 @@ struct TopkShared {
   int sel_done;
   float red_f[kTopkThreads / kWave];
   unsigned long long red_u[kTopkThreads / kWave];
+  unsigned long long red_low[kTopkThreads / kWave];  // nucleus cut: mass of the entries it leaves out of its histograms
   int bcast_n;
   unsigned long long srt[kTopkThreads];  // nucleus cut: the kept keys, sorted
   int cut;
@@ -621,6 +622,14 @@ __device__ void nucleus_cut_radix(TopkShared &sh, const Src &src, int V, float c
   // by orderable), fixed by the sign bit that pass 0 fixes; the last digit is
   // known without a pass
   constexpr int kPasses = Src::NE == 8 ? 2 : 3;
+  // Entries with z c - R < -T weigh under 2^(fb - T) each, so together under
+  // V 2^(fb - T) <= (1 - P) 2^fb / 4, at most (1 - P) / 2 of the total (the
+  // largest entry alone weighs at least 2^(fb - 1)): the cumulative mass from
+  // the top reaches P of the total before them.  Their mass only joins the
+  // total (summed in registers, exact), and no pass puts them in a histogram,
+  // which spares the LDS atomics of most of a long-tailed row.
+  const float T = ceilf(log2f(2.0f * (float)V / (1.0f - P))) + 1.0f;
+  unsigned long long low = 0ull;
 #pragma unroll 1
   for (int pass = 0; pass < kPasses; ++pass) {
     // digits of the key's high word: bits [53, 64), [42, 53), [32, 42)
@@ -633,9 +642,18 @@ __device__ void nucleus_cut_radix(TopkShared &sh, const Src &src, int V, float c
       const unsigned long long key = entry_key(z, (uint32_t)v);
       if (key >= thr0 && (key & pmask) == prefix) {
         const unsigned long long w = mass_fix(z, c, R, scale);
-        if (w) atomicAdd(&mass[(unsigned)((key >> shift) & dmask)], w);
+        if (fmaf(z, c, -R) < -T) {
+          if (pass == 0) low += w;
+        } else if (w) {
+          atomicAdd(&mass[(unsigned)((key >> shift) & dmask)], w);
+        }
       }
     });
+    if (pass == 0) {
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) low += __shfl_xor(low, off, kWave);
+      if (lane == 0) sh.red_low[wave] = low;
+    }
     __syncthreads();
     // thread t owns digits nb-1-2t and nb-2-2t (descending); inclusive scan
     const int dh = nb - 1 - 2 * tid, dl = dh - 1;
@@ -653,6 +671,7 @@ __device__ void nucleus_cut_radix(TopkShared &sh, const Src &src, int V, float c
     for (int w = 0; w < kTopkThreads / kWave; ++w) {
       if (w < wave) before += sh.red_u[w];
       total += sh.red_u[w];
+      if (pass == 0) total += sh.red_low[w];
     }
     if (pass == 0) {
       // the cumulative mass must reach P of the total: an integer target; the
